@@ -1,0 +1,53 @@
+"""Seeded input generators: determinism, dtype rounding, recipe shapes (no GPU)."""
+import hashlib
+
+import numpy as np
+import torch
+
+import gdn_inputs as gi
+
+
+def _h(*arrs):
+    m = hashlib.sha256()
+    for a in arrs:
+        m.update(np.ascontiguousarray(a).tobytes())
+    return m.hexdigest()
+
+
+def test_bf16_rounding_matches_torch_rne():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32),
+                        np.array([1.00390625, 1.01171875, -2.00781250, 0.0, -0.0], np.float32)])
+    ours = gi.round_to_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(ours.view(np.uint32), ref.view(np.uint32))
+
+
+def test_generators_are_deterministic():
+    a, b = gi.config0(), gi.config0()
+    assert _h(a.q, a.k, a.v, a.g, a.beta, a.pool) == _h(b.q, b.k, b.v, b.g, b.beta, b.pool)
+    c = gi.make_case("x", [5, 9], 2, 4, 16, 16, "bf16", seed=7, n_slots=8, scatter_slots=True)
+    d = gi.make_case("x", [5, 9], 2, 4, 16, 16, "bf16", seed=7, n_slots=8, scatter_slots=True)
+    assert _h(c.q, c.v, c.pool, c.slot_in) == _h(d.q, d.v, d.pool, d.slot_in)
+
+
+def test_recipe_shapes_and_ranges():
+    c = gi.config0()
+    assert c.q.shape == (128, 2, 32) and c.v.shape == (128, 2, 32)
+    assert np.all(c.g <= 0) and np.all((c.beta > 0) & (c.beta < 1))
+    assert not c.pool.any() and np.all(c.slot_in == -1)
+    n = np.linalg.norm(c.q.astype(np.float64), axis=-1)
+    assert np.allclose(n, 1.0, atol=1e-6)
+    b = gi.make_case("b", [70], 2, 4, 32, 32, "bf16", seed=3)
+    # bf16 storage: low 16 bits are zero
+    assert not (b.q.view(np.uint32) & 0xFFFF).any()
+    assert not (b.v.view(np.uint32) & 0xFFFF).any()
+    # strong decay: A_log = log U(1, 16)
+    assert np.all(np.exp(b.A_log) >= 1) and np.all(np.exp(b.A_log) <= 16)
+
+
+def test_decode_repacking():
+    dc = gi.make_decode("d", 3, 5, 1, 2, 8, 8, "f32", seed=1)
+    q, k, v, g, beta, cu = gi.decode_as_sequences(dc)
+    assert list(cu) == [0, 5, 10, 15]
+    assert np.array_equal(q[5 + 2], dc.q[2, 1]) and np.array_equal(v[10 + 4], dc.v[4, 2])
