@@ -1,0 +1,230 @@
+"""Python binding of libgdn (the gated DeltaNet operator on MI355X).
+
+Argument marshalling only: every step of the operator runs in the HIP kernels
+of ``libgdn.so``.  PyTorch supplies device memory and the current stream.
+There is no fallback: if the library is missing this module raises on import.
+
+    import gated_deltanet_rule_amd as gdn
+    gdn.prefill(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in, slot_out)
+    gdn.decode_step(q, k, v, g, beta, state_in, state_out, out, slot_in, slot_out)
+
+Shapes: q, k [T, H_k, d_k]; v, out [T, H_v, d_v]; g, beta [T, H_v] fp32;
+state pools fp32 [n_slots, H_v, d_k, d_v]; cu_seqlens [N+1], slot_in/slot_out
+[N] int32 on the device.  q/k/v are all fp32 or all bf16; out is fp32 or
+bf16 independently (its dtype selects the output type).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK = 0
+GDN_F32 = 0
+GDN_BF16 = 1
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libgdn status {status}: {msg}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("H_k", ctypes.c_int32), ("H_v", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("slot_stride", ctypes.c_int64), ("scale", ctypes.c_float),
+                ("eps", ctypes.c_float)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libgdn.so not built at {LIB_PATH}; run "
+                          "`python gated_deltanet_rule_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    D = ctypes.POINTER(Dims)
+    lib.gdn_version.restype = ctypes.c_int
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_prefill_workspace_size.argtypes = [D, I32, I64, ctypes.POINTER(SZ)]
+    lib.gdn_prefill_workspace_size.restype = ctypes.c_int
+    lib.gdn_chunked_prefill.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, I32, I64, P, SZ, P]
+    lib.gdn_chunked_prefill.restype = ctypes.c_int
+    lib.gdn_recurrent_step.argtypes = [D, P, P, P, P, P, P, P, P, P, P, I32, P]
+    lib.gdn_recurrent_step.restype = ctypes.c_int
+    lib.gdn_prefill_prepare.argtypes = [D, P, P, P, P, P, I32, I64, P, SZ, P]
+    lib.gdn_prefill_prepare.restype = ctypes.c_int
+    lib.gdn_prefill_scan.argtypes = [D, P, P, P, P, P, P, P, P, I32, I64, P, SZ, P]
+    lib.gdn_prefill_scan.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+EXPORTED = ["gdn_version", "gdn_status_string", "gdn_last_error",
+            "gdn_prefill_workspace_size", "gdn_chunked_prefill", "gdn_prefill_prepare",
+            "gdn_prefill_scan", "gdn_recurrent_step"]
+
+
+def version() -> int:
+    return lib.gdn_version()
+
+
+def _check(status: int):
+    if status != GDN_OK:
+        raise GdnError(status, lib.gdn_last_error().decode())
+
+
+def _code(dtype: torch.dtype, what: str) -> int:
+    if dtype == torch.bfloat16:
+        return GDN_BF16
+    if dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"{what} dtype must be float32 or bfloat16, got {dtype}")
+
+
+def make_dims(H_k: int, H_v: int, d_k: int, d_v: int, dtype: torch.dtype,
+              out_dtype: torch.dtype = torch.float32, scale: float = 0.0,
+              eps: float = 1e-6, slot_stride: int = 0) -> Dims:
+    return Dims(H_k, H_v, d_k, d_v, _code(dtype, "q/k/v"), _code(out_dtype, "out"),
+                slot_stride, scale, eps)
+
+
+def _dims_from(q, v, out, scale, eps, state) -> Dims:
+    if q.dim() != 3 or v.dim() != 3 or out.shape != v.shape:
+        raise ValueError("q must be [T, H_k, d_k], v and out [T, H_v, d_v]")
+    stride = 0
+    if state is not None:
+        stride = state.stride(0) if state.dim() == 4 else 0
+    return make_dims(q.shape[1], v.shape[1], q.shape[2], v.shape[2], q.dtype, out.dtype,
+                     scale, eps, stride)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype=None, dev=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def workspace_size(dims: Dims, n_seqs: int, total_tokens: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.gdn_prefill_workspace_size(ctypes.byref(dims), n_seqs, total_tokens, ctypes.byref(n)))
+    return n.value
+
+
+def prefill(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in, slot_out,
+            workspace: Optional[torch.Tensor] = None, *, scale: float = 0.0,
+            eps: float = 1e-6, stream=None) -> None:
+    """gdn_chunked_prefill on torch tensors (asynchronous on `stream`)."""
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, q.dtype, dev)
+    _need(out, "out", None, dev)
+    for t, name in ((g, "g"), (beta, "beta"), (state_out, "state_out")):
+        _need(t, name, torch.float32, dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, dev)
+    for t, name in ((cu_seqlens, "cu_seqlens"), (slot_in, "slot_in"), (slot_out, "slot_out")):
+        _need(t, name, torch.int32, dev)
+    dims = _dims_from(q, v, out, scale, eps, state_out)
+    n_seqs = slot_out.shape[0]
+    T = q.shape[0]
+    need = workspace_size(dims, n_seqs, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(lib.gdn_chunked_prefill(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                   _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
+                                   _ptr(cu_seqlens), _ptr(slot_in), _ptr(slot_out), n_seqs, T,
+                                   _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def _prefill_common(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in,
+                    slot_out, scale, eps):
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k")):
+        _need(t, name, q.dtype, dev)
+    if v is not None:
+        _need(v, "v", q.dtype, dev)
+    if out is not None:
+        _need(out, "out", None, dev)
+    for t, name in ((g, "g"), (beta, "beta"), (state_out, "state_out"), (state_in, "state_in")):
+        if t is not None:
+            _need(t, name, torch.float32, dev)
+    for t, name in ((cu_seqlens, "cu_seqlens"), (slot_in, "slot_in"), (slot_out, "slot_out")):
+        if t is not None:
+            _need(t, name, torch.int32, dev)
+
+
+class PrefillPlan:
+    """Dims + workspace for split-phase prefill calls of one batch shape:
+    ``prepare(...)`` then ``scan(...)`` (ordered on the caller's streams)."""
+
+    def __init__(self, q, v, out, n_seqs: int, *, state=None, scale: float = 0.0,
+                 eps: float = 1e-6, workspace: Optional[torch.Tensor] = None):
+        self.dims = _dims_from(q, v, out, scale, eps, state)
+        self.n_seqs = n_seqs
+        self.T = q.shape[0]
+        need = workspace_size(self.dims, n_seqs, self.T)
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        elif workspace.numel() < need:
+            raise ValueError(f"workspace needs {need} bytes")
+        self.workspace = workspace
+
+    def prepare(self, q, k, g, beta, cu_seqlens, stream=None):
+        _prefill_common(q, k, None, g, beta, None, None, None, cu_seqlens, None, None, 0, 0)
+        _check(lib.gdn_prefill_prepare(ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(g),
+                                       _ptr(beta), _ptr(cu_seqlens), self.n_seqs, self.T,
+                                       _ptr(self.workspace), self.workspace.numel(),
+                                       _stream(stream)))
+
+    def scan(self, q, k, v, state_in, state_out, out, slot_in, slot_out, stream=None):
+        _prefill_common(q, k, v, None, None, state_in, state_out, out, None, slot_in, slot_out, 0, 0)
+        _check(lib.gdn_prefill_scan(ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(state_in), _ptr(state_out), _ptr(out), _ptr(slot_in),
+                                    _ptr(slot_out), self.n_seqs, self.T, _ptr(self.workspace),
+                                    self.workspace.numel(), _stream(stream)))
+
+
+def decode_step(q, k, v, g, beta, state_in, state_out, out, slot_in, slot_out, *,
+                scale: float = 0.0, eps: float = 1e-6, stream=None) -> None:
+    """gdn_recurrent_step on torch tensors: one token per sequence."""
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, q.dtype, dev)
+    _need(out, "out", None, dev)
+    for t, name in ((g, "g"), (beta, "beta"), (state_out, "state_out")):
+        _need(t, name, torch.float32, dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, dev)
+    for t, name in ((slot_in, "slot_in"), (slot_out, "slot_out")):
+        _need(t, name, torch.int32, dev)
+    dims = _dims_from(q, v, out, scale, eps, state_out)
+    _check(lib.gdn_recurrent_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                  _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
+                                  _ptr(slot_in), _ptr(slot_out), slot_out.shape[0],
+                                  _stream(stream)))

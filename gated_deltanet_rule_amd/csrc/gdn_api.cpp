@@ -1,0 +1,249 @@
+// gdn_api.cpp -- the libgdn C ABI: argument validation, workspace sizing and
+// dispatch to the kernel launchers.  No allocation, no synchronisation and no
+// host reads of device memory happen here.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gdn_status fail(gdn_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_dim(int d) { return d == 32 || d == 64 || d == 128; }
+
+gdn_status resolve(const gdn_dims *d, gdn::Problem *p)
+{
+    if (!d) return fail(GDN_ERR_INVALID_ARG, "dims is NULL");
+    if (d->H_k <= 0 || d->H_v <= 0)
+        return fail(GDN_ERR_INVALID_ARG, "head counts must be positive (H_k=%d, H_v=%d)", d->H_k, d->H_v);
+    if (d->H_v % d->H_k != 0)
+        return fail(GDN_ERR_UNSUPPORTED, "H_v (%d) must be a multiple of H_k (%d)", d->H_v, d->H_k);
+    if (!supported_dim(d->d_k) || !supported_dim(d->d_v))
+        return fail(GDN_ERR_UNSUPPORTED, "head dims must be 32, 64 or 128 (d_k=%d, d_v=%d)", d->d_k, d->d_v);
+    if (d->dtype != GDN_F32 && d->dtype != GDN_BF16)
+        return fail(GDN_ERR_UNSUPPORTED, "unknown dtype %d", d->dtype);
+    if (d->out_dtype != GDN_F32 && d->out_dtype != GDN_BF16)
+        return fail(GDN_ERR_UNSUPPORTED, "unknown out_dtype %d", d->out_dtype);
+    const int64_t slot = (int64_t)d->H_v * d->d_k * d->d_v;
+    int64_t stride = d->slot_stride == 0 ? slot : d->slot_stride;
+    if (stride < slot || stride % 4 != 0)
+        return fail(GDN_ERR_INVALID_ARG, "slot_stride %lld must be 0 or a multiple of 4 >= %lld",
+                    (long long)d->slot_stride, (long long)slot);
+    if (!(d->eps >= 0.f) || !isfinite(d->eps)) return fail(GDN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (!(d->scale >= 0.f) || !isfinite(d->scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite and >= 0");
+    p->H_k = d->H_k;
+    p->H_v = d->H_v;
+    p->d_k = d->d_k;
+    p->d_v = d->d_v;
+    p->bf16 = d->dtype == GDN_BF16;
+    p->out_bf16 = d->out_dtype == GDN_BF16;
+    p->slot_stride = stride;
+    p->scale = d->scale == 0.f ? 1.0f / sqrtf((float)d->d_k) : d->scale;
+    p->eps = d->eps;
+    return GDN_OK;
+}
+
+gdn_status check_tensors(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *state_in, float *state_out,
+                         void *out, const int32_t *slot_in, const int32_t *slot_out)
+{
+    struct { const void *p; const char *name; size_t align; } t[] = {
+        {q, "q", 16}, {k, "k", 16}, {v, "v", 16}, {g, "g", 4}, {beta, "beta", 4},
+        {state_out, "state_out", 16}, {out, "out", 16}, {slot_in, "slot_in", 4},
+        {slot_out, "slot_out", 4}};
+    for (auto &e : t) {
+        if (!e.p) return fail(GDN_ERR_INVALID_ARG, "%s is NULL", e.name);
+        if (!aligned(e.p, e.align))
+            return fail(GDN_ERR_INVALID_ARG, "%s is not %zu-byte aligned", e.name, e.align);
+    }
+    if (state_in && !aligned(state_in, 16)) return fail(GDN_ERR_INVALID_ARG, "state_in is not 16-byte aligned");
+    return GDN_OK;
+}
+
+gdn_status check_counts(int32_t n_seqs, int64_t total_tokens)
+{
+    if (n_seqs < 1) return fail(GDN_ERR_INVALID_ARG, "n_seqs must be >= 1 (got %d)", n_seqs);
+    if (n_seqs > (1 << 24)) return fail(GDN_ERR_UNSUPPORTED, "n_seqs above 16M");
+    if (total_tokens < 0 || total_tokens > INT32_MAX)
+        return fail(GDN_ERR_INVALID_ARG, "total_tokens out of range (%lld)", (long long)total_tokens);
+    return GDN_OK;
+}
+
+gdn_status check_workspace(const gdn::Problem &p, int32_t n_seqs, int64_t total_tokens,
+                           const void *workspace, size_t workspace_bytes)
+{
+    const size_t need = gdn::prefill_workspace_bytes(p, n_seqs, total_tokens);
+    if (!workspace || workspace_bytes < need)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need,
+                    workspace_bytes, workspace);
+    if (!aligned(workspace, 256)) return fail(GDN_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    return GDN_OK;
+}
+
+gdn_status check_prepare_inputs(const void *q, const void *k, const float *g, const float *beta,
+                                const int32_t *cu_seqlens)
+{
+    struct { const void *p; const char *name; size_t align; } t[] = {
+        {q, "q", 16}, {k, "k", 16}, {g, "g", 4}, {beta, "beta", 4}, {cu_seqlens, "cu_seqlens", 4}};
+    for (auto &e : t) {
+        if (!e.p) return fail(GDN_ERR_INVALID_ARG, "%s is NULL", e.name);
+        if (!aligned(e.p, e.align))
+            return fail(GDN_ERR_INVALID_ARG, "%s is not %zu-byte aligned", e.name, e.align);
+    }
+    return GDN_OK;
+}
+
+gdn_status check_scan_inputs(const void *q, const void *k, const void *v, const float *state_in,
+                             float *state_out, void *out, const int32_t *slot_in,
+                             const int32_t *slot_out)
+{
+    struct { const void *p; const char *name; size_t align; } t[] = {
+        {q, "q", 16}, {k, "k", 16}, {v, "v", 16}, {state_out, "state_out", 16}, {out, "out", 16},
+        {slot_in, "slot_in", 4}, {slot_out, "slot_out", 4}};
+    for (auto &e : t) {
+        if (!e.p) return fail(GDN_ERR_INVALID_ARG, "%s is NULL", e.name);
+        if (!aligned(e.p, e.align))
+            return fail(GDN_ERR_INVALID_ARG, "%s is not %zu-byte aligned", e.name, e.align);
+    }
+    if (state_in && !aligned(state_in, 16)) return fail(GDN_ERR_INVALID_ARG, "state_in is not 16-byte aligned");
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_version(void) { return GDN_VERSION; }
+
+const char *gdn_status_string(int status)
+{
+    switch (status) {
+    case GDN_OK: return "success";
+    case GDN_ERR_INVALID_ARG: return "invalid argument";
+    case GDN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+    case GDN_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *gdn_last_error(void) { return g_last_error; }
+
+gdn_status gdn_prefill_workspace_size(const gdn_dims *dims, int32_t n_seqs,
+                                      int64_t total_tokens, size_t *bytes)
+{
+    g_last_error[0] = 0;
+    gdn::Problem p;
+    gdn_status st = resolve(dims, &p);
+    if (st != GDN_OK) return st;
+    if (!bytes) return fail(GDN_ERR_INVALID_ARG, "bytes is NULL");
+    if (n_seqs < 1) return fail(GDN_ERR_INVALID_ARG, "n_seqs must be >= 1 (got %d)", n_seqs);
+    if (total_tokens < 0 || total_tokens > INT32_MAX)
+        return fail(GDN_ERR_INVALID_ARG, "total_tokens out of range (%lld)", (long long)total_tokens);
+    *bytes = gdn::prefill_workspace_bytes(p, n_seqs, total_tokens);
+    return GDN_OK;
+}
+
+gdn_status gdn_prefill_prepare(const gdn_dims *dims, const void *q, const void *k,
+                               const float *g, const float *beta, const int32_t *cu_seqlens,
+                               int32_t n_seqs, int64_t total_tokens, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    g_last_error[0] = 0;
+    gdn::Problem p;
+    gdn_status st = resolve(dims, &p);
+    if (st == GDN_OK) st = check_counts(n_seqs, total_tokens);
+    if (st == GDN_OK) st = check_prepare_inputs(q, k, g, beta, cu_seqlens);
+    if (st == GDN_OK) st = check_workspace(p, n_seqs, total_tokens, workspace, workspace_bytes);
+    if (st != GDN_OK) return st;
+    gdn::PrefillArgs a{q, k, nullptr, g, beta, nullptr, nullptr, nullptr, cu_seqlens, nullptr,
+                       nullptr, n_seqs, total_tokens, workspace};
+    hipError_t e = gdn::launch_prepare(p, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "prepare launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+gdn_status gdn_prefill_scan(const gdn_dims *dims, const void *q, const void *k, const void *v,
+                            const float *state_in, float *state_out, void *out,
+                            const int32_t *slot_in, const int32_t *slot_out, int32_t n_seqs,
+                            int64_t total_tokens, const void *workspace, size_t workspace_bytes,
+                            void *stream)
+{
+    g_last_error[0] = 0;
+    gdn::Problem p;
+    gdn_status st = resolve(dims, &p);
+    if (st == GDN_OK) st = check_counts(n_seqs, total_tokens);
+    if (st == GDN_OK) st = check_scan_inputs(q, k, v, state_in, state_out, out, slot_in, slot_out);
+    if (st == GDN_OK) st = check_workspace(p, n_seqs, total_tokens, workspace, workspace_bytes);
+    if (st != GDN_OK) return st;
+    if (p.H_v > 65535) return fail(GDN_ERR_UNSUPPORTED, "H_v above 65535");
+    gdn::PrefillArgs a{q, k, v, nullptr, nullptr, state_in, state_out, out, nullptr, slot_in,
+                       slot_out, n_seqs, total_tokens, const_cast<void *>(workspace)};
+    hipError_t e = gdn::launch_scan(p, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+gdn_status gdn_chunked_prefill(const gdn_dims *dims, const void *q, const void *k,
+                               const void *v, const float *g, const float *beta,
+                               const float *state_in, float *state_out, void *out,
+                               const int32_t *cu_seqlens, const int32_t *slot_in,
+                               const int32_t *slot_out, int32_t n_seqs,
+                               int64_t total_tokens, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    g_last_error[0] = 0;
+    gdn::Problem p;
+    gdn_status st = resolve(dims, &p);
+    if (st == GDN_OK) st = check_counts(n_seqs, total_tokens);
+    if (st == GDN_OK) st = check_prepare_inputs(q, k, g, beta, cu_seqlens);
+    if (st == GDN_OK) st = check_scan_inputs(q, k, v, state_in, state_out, out, slot_in, slot_out);
+    if (st == GDN_OK) st = check_workspace(p, n_seqs, total_tokens, workspace, workspace_bytes);
+    if (st != GDN_OK) return st;
+    if (p.H_v > 65535) return fail(GDN_ERR_UNSUPPORTED, "H_v above 65535");
+    gdn::PrefillArgs a{q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in,
+                       slot_out, n_seqs, total_tokens, workspace};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = gdn::launch_prepare(p, a, s);
+    if (e == hipSuccess) e = gdn::launch_scan(p, a, s);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+gdn_status gdn_recurrent_step(const gdn_dims *dims, const void *q, const void *k,
+                              const void *v, const float *g, const float *beta,
+                              const float *state_in, float *state_out, void *out,
+                              const int32_t *slot_in, const int32_t *slot_out,
+                              int32_t n_seqs, void *stream)
+{
+    g_last_error[0] = 0;
+    gdn::Problem p;
+    gdn_status st = resolve(dims, &p);
+    if (st != GDN_OK) return st;
+    if (n_seqs < 1) return fail(GDN_ERR_INVALID_ARG, "n_seqs must be >= 1 (got %d)", n_seqs);
+    if (n_seqs > INT32_MAX / 2) return fail(GDN_ERR_UNSUPPORTED, "n_seqs too large");
+    if (p.H_v > 65535) return fail(GDN_ERR_UNSUPPORTED, "H_v above 65535");
+    st = check_tensors(q, k, v, g, beta, state_in, state_out, out, slot_in, slot_out);
+    if (st != GDN_OK) return st;
+    gdn::DecodeArgs a{q, k, v, g, beta, state_in, state_out, out, slot_in, slot_out, n_seqs};
+    hipError_t e = gdn::launch_decode(p, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+}  // extern "C"

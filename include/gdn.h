@@ -1,0 +1,207 @@
+/*
+ * gdn.h -- libgdn: the gated DeltaNet linear-attention operator on MI355X
+ * (gfx950), behind a C ABI.
+ *
+ * The operator (per sequence and value head h; key head kh = h / (H_v/H_k)):
+ *
+ *     q^ = q / sqrt(|q|^2 + eps) * scale,   k^ = k / sqrt(|k|^2 + eps)
+ *     S' = exp(g) * S                                   (decay first)
+ *     delta = beta * (v - S'^T k^)                      (delta rule)
+ *     S  = S' + k^ (x) delta                            (rank-1 correction)
+ *     o  = S^T q^                                       (read-out, updated S)
+ *
+ * as built by the autoregressive graph on the page "Optimization: Qwen3 next
+ * autoregressive pass (#17996)" (build_delta_net_autoregressive in
+ * src/models/qwen3next.cpp), with q/k L2-normalised and q scaled by
+ * 1/sqrt(head dim) as in both graphs there, and the key-head sharing of
+ * "ik_llama.cpp src/llama-delta-net.cpp" (build_layer_attn_linear_core: with
+ * the Qwen3-Next layout each key head is repeated H_v/H_k times in a row).
+ * The state S is d_k x d_v fp32, stored row-major with d_v contiguous.
+ *
+ * Two entry points follow that page's split of the work (build_layer_attn_linear
+ * chooses the autoregressive graph when a sequence brings one token and the
+ * chunked graph otherwise):
+ *   gdn_chunked_prefill  -- any number of tokens per sequence, chunked (64)
+ *                           WY form on matrix cores (build_delta_net_chunking);
+ *   gdn_recurrent_step   -- exactly one token per sequence.
+ * State slots follow build_layer_attn_linear_core of the ik_llama.cpp page: the
+ * state is read from a per-sequence slot (or starts at zero when the sequence
+ * starts) and the new state is written back into a slot.
+ *
+ * Conventions for every call:
+ *   - All tensor arguments are DEVICE pointers, contiguous, 16-byte aligned.
+ *   - Layouts (T = total tokens; for gdn_recurrent_step T = n_seqs):
+ *       q, k       [T][H_k][d_k]   element type dims->dtype
+ *       v          [T][H_v][d_v]   element type dims->dtype
+ *       out        [T][H_v][d_v]   element type dims->out_dtype
+ *       g, beta    [T][H_v]        fp32; g is the log-decay (<= 0 expected),
+ *                                  beta the post-sigmoid write strength
+ *       state pools fp32, slot s at element offset s * slot_stride, inside a
+ *                  slot [H_v][d_k][d_v]
+ *       cu_seqlens [n_seqs+1] int32 device; sequence i owns tokens
+ *                  [cu_seqlens[i], cu_seqlens[i+1]); cu_seqlens[0] == 0,
+ *                  non-decreasing, cu_seqlens[n_seqs] == total_tokens
+ *       slot_in, slot_out [n_seqs] int32 device; slot_in[i] < 0 means the
+ *                  sequence starts from the zero state
+ *   - The caller owns every buffer.  No call allocates, frees, synchronises
+ *     or reads device memory on the host.  Work is enqueued on `stream`
+ *     (a hipStream_t; NULL is the default stream) and completes
+ *     asynchronously; nothing is retained after return.
+ *   - Aliasing: state_out may equal state_in and slot_out[i] may equal
+ *     slot_in[i] (in-place update).  Output slots must be distinct, and no
+ *     sequence may write a slot that another sequence of the same call
+ *     reads.  q/k/v/g/beta/out must not overlap the state pools or the
+ *     workspace.
+ *   - Errors: host-checkable arguments are validated before anything is
+ *     enqueued; on error nothing is enqueued and a status != GDN_OK is
+ *     returned, with a message from gdn_last_error().  Device-resident
+ *     preconditions (cu_seqlens monotone and ending at total_tokens, slot
+ *     indices in range, distinct output slots) are the caller's duty and are
+ *     not checked.  The library never aborts or throws.
+ *   - Thread safety: calls may be made from several host threads; the error
+ *     message is thread-local.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_VERSION 1
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1,   /* null pointer, bad count, bad alignment  */
+    GDN_ERR_UNSUPPORTED = 2,   /* head dims / head ratio / dtype not built */
+    GDN_ERR_WORKSPACE = 3,     /* workspace missing or too small           */
+    GDN_ERR_HIP = 4            /* the HIP runtime reported an error        */
+} gdn_status;
+
+typedef enum gdn_dtype {
+    GDN_F32 = 0,               /* fp32                                      */
+    GDN_BF16 = 1               /* bfloat16                                  */
+} gdn_dtype;
+
+/* Problem dimensions shared by both entry points. */
+typedef struct gdn_dims {
+    int32_t H_k;          /* key heads (q and k)                            */
+    int32_t H_v;          /* value heads; H_v % H_k == 0                    */
+    int32_t d_k;          /* key head dim: 32, 64 or 128                    */
+    int32_t d_v;          /* value head dim: 32, 64 or 128                  */
+    int32_t dtype;        /* gdn_dtype of q, k and v                        */
+    int32_t out_dtype;    /* gdn_dtype of out; GDN_F32 (0) matches the
+                             pages' graphs, whose result is fp32; GDN_BF16
+                             halves the output traffic at the cost of one
+                             bf16 rounding per output element              */
+    int64_t slot_stride;  /* elements between state slots; 0 means
+                             H_v*d_k*d_v; else >= that and a multiple of 4  */
+    float scale;          /* q scale; 0 means 1/sqrt(d_k)                   */
+    float eps;            /* L2-norm epsilon, >= 0 (1e-6 for Qwen3-Next)    */
+} gdn_dims;
+
+/* Library version (GDN_VERSION). */
+int gdn_version(void);
+
+/* Static description of a status code. */
+const char *gdn_status_string(int status);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char *gdn_last_error(void);
+
+/*
+ * Workspace needed by gdn_chunked_prefill for a call with n_seqs sequences
+ * and total_tokens tokens, written to *bytes.  Host-only, no device work.
+ * The workspace holds the chunk table and the per-chunk WY factors
+ * (build_delta_net_chunking: the solved triangular matrix, k_cumdecay and
+ * the decayed q.k attention) between the two kernels.
+ */
+gdn_status gdn_prefill_workspace_size(const gdn_dims *dims, int32_t n_seqs,
+                                      int64_t total_tokens, size_t *bytes);
+
+/*
+ * Chunked prefill: runs every sequence of a packed varlen batch through the
+ * operator in chunks of 64 tokens (build_delta_net_chunking on the
+ * "Optimization: Qwen3 next autoregressive pass (#17996)" page: cumulative
+ * log-decay, the strictly lower beta*(k k^T)*decay matrix, (I+A)^-1, the WY
+ * factors, intra-chunk attention and the inter-chunk state contribution;
+ * a final partial chunk acts as if padded with identity rows).
+ *
+ *   q, k, v, g, beta : inputs, layouts above, total_tokens rows
+ *   state_in         : fp32 slot pool read at slot_in[i] (may be NULL when
+ *                      every slot_in[i] < 0)
+ *   state_out        : fp32 slot pool written at slot_out[i]
+ *   out              : [total_tokens][H_v][d_v] output, dims->out_dtype
+ *   cu_seqlens       : [n_seqs+1] int32 (device)
+ *   slot_in/slot_out : [n_seqs] int32 (device)
+ *   n_seqs >= 1, total_tokens >= 0 (0: only the state pass-through runs)
+ *   workspace        : device buffer of at least the size reported by
+ *                      gdn_prefill_workspace_size, 256-byte aligned
+ * A zero-length sequence copies its input state (or zeros) to its out slot.
+ */
+gdn_status gdn_chunked_prefill(const gdn_dims *dims,
+                               const void *q, const void *k, const void *v,
+                               const float *g, const float *beta,
+                               const float *state_in, float *state_out,
+                               void *out, const int32_t *cu_seqlens,
+                               const int32_t *slot_in, const int32_t *slot_out,
+                               int32_t n_seqs, int64_t total_tokens,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
+ * The two phases of gdn_chunked_prefill, for callers that schedule them
+ * separately (for example, preparing ubatch n+1 on a second stream while the
+ * scan of ubatch n runs; the scan is sequential over a sequence's chunks,
+ * the preparation is not).  gdn_chunked_prefill(...) is exactly
+ * gdn_prefill_prepare(...) followed by gdn_prefill_scan(...) on one stream.
+ *
+ * gdn_prefill_prepare: everything that does not depend on the carried state
+ * (build_delta_net_chunking: g_cumsum, decay_mask, the beta*(k k^T)*decay
+ * matrix and its triangular solve, k_cumdecay, and the decayed q.k
+ * attention), written into `workspace` together with the chunk table built
+ * from cu_seqlens.  Reads q, k, g, beta, cu_seqlens.
+ *
+ * gdn_prefill_scan: the state-dependent part (v_prime / v_new, attn_inter +
+ * v_attn, and the chunk-end state update), chunk after chunk per sequence,
+ * reading the workspace left by a prepare call with the same dims, q, k, g,
+ * beta, cu_seqlens, n_seqs and total_tokens (the caller orders the two, e.g.
+ * on one stream or with an event).  Reads q, k, v, the state pool; writes out
+ * and the state pool.  Arguments, layouts and errors as for
+ * gdn_chunked_prefill.
+ */
+gdn_status gdn_prefill_prepare(const gdn_dims *dims, const void *q, const void *k,
+                               const float *g, const float *beta,
+                               const int32_t *cu_seqlens, int32_t n_seqs,
+                               int64_t total_tokens, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+gdn_status gdn_prefill_scan(const gdn_dims *dims, const void *q, const void *k,
+                            const void *v, const float *state_in, float *state_out,
+                            void *out, const int32_t *slot_in, const int32_t *slot_out,
+                            int32_t n_seqs, int64_t total_tokens, const void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * One autoregressive step: exactly one token for each of n_seqs sequences
+ * (build_delta_net_autoregressive, which asserts a single token).  Token i
+ * belongs to sequence i: q/k [n_seqs][H_k][d_k], v/out [n_seqs][H_v][d_v],
+ * g/beta [n_seqs][H_v].  Reads state_in at slot_in[i] (zero state if < 0)
+ * and writes state_out at slot_out[i].  Needs no workspace.
+ */
+gdn_status gdn_recurrent_step(const gdn_dims *dims,
+                              const void *q, const void *k, const void *v,
+                              const float *g, const float *beta,
+                              const float *state_in, float *state_out,
+                              void *out, const int32_t *slot_in,
+                              const int32_t *slot_out, int32_t n_seqs,
+                              void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

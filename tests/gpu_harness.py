@@ -1,0 +1,142 @@
+"""Helpers for the GPU parity tests: move a seeded workload to the device, run
+it through libgdn's C ABI (via the thin binding), and compare with the fp64
+oracle under the tolerance the operator is held to:
+
+    max |gpu - oracle| <= tol * rms(oracle)   for outputs and final states,
+    tol = 1e-4 (fp32 q/k/v) or 2e-2 (bf16 q/k/v).
+
+With a bf16 output the result is additionally rounded once to bf16 (relative
+error <= 2^-9), so each output element is held to
+    |gpu - oracle| <= tol * rms(oracle) + 2^-8 * |oracle|.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import gdn_inputs as gi
+import oracle
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def tdt(dtype: str):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def dev_case(case, device="cuda"):
+    dt = tdt(case.dtype)
+    f = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(device).to(t)
+    return dict(
+        q=f(case.q, dt), k=f(case.k, dt), v=f(case.v, dt), g=f(case.g), beta=f(case.beta),
+        pool=f(case.pool), cu=f(case.cu_seqlens, torch.int32),
+        slot_in=f(case.slot_in, torch.int32), slot_out=f(case.slot_out, torch.int32))
+
+
+def gpu_prefill(case, d=None, inplace=True, chunks=None, out_dtype=torch.float32):
+    """Run a Case through gdn.prefill.  `chunks`: split a single-sequence case
+    into consecutive calls of that many tokens (state carried in place)."""
+    import gated_deltanet_rule_amd as gdn
+    d = d or dev_case(case)
+    T = case.total_tokens
+    out = torch.empty(d["v"].shape, dtype=out_dtype, device=d["v"].device)
+    pool_out = d["pool"] if inplace else torch.full_like(d["pool"], float("nan"))
+    if not inplace:
+        # slots that are not written must keep whatever the output pool held
+        pool_out.copy_(d["pool"])
+    if chunks is None:
+        gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], pool_out, out,
+                    d["cu"], d["slot_in"], d["slot_out"])
+    else:
+        assert case.n_seqs == 1 and inplace
+        for s in range(0, T, chunks):
+            e = min(T, s + chunks)
+            cu = torch.tensor([0, e - s], dtype=torch.int32, device=d["q"].device)
+            sl_in = d["slot_in"] if s == 0 else d["slot_out"]
+            gdn.prefill(d["q"][s:e], d["k"][s:e], d["v"][s:e], d["g"][s:e], d["beta"][s:e],
+                        d["pool"], d["pool"], out[s:e], cu, sl_in, d["slot_out"])
+    torch.cuda.synchronize()
+    return out, pool_out
+
+
+def oracle_case(case, heads=None):
+    return oracle.run_case(case, heads=heads)
+
+
+def rel_err(gpu, ref, bf16_out=False):
+    """max |gpu - ref| / rms(ref); with bf16_out the allowance 2^-8 |ref| for
+    the final rounding is subtracted first."""
+    ref = np.asarray(ref, np.float64)
+    gpu = np.asarray(gpu, np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    d = np.abs(gpu - ref)
+    if bf16_out:
+        d = np.maximum(d - 2.0 ** -8 * np.abs(ref), 0.0)
+    # a reference below fp32's useful range (e.g. a state decayed by e^-400)
+    # is compared in absolute terms against 1e-30
+    return float(np.max(d)) / max(rms, 1e-30), rms
+
+
+def compare_prefill(case, out, pool_out, ref_out, ref_state, heads=None, tol=None):
+    """Returns (out_err, state_err) relative to rms; asserts finiteness."""
+    tol = tol or TOL[case.dtype]
+    hs = list(range(case.H_v)) if heads is None else list(heads)
+    assert bool(torch.isfinite(out.float()).all()), "non-finite output"
+    o = out[:, hs].float().cpu().numpy().astype(np.float64)
+    eo, _ = rel_err(o, ref_out[:, hs], bf16_out=out.dtype == torch.bfloat16)
+    st = np.stack([pool_out[int(case.slot_out[i])].cpu().numpy().astype(np.float64)
+                   for i in range(case.n_seqs)])
+    es, _ = rel_err(st[:, hs], ref_state[:, hs])
+    say(f"  {case.name}: out err/rms = {eo:.3e}, state err/rms = {es:.3e} (tol {tol:g})")
+    assert eo <= tol, f"output error {eo:.3e} > {tol}"
+    assert es <= tol, f"state error {es:.3e} > {tol}"
+    return eo, es
+
+
+def run_decode(dc, device="cuda", inplace=True, out_dtype=torch.float32):
+    """Run a DecodeCase step by step; returns (outs [steps, N, H_v, d_v], pool)."""
+    import gated_deltanet_rule_amd as gdn
+    dt = tdt(dc.dtype)
+    f = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(device).to(t)
+    q, k, v = f(dc.q, dt), f(dc.k, dt), f(dc.v, dt)
+    g, b = f(dc.g), f(dc.beta)
+    pool = f(dc.pool)
+    slots = f(dc.slots, torch.int32)
+    outs = torch.empty(v.shape, dtype=out_dtype, device=device)
+    pool_b = pool if inplace else pool.clone()
+    for s in range(dc.n_steps):
+        src, dst = (pool, pool) if inplace else ((pool, pool_b) if s % 2 == 0 else (pool_b, pool))
+        gdn.decode_step(q[s], k[s], v[s], g[s], b[s], src, dst, outs[s], slots, slots)
+    torch.cuda.synchronize()
+    final = pool if (inplace or dc.n_steps % 2 == 0) else pool_b
+    return outs, final
+
+
+def oracle_decode(dc, heads=None):
+    q, k, v, g, b, cu = gi.decode_as_sequences(dc)
+    s0 = np.stack([dc.pool[dc.slots[i]] for i in range(dc.n_seqs)]).astype(np.float64)
+    out, sf = oracle.run(q, k, v, g, b, cu, s0, heads=heads)
+    # back to [steps, N, ...]
+    out = out.reshape(dc.n_seqs, dc.n_steps, dc.H_v, dc.d_v).swapaxes(0, 1)
+    return out, sf
+
+
+def compare_decode(dc, outs, pool, ref_out, ref_state, heads=None):
+    tol = TOL[dc.dtype]
+    o = outs.float().cpu().numpy().astype(np.float64)
+    P = pool.cpu().numpy().astype(np.float64)
+    hs = list(range(dc.H_v)) if heads is None else list(heads)
+    assert np.all(np.isfinite(o))
+    eo, _ = rel_err(o[:, :, hs], ref_out[:, :, hs], bf16_out=outs.dtype == torch.bfloat16)
+    st = np.stack([P[dc.slots[i]] for i in range(dc.n_seqs)])
+    es, _ = rel_err(st[:, hs], ref_state[:, hs])
+    say(f"  {dc.name}: out err/rms = {eo:.3e}, state err/rms = {es:.3e} (tol {tol:g})")
+    assert eo <= tol and es <= tol
+    return eo, es

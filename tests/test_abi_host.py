@@ -1,0 +1,144 @@
+"""The C ABI on the host: the library loads, exports every declared symbol,
+and rejects bad arguments before anything is enqueued (no GPU needed: every
+call here fails validation before it reaches the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_rule_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(gdn.EXPORTED)
+    raw = ctypes.CDLL(gdn.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version_and_status_strings():
+    assert gdn.version() == 1
+    for st in range(5):
+        assert gdn.lib.gdn_status_string(st)
+    assert gdn.lib.gdn_status_string(99) == b"unknown status"
+
+
+def _dims(**kw):
+    base = dict(H_k=16, H_v=32, d_k=128, d_v=128, dtype=gdn.GDN_BF16, out_dtype=0,
+                slot_stride=0, scale=0.0, eps=1e-6)
+    base.update(kw)
+    d = gdn.Dims()
+    for k, v in base.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_workspace_size_grows_with_tokens_and_is_aligned():
+    a = gdn.workspace_size(_dims(), 1, 4096)
+    b = gdn.workspace_size(_dims(), 1, 8192)
+    c = gdn.workspace_size(_dims(), 8, 4096)
+    assert 0 < a < b and a < c
+    # per (64-token chunk, value head): W, T', P fragments + scalars
+    blocks = 64 * 32 * (16 + 2 * 8 + 2 * 8 + 1) * 1024   # 64 more chunks x 32 value heads
+    assert 0 <= (b - a) - blocks <= 64 * 16 + 256  # + their chunk-table entries
+    f = gdn.workspace_size(_dims(dtype=gdn.GDN_F32), 1, 4096)
+    assert f > a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H_k=0), 1), (dict(H_v=-1), 1), (dict(H_v=24, H_k=16), 2),
+    (dict(d_k=96), 2), (dict(d_v=256), 2), (dict(dtype=7), 2), (dict(out_dtype=3), 2),
+    (dict(slot_stride=100), 1), (dict(slot_stride=32 * 128 * 128 + 2), 1),
+    (dict(eps=-1.0), 1), (dict(scale=float("nan")), 1),
+])
+def test_bad_dims_rejected(kw, status):
+    n = ctypes.c_size_t(0)
+    st = gdn.lib.gdn_prefill_workspace_size(ctypes.byref(_dims(**kw)), 1, 64, ctypes.byref(n))
+    assert st == status
+    assert gdn.lib.gdn_last_error()
+
+
+def test_null_dims_and_counts():
+    n = ctypes.c_size_t(0)
+    assert gdn.lib.gdn_prefill_workspace_size(None, 1, 64, ctypes.byref(n)) == 1
+    assert gdn.lib.gdn_prefill_workspace_size(ctypes.byref(_dims()), 0, 64, ctypes.byref(n)) == 1
+    assert gdn.lib.gdn_prefill_workspace_size(ctypes.byref(_dims()), 1, -5, ctypes.byref(n)) == 1
+    assert gdn.lib.gdn_prefill_workspace_size(ctypes.byref(_dims()), 1, 64, None) == 1
+
+
+FAKE = 0x7f0000000000  # never dereferenced: every call below fails validation
+
+
+def _prefill_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state_in=FAKE, state_out=FAKE,
+             out=FAKE, cu=FAKE, sin=FAKE, sout=FAKE, n=1, T=64, ws=FAKE, wsb=1 << 40)
+    a.update(over)
+    return a
+
+
+def _call_prefill(d, a):
+    P = ctypes.c_void_p
+    return gdn.lib.gdn_chunked_prefill(
+        ctypes.byref(d), P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]),
+        P(a["state_in"]), P(a["state_out"]), P(a["out"]), P(a["cu"]), P(a["sin"]),
+        P(a["sout"]), a["n"], a["T"], P(a["ws"]), a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(g=0), 1), (dict(beta=0), 1),
+    (dict(state_out=0), 1), (dict(out=0), 1), (dict(cu=0), 1), (dict(sin=0), 1),
+    (dict(sout=0), 1), (dict(q=FAKE + 8), 1), (dict(g=FAKE + 2), 1),
+    (dict(state_in=FAKE + 4), 1), (dict(n=0), 1), (dict(T=-1), 1), (dict(T=1 << 33), 1),
+    (dict(ws=0), 3), (dict(wsb=1000), 3), (dict(ws=FAKE + 16), 3),
+])
+def test_prefill_validation(over, status):
+    assert _call_prefill(_dims(), _prefill_args(**over)) == status
+    assert gdn.lib.gdn_last_error()
+
+
+def test_split_phase_validation():
+    P = ctypes.c_void_p
+    d = _dims()
+    prep = lambda **o: gdn.lib.gdn_prefill_prepare(
+        ctypes.byref(d), P(o.get("q", FAKE)), P(o.get("k", FAKE)), P(o.get("g", FAKE)),
+        P(o.get("beta", FAKE)), P(o.get("cu", FAKE)), o.get("n", 1), o.get("T", 64),
+        P(o.get("ws", FAKE)), o.get("wsb", 1 << 40), None)
+    assert prep(q=0) == 1 and prep(cu=0) == 1 and prep(g=FAKE + 1) == 1
+    assert prep(n=0) == 1 and prep(wsb=16) == 3 and prep(ws=0) == 3
+    scan = lambda **o: gdn.lib.gdn_prefill_scan(
+        ctypes.byref(d), P(o.get("q", FAKE)), P(o.get("k", FAKE)), P(o.get("v", FAKE)),
+        P(o.get("si", FAKE)), P(o.get("so", FAKE)), P(o.get("out", FAKE)), P(o.get("sin", FAKE)),
+        P(o.get("sout", FAKE)), o.get("n", 1), o.get("T", 64), P(o.get("ws", FAKE)),
+        o.get("wsb", 1 << 40), None)
+    assert scan(v=0) == 1 and scan(so=0) == 1 and scan(out=FAKE + 4) == 1
+    assert scan(T=-2) == 1 and scan(wsb=16) == 3
+
+
+def test_decode_validation():
+    P = ctypes.c_void_p
+    d = _dims()
+
+    def call(**over):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, si=FAKE, so=FAKE, out=FAKE,
+                 sin=FAKE, sout=FAKE, n=4)
+        a.update(over)
+        return gdn.lib.gdn_recurrent_step(ctypes.byref(d), P(a["q"]), P(a["k"]), P(a["v"]),
+                                          P(a["g"]), P(a["beta"]), P(a["si"]), P(a["so"]),
+                                          P(a["out"]), P(a["sin"]), P(a["sout"]), a["n"], None)
+    assert call(q=0) == 1
+    assert call(so=0) == 1
+    assert call(out=FAKE + 2) == 1
+    assert call(n=0) == 1
+    assert call(sout=FAKE + 1) == 1
+    assert gdn.lib.gdn_recurrent_step(None, *([None] * 10), 1, None) == 1

@@ -1,0 +1,85 @@
+"""GPU parity of gdn_recurrent_step (one token per sequence) against the fp64
+oracle.  The decode workload of 64 sequences x 128 steps runs at full size."""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+from gpu_harness import compare_decode, oracle_decode, run_decode, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_64x128_full():
+    dc = gi.config2()
+    say("decode 64 seqs x 128 steps, H_k=16 H_v=32 d=128 bf16")
+    outs, pool = run_decode(dc)
+    ref_o, ref_s = oracle_decode(dc)
+    compare_decode(dc, outs, pool, ref_o, ref_s)
+
+
+def test_decode_64x128_bf16_output():
+    dc = gi.config2(n_steps=16)
+    outs, pool = run_decode(dc, out_dtype=torch.bfloat16)
+    ref_o, ref_s = oracle_decode(dc)
+    compare_decode(dc, outs, pool, ref_o, ref_s)
+
+
+@pytest.mark.parametrize("H_k,H_v,d_k,d_v,dtype", [
+    (2, 2, 32, 32, "f32"), (1, 4, 64, 32, "f32"), (2, 4, 32, 128, "bf16"),
+    (4, 4, 128, 64, "bf16"), (2, 8, 128, 128, "f32"), (1, 1, 64, 64, "bf16"),
+])
+def test_decode_shapes(H_k, H_v, d_k, d_v, dtype):
+    dc = gi.make_decode(f"dec_{H_k}_{H_v}_{d_k}_{d_v}_{dtype}", 5, 9, H_k, H_v, d_k, d_v,
+                        dtype, seed=d_k + d_v + H_v, decay="weak", n_slots=11,
+                        scatter_slots=True)
+    say(dc.name)
+    outs, pool = run_decode(dc)
+    ref_o, ref_s = oracle_decode(dc)
+    compare_decode(dc, outs, pool, ref_o, ref_s)
+    # slots that no sequence owns are untouched
+    owned = set(int(s) for s in dc.slots)
+    P = pool.cpu().numpy()
+    for s in range(dc.pool.shape[0]):
+        if s not in owned:
+            assert np.array_equal(P[s], dc.pool[s])
+
+
+def test_decode_ping_pong_equals_in_place():
+    dc = gi.make_decode("pp", 4, 6, 2, 4, 64, 64, "bf16", seed=5, decay="weak")
+    o1, p1 = run_decode(dc, inplace=True)
+    o2, p2 = run_decode(dc, inplace=False)
+    assert torch.equal(o1, o2) and torch.equal(p1, p2)
+
+
+def test_decode_zero_state_slot():
+    """slot_in < 0 starts from the zero state: T=1 closed form o = beta (k^.q^) v."""
+    import gated_deltanet_rule_amd as gdn
+    rng = np.random.default_rng(3)
+    N, H, d = 3, 2, 64
+    q = torch.from_numpy(rng.standard_normal((N, H, d)).astype(np.float32)).cuda()
+    k = torch.from_numpy(rng.standard_normal((N, H, d)).astype(np.float32)).cuda()
+    v = torch.from_numpy(rng.standard_normal((N, H, d)).astype(np.float32)).cuda()
+    g = torch.full((N, H), -0.5, device="cuda")
+    b = torch.full((N, H), 0.7, device="cuda")
+    pool = torch.full((N, H, d, d), 7.0, device="cuda")
+    out = torch.empty_like(v)
+    sin = torch.full((N,), -1, dtype=torch.int32, device="cuda")
+    sout = torch.arange(N, dtype=torch.int32, device="cuda")
+    gdn.decode_step(q, k, v, g, b, pool, pool, out, sin, sout, eps=0.0)
+    torch.cuda.synchronize()
+    qn = q.double() / q.double().norm(dim=-1, keepdim=True) / np.sqrt(d)
+    kn = k.double() / k.double().norm(dim=-1, keepdim=True)
+    ref = 0.7 * (qn * kn).sum(-1, keepdim=True) * v.double()
+    err = (out.double() - ref).abs().max() / ref.pow(2).mean().sqrt()
+    assert err < 1e-4
+    # state = k^ (x) beta v
+    st = 0.7 * kn[..., :, None] * v.double()[..., None, :]
+    assert (pool.double() - st).abs().max() < 1e-5
+
+
+def test_decode_deterministic():
+    dc = gi.make_decode("det", 8, 3, 2, 4, 128, 128, "bf16", seed=9)
+    o1, p1 = run_decode(dc)
+    o2, p2 = run_decode(dc)
+    assert torch.equal(o1, o2) and torch.equal(p1, p2)

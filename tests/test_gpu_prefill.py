@@ -1,0 +1,162 @@
+"""GPU parity of gdn_chunked_prefill against the fp64 oracle.
+
+The named workloads run at their full sizes (the long-context one compares a
+sample of value heads: heads are independent chains, so a sampled head is
+checked element by element).  Stress sets make chunk-to-chunk state carry
+visible (weak decay), cover ragged lengths around the chunk size, head-dim
+and head-ratio combinations, beta = 0, g = 0 with beta = 1, zero-length
+sequences, the zero-state slot, in-place vs out-of-place state, and the
+prefill -> decode hand-off."""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import oracle
+from gpu_harness import (TOL, compare_prefill, dev_case, gpu_prefill, oracle_case,
+                         rel_err, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(case, heads=None, inplace=True, chunks=None, out_dtype=torch.float32):
+    say(f"prefill {case.name}: N={case.n_seqs} T={case.total_tokens} H_k={case.H_k} "
+        f"H_v={case.H_v} d_k={case.d_k} d_v={case.d_v} {case.dtype} chunks={chunks} "
+        f"out={out_dtype}")
+    out, pool = gpu_prefill(case, inplace=inplace, chunks=chunks, out_dtype=out_dtype)
+    ref_o, ref_s = oracle_case(case, heads=heads)
+    return compare_prefill(case, out, pool, ref_o, ref_s, heads=heads)
+
+
+def test_tiny_f32_T128():
+    _check(gi.config0())
+
+
+def test_prefill_T4096_full():
+    _check(gi.config1())
+
+
+def test_prefill_T4096_bf16_output():
+    _check(gi.config1(), out_dtype=torch.bfloat16)
+
+
+def test_varlen_8_sequences_scattered_slots():
+    case = gi.config3()
+    heads = [0, 1, 6, 13, 18, 25, 30, 31]
+    _check(case, heads=heads)
+
+
+def test_varlen_untouched_slots_and_out_of_place():
+    case = gi.make_case("varlen_small", [17, 64, 65, 130], 2, 4, 64, 64, "bf16", seed=31,
+                        n_slots=12, scatter_slots=True)
+    out1, pool1 = gpu_prefill(case, inplace=True)
+    out2, pool2 = gpu_prefill(case, inplace=False)
+    assert torch.equal(out1, out2) and torch.equal(pool1, pool2)
+    owned = set(int(s) for s in case.slot_out)
+    P = pool1.cpu().numpy()
+    for s in range(case.pool.shape[0]):
+        if s not in owned:
+            assert np.array_equal(P[s], case.pool[s])
+
+
+def test_stream_65536_as_128_calls_of_512():
+    case = gi.config4()
+    _check(case, heads=[0, 7, 21, 31], chunks=512)
+
+
+@pytest.mark.parametrize("shape", ["T4096", "stream8192"])
+def test_weak_decay_state_carry(shape):
+    if shape == "T4096":
+        case = gi.make_case("weak_T4096", [4096], dtype="bf16", seed=41, decay="weak",
+                            **gi.QWEN3_NEXT_HEADS)
+        _check(case)
+    else:
+        case = gi.make_case("weak_stream8192", [8192], dtype="bf16", seed=42, decay="weak",
+                            **gi.QWEN3_NEXT_HEADS)
+        _check(case, heads=[0, 3, 16, 31], chunks=512)
+
+
+def test_weak_decay_tiny_f32():
+    _check(gi.make_case("weak_tiny_f32", [128], 2, 2, 32, 32, "f32", seed=43, decay="weak"))
+
+
+LENGTHS = [1, 2, 63, 64, 65, 127, 128, 129, 0, 200]
+
+
+@pytest.mark.parametrize("H_k,H_v,d_k,d_v,dtype", [
+    (2, 2, 32, 32, "f32"), (1, 4, 64, 32, "f32"), (2, 4, 32, 128, "bf16"),
+    (4, 4, 128, 64, "bf16"), (1, 2, 128, 128, "f32"), (2, 4, 128, 128, "bf16"),
+    (1, 1, 64, 64, "bf16"), (2, 8, 64, 128, "bf16"),
+])
+def test_ragged_lengths_dims_and_ratios(H_k, H_v, d_k, d_v, dtype):
+    case = gi.make_case(f"ragged_{H_k}_{H_v}_{d_k}_{d_v}_{dtype}", LENGTHS, H_k, H_v, d_k, d_v,
+                        dtype, seed=d_k * 3 + d_v + H_v, decay="custom", a_lo=0.02, a_hi=0.3,
+                        n_slots=16, scatter_slots=True)
+    _check(case)
+
+
+@pytest.mark.parametrize("mode", ["beta0", "g0_beta1", "zero_state"])
+def test_degenerate_cases(mode):
+    if mode == "beta0":
+        case = gi.make_case("beta0", [150, 64], 2, 4, 64, 64, "f32", seed=51, beta_mode="zero",
+                            decay="weak")
+    elif mode == "g0_beta1":
+        case = gi.make_case("g0_beta1", [100], 2, 2, 128, 128, "f32", seed=52, decay="zero",
+                            beta_mode="one")
+    else:
+        case = gi.make_case("zero_state", [77, 3], 2, 4, 64, 64, "bf16", seed=53, s0_std=0.0)
+    _check(case)
+
+
+def test_strong_decay_outputs_finite_and_deterministic():
+    case = gi.make_case("strong_T1024", [1024], dtype="bf16", seed=61, decay="custom",
+                        a_lo=16.0, a_hi=64.0, **gi.QWEN3_NEXT_HEADS)
+    d = dev_case(case)
+    o1, p1 = gpu_prefill(case, d=d, inplace=False)
+    o2, p2 = gpu_prefill(case, d=d, inplace=False)
+    assert torch.isfinite(o1.float()).all() and torch.isfinite(p1).all()
+    assert torch.equal(o1, o2) and torch.equal(p1, p2)
+
+
+def test_split_phase_prefill_matches_single_call():
+    """prepare on one stream, scan on another (ordered by an event) == one call."""
+    import gated_deltanet_rule_amd as gdn
+    case = gi.make_case("split", [200, 64, 1], 2, 4, 128, 128, "bf16", seed=81, decay="weak",
+                        n_slots=5, scatter_slots=True)
+    d = dev_case(case)
+    out_ref, pool_ref = gpu_prefill(case, d=d, inplace=False)
+    out = torch.empty(d["v"].shape, dtype=torch.float32, device="cuda")
+    pool = d["pool"].clone()
+    plan = gdn.PrefillPlan(d["q"], d["v"], out, case.n_seqs, state=pool)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    torch.cuda.synchronize()
+    plan.prepare(d["q"], d["k"], d["g"], d["beta"], d["cu"], stream=s1)
+    ev.record(s1)
+    s2.wait_event(ev)
+    plan.scan(d["q"], d["k"], d["v"], d["pool"], pool, out, d["slot_in"], d["slot_out"], stream=s2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_ref) and torch.equal(pool, pool_ref)
+
+
+def test_prefill_then_decode_equals_longer_prefill():
+    """The state layout written by the prefill is the one the decode step reads:
+    prefill(T - n) followed by n decode steps reproduces prefill(T)."""
+    import gated_deltanet_rule_amd as gdn
+    case = gi.make_case("handoff", [300], 2, 4, 128, 128, "bf16", seed=71, decay="weak")
+    T, n = 300, 5
+    d = dev_case(case)
+    out_full, pool_full = gpu_prefill(case, d=d, inplace=False)
+    pool = d["pool"].clone()
+    out = torch.empty(d["v"].shape, dtype=torch.float32, device="cuda")
+    cu = torch.tensor([0, T - n], dtype=torch.int32, device="cuda")
+    gdn.prefill(d["q"][:T - n], d["k"][:T - n], d["v"][:T - n], d["g"][:T - n],
+                d["beta"][:T - n], pool, pool, out[:T - n], cu, d["slot_in"], d["slot_out"])
+    for t in range(T - n, T):
+        gdn.decode_step(d["q"][t:t + 1], d["k"][t:t + 1], d["v"][t:t + 1], d["g"][t:t + 1],
+                        d["beta"][t:t + 1], pool, pool, out[t:t + 1], d["slot_out"], d["slot_out"])
+    torch.cuda.synchronize()
+    ref_o, ref_s = oracle_case(case)
+    compare_prefill(case, out, pool, ref_o, ref_s)
+    e, _ = rel_err(out.cpu().numpy(), out_full.cpu().numpy())
+    assert e <= TOL["bf16"]
