@@ -1,0 +1,349 @@
+#!/usr/bin/env python3
+"""libgdn benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--quick]
+
+Headline (`value`): chunked-prefill throughput in tokens/s on the single-layer
+Qwen3-Next-shaped prefill (1 sequence, T=4096, H_k=16, H_v=32, d_k=d_v=128,
+bf16 q/k/v, fp32 g/beta/state, fp32 output, chunk 64).  One step = one
+gdn_prefill_prepare + gdn_prefill_scan over that batch (every prefill row of
+the path), inputs resident in HBM.  W untimed warm-up steps, then exactly K
+timed steps between two device synchronisations.
+
+Alongside (same JSON line):
+  roofline      the prefill's dominant kernel, from HIP events recorded on the
+                stream the kernels run on: algorithmic flops per launch
+                (per token per value head: 8*C*d + 6*d^2 for the whole
+                prefill, split 4*C*d_k/r + 2*C*d_k for the preparation and
+                4*C*d_v + 6*d_k*d_v for the scan) / mean launch time, against
+                the bf16 dense MFMA peak (2.5 PFLOP/s).
+  decode        gdn_recurrent_step on 64 sequences x 128 steps (state pool
+                128 MiB, in place), tokens/s and state bytes / kernel time
+                against the 8 TB/s HBM peak; also a ping-pong run (two pools,
+                256 MiB footprint).
+  varlen        8 packed sequences of 17..8192 tokens (12221), one call.
+  stream        65536 tokens as 128 calls of 512 with the state carried.
+  cpu_baseline  the fp64 oracle (test infrastructure, never tuned) on the
+                same prefill workload, on this host's cores.
+All inputs are seeded synthetic data (see gdn_inputs.py).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gdn_inputs as gi  # noqa: E402
+
+METRIC = "GDN prefill tokens/s (MFMA util) + decode tokens/s (state HBM GB/s), 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+C = 64
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops_per_token_head(H_k, H_v, d_k, d_v):
+    r = H_v // H_k
+    prep = 4 * C * d_k // r + 2 * C * d_k
+    scan = 4 * C * d_v + 6 * d_k * d_v
+    return prep, scan
+
+
+def to_dev(case, dev):
+    dt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    f = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(t)
+    return dict(q=f(case.q, dt), k=f(case.k, dt), v=f(case.v, dt), g=f(case.g),
+                beta=f(case.beta), pool=f(case.pool), cu=f(case.cu_seqlens, torch.int32),
+                slot_in=f(case.slot_in, torch.int32), slot_out=f(case.slot_out, torch.int32))
+
+
+class Timer:
+    """HIP events on the stream the kernels are launched on."""
+
+    def __init__(self, stream, n):
+        self.stream = stream
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    def mark(self, i):
+        self.ev[i].record(self.stream)
+
+    def ms(self, i, j):
+        return self.ev[i].elapsed_time(self.ev[j])
+
+
+def bench_prefill(gdn, dev, steps, warmup):
+    case = gi.config1()
+    d = to_dev(case, dev)
+    out = torch.empty(d["v"].shape, dtype=torch.float32, device=dev)
+    state_out = torch.empty_like(d["pool"])
+    plan = gdn.PrefillPlan(d["q"], d["v"], out, case.n_seqs, state=state_out)
+    stream = torch.cuda.current_stream()
+
+    def step(t=None):
+        if t: t.mark(0)
+        plan.prepare(d["q"], d["k"], d["g"], d["beta"], d["cu"], stream=stream)
+        if t: t.mark(1)
+        plan.scan(d["q"], d["k"], d["v"], d["pool"], state_out, out, d["slot_in"],
+                  d["slot_out"], stream=stream)
+        if t: t.mark(2)
+
+    for _ in range(warmup):
+        step()
+    timers = [Timer(stream, 3) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(timers[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    prep_ms = statistics.mean(t.ms(0, 1) for t in timers)
+    scan_ms = statistics.mean(t.ms(1, 2) for t in timers)
+    assert torch.isfinite(out).all() and torch.isfinite(state_out).all()
+    T, H_v = case.total_tokens, case.H_v
+    fp, fs = prefill_flops_per_token_head(case.H_k, case.H_v, case.d_k, case.d_v)
+    units = T * H_v
+    kern = {
+        "prepare": {"kernels": "chunk_table_kernel + prep_kernel", "mean_ms": prep_ms,
+                    "flops_per_token_head": fp,
+                    "tflops": fp * units / (prep_ms * 1e-3) / 1e12},
+        "scan": {"kernels": "scan_kernel", "mean_ms": scan_ms, "flops_per_token_head": fs,
+                 "tflops": fs * units / (scan_ms * 1e-3) / 1e12},
+    }
+    dom = "scan" if scan_ms >= prep_ms else "prepare"
+    ach = kern[dom]["tflops"]
+    roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "kernel": kern[dom]["kernels"],
+            "flops_per_launch": kern[dom]["flops_per_token_head"] * units,
+            "mean_launch_ms": kern[dom]["mean_ms"]}
+    whole = (fp + fs) * units / (ms_step * 1e-3) / 1e12
+    return case, dict(ms_step=ms_step, tokens_s=T / (ms_step * 1e-3), roofline=roof,
+                      kernels=kern, step_tflops=whole, step_mfma_frac=whole / PEAK_BF16_TFLOPS)
+
+
+def decode_bytes_per_step(dc, in_bytes=2, out_bytes=4):
+    N, H_k, H_v, dk, dv = dc.n_seqs, dc.H_k, dc.H_v, dc.d_k, dc.d_v
+    state = N * H_v * dk * dv * 4 * 2
+    qk = N * H_k * dk * in_bytes * 2
+    v = N * H_v * dv * in_bytes
+    o = N * H_v * dv * out_bytes
+    gb = N * H_v * 4 * 2
+    return state + qk + v + o + gb + N * 4 * 2
+
+
+def bench_decode(gdn, dev, reps=3):
+    dc = gi.config2()
+    dt = torch.bfloat16
+    f = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(t)
+    q, k, v = f(dc.q, dt), f(dc.k, dt), f(dc.v, dt)
+    g, b = f(dc.g), f(dc.beta)
+    pool = f(dc.pool)
+    pool2 = pool.clone()
+    slots = f(dc.slots, torch.int32)
+    outs = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    S = dc.n_steps
+    res = {}
+    for mode in ("in_place", "ping_pong"):
+        per_rep = []
+        kern_ms = []
+        for rep in range(reps + 1):
+            t = Timer(stream, S + 1)
+            torch.cuda.synchronize()
+            t.mark(0)
+            for s in range(S):
+                if mode == "in_place":
+                    src, dst = pool, pool
+                else:
+                    src, dst = (pool, pool2) if s % 2 == 0 else (pool2, pool)
+                gdn.decode_step(q[s], k[s], v[s], g[s], b[s], src, dst, outs[s], slots, slots,
+                                stream=stream)
+                t.mark(s + 1)
+            torch.cuda.synchronize()
+            if rep == 0:
+                continue  # warm-up pass
+            per_rep.append(t.ms(0, S))
+            kern_ms.extend(t.ms(s, s + 1) for s in range(S))
+        ms_128 = statistics.median(per_rep)
+        launch_ms = statistics.mean(kern_ms)
+        by = decode_bytes_per_step(dc)
+        gbs = by / (launch_ms * 1e-3) / 1e9
+        res[mode] = {"ms_per_128_steps": ms_128, "mean_launch_ms": launch_ms,
+                     "tokens_s": dc.n_seqs * S / (ms_128 * 1e-3),
+                     "bytes_per_launch": by, "achieved_gbs": gbs,
+                     "frac": gbs / PEAK_HBM_GBS}
+    assert torch.isfinite(outs).all()
+    ip = res["in_place"]
+    return {"workload": "decode: 64 sequences x 128 steps, H_k=16 H_v=32 d=128, bf16 in, "
+                        "fp32 out, fp32 state slots (128 MiB pool)",
+            "value": ip["tokens_s"], "unit": "tokens/s",
+            "ms_per_step": ip["mean_launch_ms"],
+            "roofline": {"bound": "hbm", "achieved": ip["achieved_gbs"], "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": ip["frac"], "traffic": None,
+                         "kernel": "decode_kernel", "bytes_per_launch": ip["bytes_per_launch"],
+                         "mean_launch_ms": ip["mean_launch_ms"]},
+            "ping_pong": res["ping_pong"], "in_place": ip}
+
+
+def bench_varlen(gdn, dev, reps=10):
+    case = gi.config3()
+    d = to_dev(case, dev)
+    out = torch.empty(d["v"].shape, dtype=torch.float32, device=dev)
+    pool_out = d["pool"].clone()
+    plan = gdn.PrefillPlan(d["q"], d["v"], out, case.n_seqs, state=pool_out)
+    stream = torch.cuda.current_stream()
+    t = Timer(stream, 2 * reps + 1)
+    for i in range(2):
+        plan.prepare(d["q"], d["k"], d["g"], d["beta"], d["cu"], stream=stream)
+        plan.scan(d["q"], d["k"], d["v"], d["pool"], pool_out, out, d["slot_in"], d["slot_out"],
+                  stream=stream)
+    torch.cuda.synchronize()
+    t.mark(0)
+    for i in range(reps):
+        plan.prepare(d["q"], d["k"], d["g"], d["beta"], d["cu"], stream=stream)
+        t.mark(2 * i + 1)
+        plan.scan(d["q"], d["k"], d["v"], d["pool"], pool_out, out, d["slot_in"], d["slot_out"],
+                  stream=stream)
+        t.mark(2 * i + 2)
+    torch.cuda.synchronize()
+    total = t.ms(0, 2 * reps) / reps
+    scan = statistics.mean(t.ms(2 * i + 1, 2 * i + 2) for i in range(reps))
+    T = case.total_tokens
+    fp, fs = prefill_flops_per_token_head(case.H_k, case.H_v, case.d_k, case.d_v)
+    tf = (fp + fs) * T * case.H_v / (total * 1e-3) / 1e12
+    return {"workload": "varlen: 8 sequences {17,64,65,300,512,1023,2048,8192} = 12221 tokens, "
+                        "scattered slots", "ms_per_call": total, "scan_ms": scan,
+            "tokens_s": T / (total * 1e-3), "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}
+
+
+def bench_stream(gdn, dev, reps=2):
+    case = gi.config4()
+    d = to_dev(case, dev)
+    T, U = case.total_tokens, 512
+    out = torch.empty(d["v"].shape, dtype=torch.float32, device=dev)
+    pool = d["pool"].clone()
+    plan = gdn.PrefillPlan(d["q"][:U], d["v"][:U], out[:U], 1, state=pool)
+    cu = torch.tensor([0, U], dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        for s in range(0, T, U):
+            sl_in = d["slot_in"] if s == 0 else d["slot_out"]
+            plan.prepare(d["q"][s:s + U], d["k"][s:s + U], d["g"][s:s + U], d["beta"][s:s + U],
+                         cu, stream=stream)
+            plan.scan(d["q"][s:s + U], d["k"][s:s + U], d["v"][s:s + U], pool, pool,
+                      out[s:s + U], sl_in, d["slot_out"], stream=stream)
+
+    run()
+    times = []
+    for _ in range(reps):
+        pool.copy_(d["pool"])
+        t = Timer(stream, 2)
+        torch.cuda.synchronize()
+        t.mark(0)
+        run()
+        t.mark(1)
+        torch.cuda.synchronize()
+        times.append(t.ms(0, 1))
+    ms = statistics.median(times)
+    fp, fs = prefill_flops_per_token_head(case.H_k, case.H_v, case.d_k, case.d_v)
+    tf = (fp + fs) * T * case.H_v / (ms * 1e-3) / 1e12
+    return {"workload": "stream: 65536 tokens as 128 calls of 512, state carried in place",
+            "ms_total": ms, "us_per_call": ms * 1e3 / (T // U), "tokens_s": T / (ms * 1e-3),
+            "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}
+
+
+def cpu_baseline(case, reps=3):
+    import oracle
+    threads = oracle.default_threads()
+    walls = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.run_case(case, threads=threads)
+        walls.append(time.perf_counter() - t0)
+    w = statistics.median(walls)
+    return {"value": case.total_tokens / w, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole prefill workload (1 x {case.total_tokens} tokens, all "
+                      f"{case.H_v} value heads), fp64 sequential recurrence threaded over heads, "
+                      f"median of {reps} runs ({w:.2f} s wall each)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="headline prefill + decode only")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not "
+              "supported: the operator is benchmarked on a single MI355X", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import gated_deltanet_rule_amd as gdn
+    dev = torch.device("cuda:0")
+
+    log("prefill T=4096 ...")
+    case, pf = bench_prefill(gdn, dev, args.steps, args.warmup)
+    log(f"  {pf['ms_step']:.4f} ms/step, {pf['tokens_s']:.4g} tok/s")
+    log("decode 64x128 ...")
+    dec = bench_decode(gdn, dev)
+    log(f"  {dec['ms_per_step']*1e3:.2f} us/step, {dec['roofline']['achieved']:.0f} GB/s")
+    extra = {}
+    if not args.quick:
+        log("varlen ...")
+        extra["varlen"] = bench_varlen(gdn, dev)
+        log("stream 65536 ...")
+        extra["stream"] = bench_stream(gdn, dev)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(case)
+
+    line = {
+        "metric": METRIC,
+        "value": pf["tokens_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pf["ms_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill: 1 sequence x 4096 tokens, H_k=16 H_v=32 d_k=d_v=128, "
+                               "chunk 64, bf16 q/k/v, fp32 g/beta/state, fp32 out",
+                   "tokens": case.total_tokens, "H_k": 16, "H_v": 32, "d_k": 128, "d_v": 128,
+                   "chunk": C, "parallelism": "single GPU"},
+        "roofline": pf["roofline"],
+        "prefill_kernels": pf["kernels"],
+        "prefill_step_tflops": pf["step_tflops"],
+        "prefill_step_mfma_frac": pf["step_mfma_frac"],
+        "decode": dec,
+        "cpu_baseline": cpu,
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
