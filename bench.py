@@ -93,10 +93,9 @@ def bench_prefill(gdn, dev, steps, warmup):
 
     def step(t=None):
         if t: t.mark(0)
-        plan.prepare(d["q"], d["k"], d["g"], d["beta"], d["cu"], stream=stream)
+        plan.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], stream=stream)
         if t: t.mark(1)
-        plan.scan(d["q"], d["k"], d["v"], d["pool"], state_out, out, d["slot_in"],
-                  d["slot_out"], stream=stream)
+        plan.scan(d["pool"], state_out, out, d["slot_in"], d["slot_out"], stream=stream)
         if t: t.mark(2)
 
     for _ in range(warmup):
@@ -206,16 +205,14 @@ def bench_varlen(gdn, dev, reps=10):
     stream = torch.cuda.current_stream()
     t = Timer(stream, 2 * reps + 1)
     for i in range(2):
-        plan.prepare(d["q"], d["k"], d["g"], d["beta"], d["cu"], stream=stream)
-        plan.scan(d["q"], d["k"], d["v"], d["pool"], pool_out, out, d["slot_in"], d["slot_out"],
-                  stream=stream)
+        plan.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], stream=stream)
+        plan.scan(d["pool"], pool_out, out, d["slot_in"], d["slot_out"], stream=stream)
     torch.cuda.synchronize()
     t.mark(0)
     for i in range(reps):
-        plan.prepare(d["q"], d["k"], d["g"], d["beta"], d["cu"], stream=stream)
+        plan.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], stream=stream)
         t.mark(2 * i + 1)
-        plan.scan(d["q"], d["k"], d["v"], d["pool"], pool_out, out, d["slot_in"], d["slot_out"],
-                  stream=stream)
+        plan.scan(d["pool"], pool_out, out, d["slot_in"], d["slot_out"], stream=stream)
         t.mark(2 * i + 2)
     torch.cuda.synchronize()
     total = t.ms(0, 2 * reps) / reps
@@ -241,10 +238,9 @@ def bench_stream(gdn, dev, reps=2):
     def run():
         for s in range(0, T, U):
             sl_in = d["slot_in"] if s == 0 else d["slot_out"]
-            plan.prepare(d["q"][s:s + U], d["k"][s:s + U], d["g"][s:s + U], d["beta"][s:s + U],
-                         cu, stream=stream)
-            plan.scan(d["q"][s:s + U], d["k"][s:s + U], d["v"][s:s + U], pool, pool,
-                      out[s:s + U], sl_in, d["slot_out"], stream=stream)
+            plan.prepare(d["q"][s:s + U], d["k"][s:s + U], d["v"][s:s + U], d["g"][s:s + U],
+                         d["beta"][s:s + U], cu, stream=stream)
+            plan.scan(pool, pool, out[s:s + U], sl_in, d["slot_out"], stream=stream)
 
     run()
     times = []

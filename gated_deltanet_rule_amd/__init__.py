@@ -60,9 +60,9 @@ def _load() -> ctypes.CDLL:
     lib.gdn_chunked_prefill.restype = ctypes.c_int
     lib.gdn_recurrent_step.argtypes = [D, P, P, P, P, P, P, P, P, P, P, I32, P]
     lib.gdn_recurrent_step.restype = ctypes.c_int
-    lib.gdn_prefill_prepare.argtypes = [D, P, P, P, P, P, I32, I64, P, SZ, P]
+    lib.gdn_prefill_prepare.argtypes = [D, P, P, P, P, P, P, I32, I64, P, SZ, P]
     lib.gdn_prefill_prepare.restype = ctypes.c_int
-    lib.gdn_prefill_scan.argtypes = [D, P, P, P, P, P, P, P, P, I32, I64, P, SZ, P]
+    lib.gdn_prefill_scan.argtypes = [D, P, P, P, P, P, I32, I64, P, SZ, P]
     lib.gdn_prefill_scan.restype = ctypes.c_int
     return lib
 
@@ -195,19 +195,25 @@ class PrefillPlan:
             raise ValueError(f"workspace needs {need} bytes")
         self.workspace = workspace
 
-    def prepare(self, q, k, g, beta, cu_seqlens, stream=None):
-        _prefill_common(q, k, None, g, beta, None, None, None, cu_seqlens, None, None, 0, 0)
-        _check(lib.gdn_prefill_prepare(ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(g),
-                                       _ptr(beta), _ptr(cu_seqlens), self.n_seqs, self.T,
-                                       _ptr(self.workspace), self.workspace.numel(),
+    def prepare(self, q, k, v, g, beta, cu_seqlens, stream=None):
+        _prefill_common(q, k, v, g, beta, None, None, None, cu_seqlens, None, None, 0, 0)
+        _check(lib.gdn_prefill_prepare(ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(g), _ptr(beta), _ptr(cu_seqlens), self.n_seqs,
+                                       self.T, _ptr(self.workspace), self.workspace.numel(),
                                        _stream(stream)))
 
-    def scan(self, q, k, v, state_in, state_out, out, slot_in, slot_out, stream=None):
-        _prefill_common(q, k, v, None, None, state_in, state_out, out, None, slot_in, slot_out, 0, 0)
-        _check(lib.gdn_prefill_scan(ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v),
-                                    _ptr(state_in), _ptr(state_out), _ptr(out), _ptr(slot_in),
-                                    _ptr(slot_out), self.n_seqs, self.T, _ptr(self.workspace),
-                                    self.workspace.numel(), _stream(stream)))
+    def scan(self, state_in, state_out, out, slot_in, slot_out, stream=None):
+        dev = self.workspace.device
+        _need(out, "out", None, dev)
+        for t, name in ((state_out, "state_out"), (state_in, "state_in")):
+            if t is not None:
+                _need(t, name, torch.float32, dev)
+        for t, name in ((slot_in, "slot_in"), (slot_out, "slot_out")):
+            _need(t, name, torch.int32, dev)
+        _check(lib.gdn_prefill_scan(ctypes.byref(self.dims), _ptr(state_in), _ptr(state_out),
+                                    _ptr(out), _ptr(slot_in), _ptr(slot_out), self.n_seqs,
+                                    self.T, _ptr(self.workspace), self.workspace.numel(),
+                                    _stream(stream)))
 
 
 def decode_step(q, k, v, g, beta, state_in, state_out, out, slot_in, slot_out, *,

@@ -95,11 +95,12 @@ gdn_status check_workspace(const gdn::Problem &p, int32_t n_seqs, int64_t total_
     return GDN_OK;
 }
 
-gdn_status check_prepare_inputs(const void *q, const void *k, const float *g, const float *beta,
-                                const int32_t *cu_seqlens)
+gdn_status check_prepare_inputs(const void *q, const void *k, const void *v, const float *g,
+                                const float *beta, const int32_t *cu_seqlens)
 {
     struct { const void *p; const char *name; size_t align; } t[] = {
-        {q, "q", 16}, {k, "k", 16}, {g, "g", 4}, {beta, "beta", 4}, {cu_seqlens, "cu_seqlens", 4}};
+        {q, "q", 16}, {k, "k", 16}, {v, "v", 16}, {g, "g", 4}, {beta, "beta", 4},
+        {cu_seqlens, "cu_seqlens", 4}};
     for (auto &e : t) {
         if (!e.p) return fail(GDN_ERR_INVALID_ARG, "%s is NULL", e.name);
         if (!aligned(e.p, e.align))
@@ -108,13 +109,12 @@ gdn_status check_prepare_inputs(const void *q, const void *k, const float *g, co
     return GDN_OK;
 }
 
-gdn_status check_scan_inputs(const void *q, const void *k, const void *v, const float *state_in,
-                             float *state_out, void *out, const int32_t *slot_in,
-                             const int32_t *slot_out)
+gdn_status check_scan_inputs(const float *state_in, float *state_out, void *out,
+                             const int32_t *slot_in, const int32_t *slot_out)
 {
     struct { const void *p; const char *name; size_t align; } t[] = {
-        {q, "q", 16}, {k, "k", 16}, {v, "v", 16}, {state_out, "state_out", 16}, {out, "out", 16},
-        {slot_in, "slot_in", 4}, {slot_out, "slot_out", 4}};
+        {state_out, "state_out", 16}, {out, "out", 16}, {slot_in, "slot_in", 4},
+        {slot_out, "slot_out", 4}};
     for (auto &e : t) {
         if (!e.p) return fail(GDN_ERR_INVALID_ARG, "%s is NULL", e.name);
         if (!aligned(e.p, e.align))
@@ -160,39 +160,38 @@ gdn_status gdn_prefill_workspace_size(const gdn_dims *dims, int32_t n_seqs,
 }
 
 gdn_status gdn_prefill_prepare(const gdn_dims *dims, const void *q, const void *k,
-                               const float *g, const float *beta, const int32_t *cu_seqlens,
-                               int32_t n_seqs, int64_t total_tokens, void *workspace,
-                               size_t workspace_bytes, void *stream)
+                               const void *v, const float *g, const float *beta,
+                               const int32_t *cu_seqlens, int32_t n_seqs, int64_t total_tokens,
+                               void *workspace, size_t workspace_bytes, void *stream)
 {
     g_last_error[0] = 0;
     gdn::Problem p;
     gdn_status st = resolve(dims, &p);
     if (st == GDN_OK) st = check_counts(n_seqs, total_tokens);
-    if (st == GDN_OK) st = check_prepare_inputs(q, k, g, beta, cu_seqlens);
+    if (st == GDN_OK) st = check_prepare_inputs(q, k, v, g, beta, cu_seqlens);
     if (st == GDN_OK) st = check_workspace(p, n_seqs, total_tokens, workspace, workspace_bytes);
     if (st != GDN_OK) return st;
-    gdn::PrefillArgs a{q, k, nullptr, g, beta, nullptr, nullptr, nullptr, cu_seqlens, nullptr,
+    gdn::PrefillArgs a{q, k, v, g, beta, nullptr, nullptr, nullptr, cu_seqlens, nullptr,
                        nullptr, n_seqs, total_tokens, workspace};
     hipError_t e = gdn::launch_prepare(p, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "prepare launch failed: %s", hipGetErrorString(e));
     return GDN_OK;
 }
 
-gdn_status gdn_prefill_scan(const gdn_dims *dims, const void *q, const void *k, const void *v,
-                            const float *state_in, float *state_out, void *out,
-                            const int32_t *slot_in, const int32_t *slot_out, int32_t n_seqs,
-                            int64_t total_tokens, const void *workspace, size_t workspace_bytes,
-                            void *stream)
+gdn_status gdn_prefill_scan(const gdn_dims *dims, const float *state_in, float *state_out,
+                            void *out, const int32_t *slot_in, const int32_t *slot_out,
+                            int32_t n_seqs, int64_t total_tokens, const void *workspace,
+                            size_t workspace_bytes, void *stream)
 {
     g_last_error[0] = 0;
     gdn::Problem p;
     gdn_status st = resolve(dims, &p);
     if (st == GDN_OK) st = check_counts(n_seqs, total_tokens);
-    if (st == GDN_OK) st = check_scan_inputs(q, k, v, state_in, state_out, out, slot_in, slot_out);
+    if (st == GDN_OK) st = check_scan_inputs(state_in, state_out, out, slot_in, slot_out);
     if (st == GDN_OK) st = check_workspace(p, n_seqs, total_tokens, workspace, workspace_bytes);
     if (st != GDN_OK) return st;
     if (p.H_v > 65535) return fail(GDN_ERR_UNSUPPORTED, "H_v above 65535");
-    gdn::PrefillArgs a{q, k, v, nullptr, nullptr, state_in, state_out, out, nullptr, slot_in,
+    gdn::PrefillArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, state_in, state_out, out, nullptr, slot_in,
                        slot_out, n_seqs, total_tokens, const_cast<void *>(workspace)};
     hipError_t e = gdn::launch_scan(p, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
@@ -211,8 +210,8 @@ gdn_status gdn_chunked_prefill(const gdn_dims *dims, const void *q, const void *
     gdn::Problem p;
     gdn_status st = resolve(dims, &p);
     if (st == GDN_OK) st = check_counts(n_seqs, total_tokens);
-    if (st == GDN_OK) st = check_prepare_inputs(q, k, g, beta, cu_seqlens);
-    if (st == GDN_OK) st = check_scan_inputs(q, k, v, state_in, state_out, out, slot_in, slot_out);
+    if (st == GDN_OK) st = check_prepare_inputs(q, k, v, g, beta, cu_seqlens);
+    if (st == GDN_OK) st = check_scan_inputs(state_in, state_out, out, slot_in, slot_out);
     if (st == GDN_OK) st = check_workspace(p, n_seqs, total_tokens, workspace, workspace_bytes);
     if (st != GDN_OK) return st;
     if (p.H_v > 65535) return fail(GDN_ERR_UNSUPPORTED, "H_v above 65535");

@@ -7,6 +7,7 @@
 namespace gdn {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // raw 16-byte word
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // Storage tag for bfloat16 tensors (raw 16-bit patterns in memory).
@@ -33,6 +34,31 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
     bf16_t r;
     r.bits = bf16_bits_rne(x);
     return r;
+}
+
+// Raw buffer resource over `bytes` bytes at `base`: stores at offsets past
+// the end are dropped by the hardware range check, which lets a partial tile
+// be written without a branch per row (a branch around a store leaves the
+// compiler unable to count it, and the next wait for a load then waits for
+// the store too).  0x00020000 is the gfx9 dword-3 value of a raw 32-bit
+// buffer.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void buffer_store(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buffer_store(bf16_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b16(v.bits, r, off, 0, 0);
+}
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every outstanding global load and store of the wave, which would
+// serialise a prefetch issued before the barrier with the barrier itself.
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Wave-wide (64 lanes) sum.

@@ -18,20 +18,27 @@
 // MI355X mapping (three launches):
 //   1. chunk_table_kernel: cu_seqlens -> one descriptor per 64-token chunk
 //      (sequence, first token, length) and each sequence's chunk range.
-//   2. prep_kernel, one workgroup per (chunk, key head): everything that does
-//      not depend on the carried state, for all value heads sharing the key
-//      head: K K^T and K Q^T once (bf16 MFMA, fp32 accumulate), the decay
-//      masks from an fp64 cumulative sum (so exp(G_r - G_c) never forms a
-//      factor exp(-G) that would overflow), T by blocked forward substitution
-//      in LDS (16x16 diagonal blocks by substitution, off-diagonal blocks with
-//      fp32 MFMA), then W.  T diag(beta), W and the masked attention are
-//      written to the workspace as ready-made MFMA operand fragments.
-//   3. scan_kernel, one workgroup per (sequence, value head, 16*NW value
-//      columns): walks the sequence's chunks in order with the state held in
-//      MFMA accumulator registers for the whole sequence (never round-tripped
-//      through HBM between chunks).  Per chunk: U = T'V - W S, the output
-//      O = qs*(Q S) + P U, and S = gn*S + K^T (ks*U).  Each wave owns 16 state
-//      columns, so every product on the state chain is wave-local.
+//   2. prep_kernel, one workgroup per (chunk, key head), fully parallel:
+//      everything that does not depend on the carried state, for all value
+//      heads sharing the key head.  K K^T and K Q^T once (bf16 MFMA, fp32
+//      accumulate); the decay masks from an fp64 cumulative sum (so
+//      exp(G_r - G_c) never forms a factor exp(-G) that would overflow); T by
+//      blocked forward substitution in LDS (16x16 diagonal blocks by
+//      substitution, off-diagonal blocks with fp32 MFMA); then W, the masked
+//      attention P and U0 = T diag(beta) V.  Results go to the workspace as
+//      ready-made MFMA operand fragments (W, P, and q / k^T of the key head)
+//      and accumulator tiles (U0).
+//   3. scan_kernel, one workgroup per (sequence, value head, 2 column tiles
+//      of 16 state columns): walks the sequence's chunks in order with the
+//      state on chip for the whole sequence.  Inside a column tile the four
+//      token-row tiles of a chunk are split over four waves, so each wave
+//      runs ~30 matrix-core ops per chunk on the state chain:
+//        phase A (wave = token rows rt):  U = U0 - W S,  Q S
+//        phase B (wave = token rows rt):  O = qs * (Q S) + P U
+//                (wave = dk block rt):    S = gn * S + K^T (ks * U)
+//      U and S are exchanged through LDS between the phases; the chunk's
+//      shared operands are copied into LDS once per workgroup, prefetched one
+//      chunk ahead.
 //
 // Norms, scale, beta and decay are folded into per-row / per-column scalars
 // of raw (bf16) operands, so the inputs are used as MFMA operands exactly as
@@ -50,20 +57,48 @@ struct ChunkEntry {
     int32_t seq, t0, len, pad;
 };
 
+// --------------------------------------------------------------------------
+// workspace geometry
+//
+// per (chunk, value head), in 1 KiB units:
+//   W fragments (4 x NKD) | P hi (4 x NKC) | [P lo (4 x NKC)] | scalars | U0 tiles (4 x NCT)
+// per (chunk, key head):
+//   q fragments (4 x NKD) | k^T fragments (NMT x NKC)
+// A fragment is a 16-row x KB-deep MFMA operand, 64 lanes x 16 bytes.  The
+// scalars are qs[64] (q scale * e^{G_r}), ks[64] (e^{G_n - G_r} / |k_r|), gn,
+// and the chunk's first token and length (int bits).  U0 tiles are stored
+// column-tile major (ct, rt) so a workgroup's column tiles are contiguous.
+// --------------------------------------------------------------------------
 __host__ __device__ constexpr int kb_of(bool bf16) { return bf16 ? 32 : 16; }
-
-// Per (chunk, value head) workspace block, in 1 KiB fragments:
-//   W (4 x d_k/KB) | T' hi [| T' lo] | P hi [| P lo] | scalars (qs, ks, gn)
-// (the lo halves exist for bf16 operands only).
-__host__ __device__ constexpr int n_split(bool bf16) { return bf16 ? 2 : 1; }
-__host__ __device__ constexpr int n_wfrag(int d_k, bool bf16) { return 4 * (d_k / kb_of(bf16)); }
-__host__ __device__ constexpr int n_tfrag(bool bf16) { return 4 * (C / kb_of(bf16)); }
-__host__ __device__ constexpr size_t block_bytes(int d_k, bool bf16) {
-    return (size_t)(n_wfrag(d_k, bf16) + 2 * n_split(bf16) * n_tfrag(bf16)) * 1024 + 1024;
+__host__ __device__ constexpr int ns_of(bool bf16) { return bf16 ? 2 : 1; }
+__host__ __device__ constexpr int vshared_kib(int dk, bool bf16) {
+    return 4 * (dk / kb_of(bf16)) + ns_of(bf16) * 4 * (C / kb_of(bf16)) + 1;
+}
+__host__ __device__ constexpr int vblk_kib(int dk, int dv, bool bf16) {
+    return vshared_kib(dk, bf16) + 4 * (dv / 16);
+}
+__host__ __device__ constexpr int kblk_kib(int dk, bool bf16) {
+    return 4 * (dk / kb_of(bf16)) + (dk / 16) * (C / kb_of(bf16));
 }
 
+template <int DK, int DV, typename E> struct Geo {
+    using M = Mfma<E>;
+    static constexpr bool BF = sizeof(E) == 2;
+    static constexpr int KB = M::KB, TPB = M::TPB, NS = Split<E>::N;
+    static constexpr int NKD = DK / KB, NKC = C / KB, NMT = DK / 16, NCT = DV / 16;
+    static constexpr int NWF = 4 * NKD, NPF = 4 * NKC, NQF = 4 * NKD, NKF = NMT * NKC;
+    static constexpr int F_W = 0, F_PH = NWF, F_PL = NWF + NPF, F_SCAL = NWF + NS * NPF;
+    static constexpr int SV = F_SCAL + 1;                 // shared part of the value-head block
+    static constexpr int F_U0 = SV;
+    static constexpr int VBLK = SV + 4 * NCT;
+    static constexpr int F_Q = 0, F_KT = NQF;
+    static constexpr int KBLK = NQF + NKF;
+    static constexpr int A_Q = SV, A_KT = SV + NQF, SA = SV + KBLK;   // scan LDS copy
+    static_assert(VBLK == vblk_kib(DK, DV, BF) && KBLK == kblk_kib(DK, BF), "geometry");
+};
+
 struct WsLayout {
-    size_t entries, cstart, blocks, block, total;
+    size_t entries, cstart, vblocks, kblocks, vblk, kblk, total;
     int max_chunks;
 };
 
@@ -72,25 +107,32 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 WsLayout ws_layout(const Problem &p, int32_t n_seqs, int64_t T)
 {
     WsLayout L;
+    const bool bf = p.bf16 != 0;
     L.max_chunks = (int)max_chunks(n_seqs, T);
     L.entries = 256;
     L.cstart = align256(L.entries + sizeof(ChunkEntry) * (size_t)L.max_chunks);
-    L.blocks = align256(L.cstart + sizeof(int32_t) * ((size_t)n_seqs + 1));
-    L.block = block_bytes(p.d_k, p.bf16 != 0);
-    L.total = L.blocks + L.block * (size_t)L.max_chunks * p.H_v;
+    L.vblocks = align256(L.cstart + sizeof(int32_t) * ((size_t)n_seqs + 1));
+    L.vblk = (size_t)vblk_kib(p.d_k, p.d_v, bf) * 1024;
+    L.kblk = (size_t)kblk_kib(p.d_k, bf) * 1024;
+    L.kblocks = L.vblocks + L.vblk * (size_t)L.max_chunks * p.H_v;
+    L.total = L.kblocks + L.kblk * (size_t)L.max_chunks * p.H_k;
     return L;
 }
 
 // --------------------------------------------------------------------------
 // 1. chunk table
 // --------------------------------------------------------------------------
+constexpr int kTableSeqsInLds = 4096;
+
 __global__ __launch_bounds__(1024) void chunk_table_kernel(
     const int32_t *__restrict__ cu, int n_seqs, int T, int max_ch,
     int32_t *__restrict__ hdr, ChunkEntry *__restrict__ ent, int32_t *__restrict__ cstart)
 {
     __shared__ int wsum[16];
     __shared__ int s_carry;
+    __shared__ int s_cs[kTableSeqsInLds + 1];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const bool small = n_seqs <= kTableSeqsInLds;
     if (tid == 0) s_carry = 0;
     __syncthreads();
     for (int base = 0; base < n_seqs; base += 1024) {
@@ -118,15 +160,12 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(
         const int start = carry + before + x - nc;
         if (i < n_seqs) {
             cstart[i] = min(start, max_ch);
-            for (int c = 0; c < nc; ++c) {
-                const int idx = start + c;
-                if (idx < max_ch) {
-                    ChunkEntry e;
-                    e.seq = i;
-                    e.t0 = tb + c * C;
-                    e.len = min(C, te - tb - c * C);
-                    e.pad = 0;
-                    ent[idx] = e;
+            if (small) {
+                s_cs[i] = start;
+            } else {
+                for (int c = 0; c < nc; ++c) {
+                    const int idx = start + c;
+                    if (idx < max_ch) ent[idx] = ChunkEntry{i, tb + c * C, min(C, te - tb - c * C), 0};
                 }
             }
         }
@@ -134,10 +173,25 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(
         if (tid == 0) s_carry = carry + total;
         __syncthreads();
     }
+    const int n = min(s_carry, max_ch);
     if (tid == 0) {
-        const int n = min(s_carry, max_ch);
         cstart[n_seqs] = n;
         hdr[0] = n;
+        if (small) s_cs[n_seqs] = s_carry;
+    }
+    if (!small) return;
+    __syncthreads();
+    // one thread per chunk: binary search for the owning sequence
+    for (int j = tid; j < n; j += 1024) {
+        int lo = 0, hi = n_seqs - 1;
+        while (lo < hi) {                       // last i with s_cs[i] <= j
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_cs[mid] <= j) lo = mid; else hi = mid - 1;
+        }
+        const int tb = min(max(cu[lo], 0), T);
+        const int te = min(max(cu[lo + 1], tb), T);
+        const int c = j - s_cs[lo];
+        ent[j] = ChunkEntry{lo, tb + c * C, min(C, te - tb - c * C), 0};
     }
 }
 
@@ -197,52 +251,56 @@ template <> struct ElemVec<float> {
     __device__ static __forceinline__ float raw(const uint4 &u, int e) { return __uint_as_float((&u.x)[e]); }
 };
 
-// lower 16x16 tile pairs (rt, ct), ct <= rt, and the strictly upper ones
-__constant__ int kLowR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ int kLowC[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-__constant__ int kUpR[6] = {0, 0, 0, 1, 1, 2};
-__constant__ int kUpC[6] = {1, 2, 3, 2, 3, 3};
+// The 10 lower 16x16 tile pairs (rt, ct), ct <= rt, of a 64x64 matrix in
+// row order, and the 6 strictly upper ones.  Computed, not tabulated: a table
+// indexed per wave becomes a vector memory load, and on gfx9 waiting for it
+// also waits for every store issued before it.
+__device__ __forceinline__ int low_r(int it) { return it >= 6 ? 3 : it >= 3 ? 2 : it >= 1 ? 1 : 0; }
+__device__ __forceinline__ int low_c(int it) { const int r = low_r(it); return it - r * (r + 1) / 2; }
+__device__ __forceinline__ int up_r(int z) { return z >= 5 ? 2 : z >= 3 ? 1 : 0; }
+__device__ __forceinline__ int up_c(int z) { const int r = up_r(z); return r == 0 ? z + 1 : r == 1 ? z - 1 : 3; }
 
 struct PrepParams {
-    const void *q, *k;
+    const void *q, *k, *v;
     const float *g, *beta;
     const int32_t *hdr;
     const ChunkEntry *ent;
-    char *blocks;
-    size_t block;
+    char *vblocks, *kblocks;
     int H_k, H_v;
     float scale, eps;
 };
 
-template <int DK, typename E> struct PrepLds {
+template <int DK, int DV, typename E> struct PrepLds {
     static constexpr int VEC = 16 / (int)sizeof(E);
     static constexpr int LDK = DK + VEC;     // row-major K, Q (elements)
-    static constexpr int LDT = C + VEC;      // transposed K
+    static constexpr int LDT = C + VEC;      // transposed K and V (elements)
     static constexpr int LDA = C + 4;        // fp32 A and T
     static constexpr size_t R1a = 2ull * C * LDK * sizeof(E);
     static constexpr size_t R1b = 2ull * C * LDA * sizeof(float);
     static constexpr size_t R1 = R1a > R1b ? R1a : R1b;
-    static constexpr size_t R2 = (size_t)DK * LDT * sizeof(E);
-    static constexpr size_t R2p = (R2 + 15) / 16 * 16;
+    static constexpr size_t R2 = ((size_t)DK * LDT * sizeof(E) + 15) / 16 * 16;
+    static constexpr size_t R3 = ((size_t)DV * LDT * sizeof(E) + 15) / 16 * 16;
     static constexpr size_t SMALL = C * sizeof(double) + 5 * C * sizeof(float);
-    static constexpr size_t BYTES = R1 + R2p + SMALL;
+    static constexpr size_t BYTES = R1 + R2 + R3 + SMALL;
 };
 
 // --------------------------------------------------------------------------
 // 2. per-chunk preparation (state independent)
 // --------------------------------------------------------------------------
-template <int DK, typename E>
+template <int DK, int DV, typename E>
 __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
 {
     using M = Mfma<E>;
     using SP = Split<E>;
-    using L = PrepLds<DK, E>;
+    using G = Geo<DK, DV, E>;
+    using L = PrepLds<DK, DV, E>;
     using V = ElemVec<E>;
+    using Frag = typename M::Frag;
     constexpr int KB = M::KB, TPB = M::TPB, VEC = L::VEC, NS = SP::N;
     constexpr int LDK = L::LDK, LDT = L::LDT, LDA = L::LDA;
-    constexpr int NKD = DK / KB, NKC = C / KB;
-    constexpr int NWF = 4 * NKD, NTF = 4 * NKC;
-    constexpr int VPR = DK / VEC;
+    constexpr int NKD = G::NKD, NKC = G::NKC, NCT = G::NCT;
+    constexpr int VPR = DK / VEC;         // 16-byte vectors per q/k row
+    constexpr int VPRV = DV / VEC;        // 16-byte vectors per v row
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     E *sK = reinterpret_cast<E *>(smem);
@@ -250,7 +308,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
     float *sA = reinterpret_cast<float *>(smem);
     float *sT = sA + C * LDA;
     E *sKT = reinterpret_cast<E *>(smem + L::R1);
-    double *sG = reinterpret_cast<double *>(smem + L::R1 + L::R2p);
+    E *sVT = reinterpret_cast<E *>(smem + L::R1 + L::R2);
+    double *sG = reinterpret_cast<double *>(smem + L::R1 + L::R2 + L::R3);
     float *sBeta = reinterpret_cast<float *>(sG + C);
     float *srk = sBeta + C;
     float *srq = srk + C;
@@ -264,6 +323,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
     const int n = lane & 15, qd = lane >> 4;
     const E *qg = static_cast<const E *>(pp.q);
     const E *kg = static_cast<const E *>(pp.k);
+    const E *vg = static_cast<const E *>(pp.v);
 
     // 1. stage K, Q (row-major) and K^T; inverse row norms
     for (int vi = tid; vi < C * VPR; vi += 256) {
@@ -294,9 +354,22 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
             srq[r] = r < len ? rsqrtf(q2 + pp.eps) * pp.scale : 0.f;
         }
     }
-    __syncthreads();
+    lds_sync();
 
-    // 2. raw K K^T (lower tiles) and K Q^T (tiles (ct, rt), ct <= rt): 20
+    // 2. raw q and k^T of this key head as operand fragments for the scan
+    {
+        char *kb_blk = pp.kblocks + ((size_t)chunk * pp.H_k + kh) * ((size_t)G::KBLK * 1024);
+        for (int f = w; f < G::NQF; f += 4) {
+            const int rt = f / NKD, kb = f % NKD;
+            store_frag<E>(kb_blk + G::F_Q * 1024, f, lane, M::load_rm(sQ + (16 * rt + n) * LDK, kb * KB, qd));
+        }
+        for (int f = w; f < G::NKF; f += 4) {
+            const int mt = f / NKC, kc = f % NKC;
+            store_frag<E>(kb_blk + G::F_KT * 1024, f, lane, M::load_rm(sKT + (16 * mt + n) * LDT, kc * KB, qd));
+        }
+    }
+
+    // 3. raw K K^T (lower tiles) and K Q^T (tiles (ct, rt), ct <= rt): 20
     //    tile products, 5 per wave; kept in registers for all value heads.
     floatx4 acc[5];
 #pragma unroll
@@ -304,55 +377,86 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
         acc[s] = floatx4{0.f, 0.f, 0.f, 0.f};
         const int it = w + 4 * s;
         const int pr = it < 10 ? it : it - 10;
-        const int rt = kLowR[pr], ct = kLowC[pr];
+        const int rt = low_r(pr), ct = low_c(pr);
         const E *ra = it < 10 ? sK + (16 * rt + n) * LDK : sK + (16 * ct + n) * LDK;
         const E *rb = it < 10 ? sK + (16 * ct + n) * LDK : sQ + (16 * rt + n) * LDK;
 #pragma unroll
         for (int kb = 0; kb < NKD; ++kb)
             M::mma(acc[s], M::load_rm(ra, kb * KB, qd), M::load_rm(rb, kb * KB, qd));
     }
-    __syncthreads();   // sK / sQ are dead from here on (sA / sT alias them)
+    lds_sync();   // sK / sQ are dead from here on (sA / sT alias them)
 
     const int ratio = pp.H_v / pp.H_k;
+    // V rows, g and beta of the next value head are loaded one head ahead
+    constexpr int VL = (C * VPRV + 255) / 256;
+    u32x4 vpre[VL];
+    float gpre = 0.f, bpre = 0.f;
+    auto load_head = [&](int hh) {
+#pragma unroll
+        for (int p = 0; p < VL; ++p) {
+            const int vi = tid + 256 * p;
+            const int r = vi / VPRV, cv = vi % VPRV;
+            vpre[p] = u32x4{0u, 0u, 0u, 0u};
+            if (vi < C * VPRV && r < len)
+                vpre[p] = *reinterpret_cast<const u32x4 *>(vg + ((size_t)(t0 + r) * pp.H_v + hh) * DV + cv * VEC);
+        }
+        if (w == 0 && lane < len) {
+            gpre = pp.g[(size_t)(t0 + lane) * pp.H_v + hh];
+            bpre = pp.beta[(size_t)(t0 + lane) * pp.H_v + hh];
+        }
+    };
+    load_head(kh * ratio);
     for (int jv = 0; jv < ratio; ++jv) {
         const int h = kh * ratio + jv;
-        char *blk = pp.blocks + ((size_t)chunk * pp.H_v + h) * pp.block;
-        char *Wf = blk;
-        char *Tf = blk + NWF * 1024;                    // T' hi, then T' lo
-        char *Pf = blk + (NWF + NS * NTF) * 1024;       // P hi, then P lo
-        float *scal = reinterpret_cast<float *>(blk + (NWF + 2 * NS * NTF) * 1024);
+        char *blk = pp.vblocks + ((size_t)chunk * pp.H_v + h) * ((size_t)G::VBLK * 1024);
+        char *Wf = blk + G::F_W * 1024;
+        char *Pf = blk + G::F_PH * 1024;
+        char *Plf = blk + G::F_PL * 1024;
+        float *scal = reinterpret_cast<float *>(blk + G::F_SCAL * 1024);
+        char *U0f = blk + G::F_U0 * 1024;
 
-        // 3a. cumulative log-decay in fp64, per-row scalars
+        // 4a. V^T of this value head; cumulative log-decay in fp64, row scalars
+#pragma unroll
+        for (int p = 0; p < VL; ++p) {
+            const int vi = tid + 256 * p;
+            const int r = vi / VPRV, cv = vi % VPRV;
+            if (vi < C * VPRV) {
+                const uint4 vv = __builtin_bit_cast(uint4, vpre[p]);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) sVT[(cv * VEC + e) * LDT + r] = V::raw(vv, e);
+            }
+        }
+        const float gv = gpre, bv = bpre;
+        if (jv + 1 < ratio) load_head(h + 1);
         if (w == 0) {
             const int r = lane;
-            float gv = 0.f, bv = 0.f;
-            if (r < len) {
-                gv = pp.g[(size_t)(t0 + r) * pp.H_v + h];
-                bv = pp.beta[(size_t)(t0 + r) * pp.H_v + h];
-            }
-            double G = gv;
+            double Gc = gv;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
-                const double y = __shfl_up(G, off, 64);
-                if (lane >= off) G += y;
+                const double y = __shfl_up(Gc, off, 64);
+                if (lane >= off) Gc += y;
             }
-            const double Gn = __shfl(G, 63, 64);
-            sG[r] = G;
+            const double Gn = __shfl(Gc, 63, 64);
+            sG[r] = Gc;
             sBeta[r] = bv;
-            const float eG = expf((float)G);
+            const float eG = expf((float)Gc);
             scal[r] = srq[r] * eG;                              // qs: q scale * e^{G_r}
-            scal[64 + r] = srk[r] * expf((float)(Gn - G));      // ks: e^{G_n - G_r} / |k_r|
-            if (r == 0) scal[128] = expf((float)Gn);            // gn: e^{G_n}
+            scal[64 + r] = srk[r] * expf((float)(Gn - Gc));     // ks: e^{G_n - G_r} / |k_r|
+            if (r == 0) {
+                scal[128] = expf((float)Gn);                    // gn: e^{G_n}
+                scal[129] = __int_as_float(t0);                 // the chunk's first token
+                scal[130] = __int_as_float(len);                // and length
+            }
             scol[r] = bv * eG * srk[r];                         // columns of T'' = T diag(beta e^G / |k|)
         }
-        __syncthreads();
+        lds_sync();
 
-        // 3b. A (strictly lower) -> LDS; masked, decayed Q.K -> P fragments
+        // 4b. A (strictly lower) -> LDS; masked, decayed Q.K -> P fragments
 #pragma unroll
         for (int s = 0; s < 5; ++s) {
             const int it = w + 4 * s;
             if (it < 10) {
-                const int rt = kLowR[it], ct = kLowC[it];
+                const int rt = low_r(it), ct = low_c(it);
                 const int c = 16 * ct + n;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -364,7 +468,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
                 }
             } else {
                 const int pr = it - 10;
-                const int rt = kLowR[pr], ct = kLowC[pr];
+                const int rt = low_r(pr), ct = low_c(pr);
                 const int r = 16 * rt + n;
                 floatx4 pv;
 #pragma unroll
@@ -372,17 +476,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
                     const int c = 16 * ct + 4 * qd + j;
                     pv[j] = (c <= r) ? srq[r] * srk[c] * acc[s][j] * expf((float)(sG[r] - sG[c])) : 0.f;
                 }
-                store_quarter2<E>(Pf, Pf + NTF * 1024, rt * NKC + ct / TPB, lane, ct % TPB, pv);
+                store_quarter2<E>(Pf, Plf, rt * NKC + ct / TPB, lane, ct % TPB, pv);
             }
         }
         for (int z = w; z < 6; z += 4) {
-            const int rt = kUpR[z], ct = kUpC[z];
-            store_quarter2<E>(Pf, Pf + NTF * 1024, rt * NKC + ct / TPB, lane, ct % TPB,
-                              floatx4{0.f, 0.f, 0.f, 0.f});
+            const int rt = up_r(z), ct = up_c(z);
+            store_quarter2<E>(Pf, Plf, rt * NKC + ct / TPB, lane, ct % TPB, floatx4{0.f, 0.f, 0.f, 0.f});
         }
-        __syncthreads();
+        lds_sync();
 
-        // 3c. T = (I + A)^-1: diagonal 16x16 blocks by forward substitution
+        // 4c. T = (I + A)^-1: diagonal 16x16 blocks by forward substitution
         //     (wave 0, one lane per column); other waves zero the upper blocks.
         if (w == 0) {
             const int b = lane >> 4, j = lane & 15;
@@ -400,10 +503,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
         } else {
             for (int e = tid - 64; e < 6 * 256; e += 192) {
                 const int z = e >> 8, within = e & 255;
-                sT[(16 * kUpR[z] + (within >> 4)) * LDA + 16 * kUpC[z] + (within & 15)] = 0.f;
+                sT[(16 * up_r(z) + (within >> 4)) * LDA + 16 * up_c(z) + (within & 15)] = 0.f;
             }
         }
-        __syncthreads();
+        lds_sync();
         //     off-diagonal blocks by distance: T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
         for (int d = 1; d < 4; ++d) {
             if (w < 4 - d) {
@@ -424,33 +527,40 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) sT[(16 * bi + 4 * qd + j) * LDA + 16 * bj + n] = Y[j];
             }
-            __syncthreads();
+            lds_sync();
         }
 
-        // 3d. T' = T diag(beta) as (two-term) A-operand fragments (rows r, k = c)
-        for (int f = w; f < NTF; f += 4) {
-            const int rt = f / NKC, kb = f % NKC;
-            typename M::Frag hi, lo;
-            SP::rm_f32(sT + (16 * rt + n) * LDA, kb * KB, qd, sBeta, hi, lo);
-            store_frag<E>(Tf, f, lane, hi);
-            if constexpr (NS == 2) store_frag<E>(Tf + NTF * 1024, f, lane, lo);
-        }
-        //     W^T = K^T T''^T tiles (dk tile dt, token tile tt) -> W fragments
+        // 4d. W^T = K^T T''^T tiles (dk tile dt, token tile tt) -> W fragments
         for (int item = w; item < (DK / 16) * 4; item += 4) {
             const int dt = item % (DK / 16), tt = item / (DK / 16);
             floatx4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NKC; ++kb) {
                 if (kb * KB > 16 * tt + 15) break;
-                const typename M::Frag a = M::load_rm(sKT + (16 * dt + n) * LDT, kb * KB, qd);
-                typename M::Frag hi, lo;
+                const Frag a = M::load_rm(sKT + (16 * dt + n) * LDT, kb * KB, qd);
+                Frag hi, lo;
                 SP::rm_f32(sT + (16 * tt + n) * LDA, kb * KB, qd, scol, hi, lo);
                 M::mma(a4, a, hi);
                 if constexpr (NS == 2) M::mma(a4, a, lo);
             }
             store_quarter<E>(Wf, tt * NKD + dt / TPB, lane, dt % TPB, a4);
         }
-        __syncthreads();
+        //     U0 = T diag(beta) V tiles (token tile rt, value-column tile ct)
+        for (int item = w; item < 4 * NCT; item += 4) {
+            const int ct = item % NCT, rt = item / NCT;
+            floatx4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKC; ++kb) {
+                if (kb * KB > 16 * rt + 15) break;
+                Frag hi, lo;
+                SP::rm_f32(sT + (16 * rt + n) * LDA, kb * KB, qd, sBeta, hi, lo);
+                const Frag b = M::load_rm(sVT + (16 * ct + n) * LDT, kb * KB, qd);
+                M::mma(a4, hi, b);
+                if constexpr (NS == 2) M::mma(a4, lo, b);
+            }
+            *(reinterpret_cast<floatx4 *>(U0f) + (size_t)(ct * 4 + rt) * 64 + lane) = a4;
+        }
+        lds_sync();
     }
 }
 
@@ -458,201 +568,227 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
 // 3. sequential state scan + output
 // --------------------------------------------------------------------------
 struct ScanParams {
-    const void *q, *k, *v;
     const float *state_in;
     float *state_out;
     void *out;
     const int32_t *slot_in, *slot_out;
     const int32_t *cstart;
     const ChunkEntry *ent;
-    const char *blocks;
-    size_t block;
+    const char *vblocks, *kblocks;
     int H_k, H_v;
     int64_t slot_stride;
 };
 
-template <int DK, int NW, typename E> struct ScanLds {
-    static constexpr int VEC = 16 / (int)sizeof(E);
-    static constexpr int DVB = 16 * NW;
-    static constexpr int LDQ = DK + VEC;
-    static constexpr int LDT = C + VEC;
-    static constexpr size_t Q = (size_t)C * LDQ * sizeof(E);
-    static constexpr size_t KT = (size_t)DK * LDT * sizeof(E);
-    static constexpr size_t VT = (size_t)DVB * LDT * sizeof(E);
-    static constexpr size_t BYTES = Q + KT + VT + 3 * C * sizeof(float);
+template <int DK, int DV, int CT, typename E> struct ScanLds {
+    using G = Geo<DK, DV, E>;
+    // operand copy: value-head shared part | this workgroup's U0 tiles | key-head block
+    static constexpr int U0K = 4 * CT;
+    static constexpr int AK = G::SV + U0K + G::KBLK;
+    static constexpr int A_U0 = G::SV, A_Q = G::SV + U0K, A_KT = G::SV + U0K + G::NQF;
+    static constexpr size_t A = (size_t)AK * 1024;
+    static constexpr size_t U = (size_t)CT * 4 * 64 * 16;
+    static constexpr size_t S = (size_t)CT * G::NMT * 64 * 16;
+    static constexpr size_t BYTES = A + U + S;
 };
 
-template <int DK, int DV, int NW, typename E, typename OT>
-__global__ __launch_bounds__(NW * 64) void scan_kernel(ScanParams sp)
+template <int DK, int DV, int CT, typename E, typename OT>
+__global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
 {
     using M = Mfma<E>;
     using SP = Split<E>;
+    using G = Geo<DK, DV, E>;
+    using L = ScanLds<DK, DV, CT, E>;
     using Frag = typename M::Frag;
-    using L = ScanLds<DK, NW, E>;
-    using V = ElemVec<E>;
-    constexpr int KB = M::KB, VEC = L::VEC, DVB = L::DVB, NS = SP::N;
-    constexpr int LDQ = L::LDQ, LDT = L::LDT;
-    constexpr int NKD = DK / KB, NKC = C / KB, NMT = DK / 16;
-    constexpr int NWF = 4 * NKD, NTF = 4 * NKC;
-    constexpr int NT = NW * 64;
-    constexpr int VPR = DK / VEC;        // 16-byte vectors per q/k row
-    constexpr int VPB = DVB / VEC;       // 16-byte vectors per v row block
+    constexpr int KB = M::KB, TPB = M::TPB, NS = SP::N;
+    constexpr int NKD = G::NKD, NKC = G::NKC, NMT = G::NMT, NCT = G::NCT;
+    constexpr int NT = CT * 256;
+    constexpr int SV16 = G::SV * 64;              // 16-byte words in the value-head part
+    constexpr int U016 = L::U0K * 64;             // ... in this workgroup's U0 tiles
+    constexpr int A16 = L::AK * 64;               // ... in the LDS operand copy
+    constexpr int PF = (A16 + NT - 1) / NT;
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    E *sQ = reinterpret_cast<E *>(smem);
-    E *sKT = reinterpret_cast<E *>(smem + L::Q);
-    E *sVT = reinterpret_cast<E *>(smem + L::Q + L::KT);
-    float *sScal = reinterpret_cast<float *>(smem + L::Q + L::KT + L::VT);
+    u32x4 *sA = reinterpret_cast<u32x4 *>(smem);
+    floatx4 *sU = reinterpret_cast<floatx4 *>(smem + L::A);            // [CT][4][64]
+    floatx4 *sS = reinterpret_cast<floatx4 *>(smem + L::A + L::U);     // [CT][NMT][64]
+    const float *sScal = reinterpret_cast<const float *>(sA + G::F_SCAL * 64);
 
-    const int i = blockIdx.x, h = blockIdx.y, cb = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int i = blockIdx.x, h = blockIdx.y, cg = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int ctl = wv >> 2, rt = wv & 3;      // column tile in the group, token-row / dk-block role
     const int n = lane & 15, qd = lane >> 4;
     const int kh = h / (sp.H_v / sp.H_k);
-    const int col0 = cb * DVB + 16 * w;
-    const E *qg = static_cast<const E *>(sp.q);
-    const E *kg = static_cast<const E *>(sp.k);
-    const E *vg = static_cast<const E *>(sp.v);
+    const int ct = cg * CT + ctl;
+    const int col0 = 16 * ct;
     OT *og = static_cast<OT *>(sp.out);
 
-    // state columns col0..col0+15 in accumulator layout
-    floatx4 S[NMT];
-    const int sin = sp.state_in ? sp.slot_in[i] : -1;
-    if (sin >= 0) {
-        const float *base = sp.state_in + (int64_t)sin * sp.slot_stride + (int64_t)h * DK * DV + col0 + n;
+    auto frag = [&](int f) -> Frag { return __builtin_bit_cast(Frag, sA[f * 64 + lane]); };
+
+    // initial state: each wave loads the dk blocks it owns (kb = rt mod 4)
+    {
+        const int sin = sp.state_in ? sp.slot_in[i] : -1;
+        const float *base = sin >= 0 ? sp.state_in + (int64_t)sin * sp.slot_stride + (int64_t)h * DK * DV + col0 + n
+                                     : nullptr;
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt)
+        for (int mt = 0; mt < NMT; ++mt) {
+            if ((mt / TPB) % 4 != rt) continue;
+            floatx4 v = {0.f, 0.f, 0.f, 0.f};
+            if (base) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) S[mt][j] = base[(int64_t)(16 * mt + 4 * qd + j) * DV];
-    } else {
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) S[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < 4; ++j) v[j] = base[(int64_t)(16 * mt + 4 * qd + j) * DV];
+            }
+            sS[(ctl * NMT + mt) * 64 + lane] = v;
+        }
     }
 
     const int cs = sp.cstart[i], ce = sp.cstart[i + 1];
-    for (int c = cs; c < ce; ++c) {
-        const ChunkEntry e = sp.ent[c];
-        const int t0 = e.t0, len = e.len;
-        const char *blk = sp.blocks + ((size_t)c * sp.H_v + h) * sp.block;
-        const char *Wf = blk;
-        const char *Tf = blk + NWF * 1024;
-        const char *Pf = blk + (NWF + NS * NTF) * 1024;
-        const float *scal = reinterpret_cast<const float *>(blk + (NWF + 2 * NS * NTF) * 1024);
+    const size_t vstride = (size_t)G::VBLK * 1024, kstride = (size_t)G::KBLK * 1024;
+    const char *vbase = sp.vblocks + (size_t)h * vstride;
+    const char *kbase = sp.kblocks + (size_t)kh * kstride;
+    const size_t vstep = (size_t)sp.H_v * vstride, kstep = (size_t)sp.H_k * kstride;
+    const int u0_src = G::F_U0 * 64 + cg * U016;  // this workgroup's U0 tiles, in 16-byte words
 
-        // stage raw Q (row-major), K^T and this block's V^T columns
-        for (int vi = tid; vi < C * VPR; vi += NT) {
-            const int r = vi / VPR, cv = vi % VPR;
-            uint4 kv = make_uint4(0, 0, 0, 0), qv = kv;
-            if (r < len) {
-                const size_t off = ((size_t)(t0 + r) * sp.H_k + kh) * DK + (size_t)cv * VEC;
-                kv = *reinterpret_cast<const uint4 *>(kg + off);
-                qv = *reinterpret_cast<const uint4 *>(qg + off);
-            }
-            *reinterpret_cast<uint4 *>(sQ + r * LDQ + cv * VEC) = qv;
+    // register prefetch of one chunk: this thread's share of the LDS operand copy
+    u32x4 pre[PF];
+    if (cs < ce) {
+        const u32x4 *vb = reinterpret_cast<const u32x4 *>(vbase + (size_t)cs * vstep);
+        const u32x4 *kb = reinterpret_cast<const u32x4 *>(kbase + (size_t)cs * kstep);
 #pragma unroll
-            for (int x = 0; x < VEC; ++x) sKT[(cv * VEC + x) * LDT + r] = V::raw(kv, x);
+        for (int p = 0; p < PF; ++p) {
+            const int idx = tid + p * NT;
+            if (idx < A16)
+                pre[p] = idx < SV16 ? vb[idx] : idx < SV16 + U016 ? vb[u0_src + idx - SV16]
+                                                                  : kb[idx - SV16 - U016];
         }
-        for (int vi = tid; vi < C * VPB; vi += NT) {
-            const int r = vi / VPB, cv = vi % VPB;
-            uint4 vv = make_uint4(0, 0, 0, 0);
-            if (r < len)
-                vv = *reinterpret_cast<const uint4 *>(vg + ((size_t)(t0 + r) * sp.H_v + h) * DV + cb * DVB + cv * VEC);
-#pragma unroll
-            for (int x = 0; x < VEC; ++x) sVT[(cv * VEC + x) * LDT + r] = V::raw(vv, x);
-        }
-        for (int x = tid; x < 129; x += NT) sScal[x] = scal[x];
-        __syncthreads();
-
-        // the incoming state as two-term B operands, one per dk block
-        Frag Sh[NKD], Sl[NKD];
-#pragma unroll
-        for (int kb = 0; kb < NKD; ++kb) SP::acc(S, kb, 1.f, Sh[kb], Sl[kb]);
-
-        // U = T' V - W S   (token rows, this wave's 16 columns)
-        floatx4 U[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            U[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < NKC; ++kb)
-                if (kb * KB <= 16 * rt + 15) {
-                    const Frag vb = M::load_rm(sVT + (16 * w + n) * LDT, kb * KB, qd);
-                    M::mma(U[rt], load_frag<E>(Tf, rt * NKC + kb, lane), vb);
-                    if constexpr (NS == 2) M::mma(U[rt], load_frag<E>(Tf + NTF * 1024, rt * NKC + kb, lane), vb);
-                }
-#pragma unroll
-            for (int kb = 0; kb < NKD; ++kb) {
-                const Frag wa = load_frag<E>(Wf, rt * NKD + kb, lane);
-                floatx4 t = {0.f, 0.f, 0.f, 0.f};
-                M::mma(t, wa, Sh[kb]);
-                if constexpr (NS == 2) M::mma(t, wa, Sl[kb]);
-                U[rt] -= t;
-            }
-        }
-
-        // the chunk deltas as two-term B operands (K blocks over tokens)
-        Frag Uh[NKC], Ul[NKC];
-#pragma unroll
-        for (int kb = 0; kb < NKC; ++kb) SP::acc(U, kb, 1.f, Uh[kb], Ul[kb]);
-
-        // O = qs * (Q S) + P U
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            floatx4 O = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < NKD; ++kb) {
-                const Frag qa = M::load_rm(sQ + (16 * rt + n) * LDQ, kb * KB, qd);
-                M::mma(O, qa, Sh[kb]);
-                if constexpr (NS == 2) M::mma(O, qa, Sl[kb]);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) O[j] *= sScal[16 * rt + 4 * qd + j];
-#pragma unroll
-            for (int kb = 0; kb < NKC; ++kb)
-                if (kb * KB <= 16 * rt + 15) {
-                    const Frag ph = load_frag<E>(Pf, rt * NKC + kb, lane);
-                    M::mma(O, ph, Uh[kb]);
-                    if constexpr (NS == 2) {
-                        M::mma(O, ph, Ul[kb]);
-                        M::mma(O, load_frag<E>(Pf + NTF * 1024, rt * NKC + kb, lane), Uh[kb]);
-                    }
-                }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * rt + 4 * qd + j;
-                if (r < len) og[((size_t)(t0 + r) * sp.H_v + h) * DV + col0 + n] = from_f32<OT>(O[j]);
-            }
-        }
-
-        // S = gn S + K^T (ks * U)
-        const float gn = sScal[128];
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) S[mt][j] *= gn;
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) U[rt][j] *= sScal[64 + 16 * rt + 4 * qd + j];
-#pragma unroll
-        for (int kb = 0; kb < NKC; ++kb) SP::acc(U, kb, 1.f, Uh[kb], Ul[kb]);
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) {
-                const Frag ka = M::load_rm(sKT + (16 * mt + n) * LDT, kb * KB, qd);
-                M::mma(S[mt], ka, Uh[kb]);
-                if constexpr (NS == 2) M::mma(S[mt], ka, Ul[kb]);
-            }
-        __syncthreads();
     }
+    lds_sync();
+
+    // The output tile of chunk c is stored at the top of iteration c+1, before
+    // that iteration's prefetch loads: the only wait for memory in the loop
+    // (publishing the prefetched operands) then covers operations issued a
+    // whole chunk of work earlier.
+    const uint32_t row_bytes = (uint32_t)(sp.H_v * DV * sizeof(OT));
+    floatx4 Oprev = {0.f, 0.f, 0.f, 0.f};
+    int t0prev = 0, lenprev = 0;
+    auto store_out = [&](const floatx4 &O, int t0o, int leno) {
+        // rows >= len of a partial chunk fall outside the buffer and are dropped
+        const __amdgpu_buffer_rsrc_t ob =
+            raw_buffer(og + ((size_t)t0o * sp.H_v + h) * DV + col0, (uint32_t)leno * row_bytes);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            buffer_store(from_f32<OT>(O[j]), ob,
+                         (uint32_t)(16 * rt + 4 * qd + j) * row_bytes + n * (uint32_t)sizeof(OT));
+    };
+
+    for (int c = cs; c < ce; ++c) {
+        // publish this chunk's operands, store the previous chunk's output,
+        // then prefetch the next chunk's operands
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int idx = tid + p * NT;
+            if (idx < A16) sA[idx] = pre[p];
+        }
+        store_out(Oprev, t0prev, lenprev);
+        if (c + 1 < ce) {
+            const u32x4 *vb = reinterpret_cast<const u32x4 *>(vbase + (size_t)(c + 1) * vstep);
+            const u32x4 *kb = reinterpret_cast<const u32x4 *>(kbase + (size_t)(c + 1) * kstep);
+#pragma unroll
+            for (int p = 0; p < PF; ++p) {
+                const int idx = tid + p * NT;
+                if (idx < A16)
+                    pre[p] = idx < SV16 ? vb[idx] : idx < SV16 + U016 ? vb[u0_src + idx - SV16]
+                                                                      : kb[idx - SV16 - U016];
+            }
+        }
+        lds_sync();
+        const int t0 = __builtin_amdgcn_readfirstlane(__float_as_int(sScal[129]));
+        const int len = __builtin_amdgcn_readfirstlane(__float_as_int(sScal[130]));
+        const floatx4 u0 = __builtin_bit_cast(floatx4, sA[(L::A_U0 + ctl * 4 + rt) * 64 + lane]);
+
+        // phase A (token rows rt): U = U0 - W S and Q S, both with the
+        // incoming state as two-term B operands
+        floatx4 St[NMT];
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) St[mt] = sS[(ctl * NMT + mt) * 64 + lane];
+        floatx4 WS = {0.f, 0.f, 0.f, 0.f}, OQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKD; ++kb) {
+            Frag sh, sl;
+            SP::acc(St, kb, 1.f, sh, sl);
+            const Frag wa = frag(G::F_W + rt * NKD + kb);
+            const Frag qa = frag(L::A_Q + rt * NKD + kb);
+            M::mma(WS, wa, sh);
+            M::mma(OQ, qa, sh);
+            if constexpr (NS == 2) {
+                M::mma(WS, wa, sl);
+                M::mma(OQ, qa, sl);
+            }
+        }
+        const floatx4 U = u0 - WS;
+        sU[(ctl * 4 + rt) * 64 + lane] = U;
+        lds_sync();
+
+        // phase B: output rows rt, then the state update of dk block(s) rt
+        floatx4 Ut[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ut[r] = sU[(ctl * 4 + r) * 64 + lane];
+        floatx4 O;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) O[j] = OQ[j] * sScal[16 * rt + 4 * qd + j];
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            if (kc * KB > 16 * rt + 15) continue;
+            Frag uh, ul;
+            SP::acc(Ut, kc, 1.f, uh, ul);
+            const Frag ph = frag(G::F_PH + rt * NKC + kc);
+            M::mma(O, ph, uh);
+            if constexpr (NS == 2) {
+                M::mma(O, ph, ul);
+                M::mma(O, frag(G::F_PL + rt * NKC + kc), uh);
+            }
+        }
+        Oprev = O;
+        t0prev = t0;
+        lenprev = len;
+
+        if (rt < NKD) {
+            const float gn = sScal[128];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Ut[r][j] *= sScal[64 + 16 * r + 4 * qd + j];
+            Frag kh_[NKC], kl_[NKC];
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) SP::acc(Ut, kc, 1.f, kh_[kc], kl_[kc]);
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) {
+                if ((mt / TPB) % 4 != rt) continue;
+                floatx4 Sm = St[mt] * gn;
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) {
+                    const Frag ka = frag(L::A_KT + mt * NKC + kc);
+                    M::mma(Sm, ka, kh_[kc]);
+                    if constexpr (NS == 2) M::mma(Sm, ka, kl_[kc]);
+                }
+                sS[(ctl * NMT + mt) * 64 + lane] = Sm;
+            }
+        }
+        lds_sync();
+    }
+
+    store_out(Oprev, t0prev, lenprev);     // last chunk (a zero-length store if none)
 
     const int sout = sp.slot_out[i];
     if (sout >= 0) {
         float *base = sp.state_out + (int64_t)sout * sp.slot_stride + (int64_t)h * DK * DV + col0 + n;
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt)
+        for (int mt = 0; mt < NMT; ++mt) {
+            if ((mt / TPB) % 4 != rt) continue;
+            const floatx4 v = sS[(ctl * NMT + mt) * 64 + lane];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) base[(int64_t)(16 * mt + 4 * qd + j) * DV] = S[mt][j];
+            for (int j = 0; j < 4; ++j) base[(int64_t)(16 * mt + 4 * qd + j) * DV] = v[j];
+        }
     }
 }
 
@@ -672,7 +808,7 @@ struct WsPtrs {
     int32_t *hdr;
     ChunkEntry *ent;
     int32_t *cstart;
-    char *blocks;
+    char *vblocks, *kblocks;
 };
 
 WsPtrs ws_ptrs(const Problem &p, const PrefillArgs &a)
@@ -683,11 +819,12 @@ WsPtrs ws_ptrs(const Problem &p, const PrefillArgs &a)
     w.hdr = reinterpret_cast<int32_t *>(ws);
     w.ent = reinterpret_cast<ChunkEntry *>(ws + w.L.entries);
     w.cstart = reinterpret_cast<int32_t *>(ws + w.L.cstart);
-    w.blocks = ws + w.L.blocks;
+    w.vblocks = ws + w.L.vblocks;
+    w.kblocks = ws + w.L.kblocks;
     return w;
 }
 
-template <int DK, typename E>
+template <int DK, int DV, typename E>
 hipError_t prepare_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
 {
     const WsPtrs w = ws_ptrs(p, a);
@@ -695,11 +832,12 @@ hipError_t prepare_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
                        (int)a.total_tokens, w.L.max_chunks, w.hdr, w.ent, w.cstart);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.total_tokens == 0) return e;
-    PrepParams pp{a.q, a.k, a.g, a.beta, w.hdr, w.ent, w.blocks, w.L.block, p.H_k, p.H_v, p.scale, p.eps};
-    constexpr size_t lds = PrepLds<DK, E>::BYTES;
-    e = set_lds(prep_kernel<DK, E>, lds);
+    PrepParams pp{a.q, a.k, a.v, a.g, a.beta, w.hdr, w.ent, w.vblocks, w.kblocks,
+                  p.H_k, p.H_v, p.scale, p.eps};
+    constexpr size_t lds = PrepLds<DK, DV, E>::BYTES;
+    e = set_lds(prep_kernel<DK, DV, E>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prep_kernel<DK, E>), dim3(w.L.max_chunks, p.H_k), dim3(256), lds, st, pp);
+    hipLaunchKernelGGL((prep_kernel<DK, DV, E>), dim3(w.L.max_chunks, p.H_k), dim3(256), lds, st, pp);
     return hipGetLastError();
 }
 
@@ -707,21 +845,32 @@ template <int DK, int DV, typename E, typename OT>
 hipError_t scan_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
 {
     const WsPtrs w = ws_ptrs(p, a);
-    constexpr int NW = DV >= 64 ? 4 : DV / 16;
-    ScanParams sp{a.q, a.k, a.v, a.state_in, a.state_out, a.out, a.slot_in, a.slot_out, w.cstart,
-                  w.ent, w.blocks, w.L.block, p.H_k, p.H_v, p.slot_stride};
-    constexpr size_t lds = ScanLds<DK, NW, E>::BYTES;
-    hipError_t e = set_lds(scan_kernel<DK, DV, NW, E, OT>, lds);
+    constexpr int CT = 2;    // column tiles per workgroup (d_v >= 32 always)
+    ScanParams sp{a.state_in, a.state_out, a.out, a.slot_in, a.slot_out, w.cstart, w.ent,
+                  w.vblocks, w.kblocks, p.H_k, p.H_v, p.slot_stride};
+    constexpr size_t lds = ScanLds<DK, DV, CT, E>::BYTES;
+    hipError_t e = set_lds(scan_kernel<DK, DV, CT, E, OT>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_kernel<DK, DV, NW, E, OT>), dim3(a.n_seqs, p.H_v, DV / (16 * NW)),
-                       dim3(NW * 64), lds, st, sp);
+    hipLaunchKernelGGL((scan_kernel<DK, DV, CT, E, OT>), dim3(a.n_seqs, p.H_v, DV / (16 * CT)),
+                       dim3(CT * 256), lds, st, sp);
     return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t prepare_dv(const Problem &p, const PrefillArgs &a, hipStream_t st)
+{
+    return p.bf16 ? prepare_t<DK, DV, bf16_t>(p, a, st) : prepare_t<DK, DV, float>(p, a, st);
 }
 
 template <int DK>
 hipError_t prepare_dk(const Problem &p, const PrefillArgs &a, hipStream_t st)
 {
-    return p.bf16 ? prepare_t<DK, bf16_t>(p, a, st) : prepare_t<DK, float>(p, a, st);
+    switch (p.d_v) {
+    case 32: return prepare_dv<DK, 32>(p, a, st);
+    case 64: return prepare_dv<DK, 64>(p, a, st);
+    case 128: return prepare_dv<DK, 128>(p, a, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int DK, int DV>

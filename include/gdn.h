@@ -116,8 +116,9 @@ const char *gdn_last_error(void);
  * Workspace needed by gdn_chunked_prefill for a call with n_seqs sequences
  * and total_tokens tokens, written to *bytes.  Host-only, no device work.
  * The workspace holds the chunk table and the per-chunk WY factors
- * (build_delta_net_chunking: the solved triangular matrix, k_cumdecay and
- * the decayed q.k attention) between the two kernels.
+ * (build_delta_net_chunking: k_cumdecay, the beta-weighted values and the
+ * decayed q.k attention, plus q and k in matrix-core operand order) between
+ * the two phases.
  */
 gdn_status gdn_prefill_workspace_size(const gdn_dims *dims, int32_t n_seqs,
                                       int64_t total_tokens, size_t *bytes);
@@ -161,26 +162,25 @@ gdn_status gdn_chunked_prefill(const gdn_dims *dims,
  *
  * gdn_prefill_prepare: everything that does not depend on the carried state
  * (build_delta_net_chunking: g_cumsum, decay_mask, the beta*(k k^T)*decay
- * matrix and its triangular solve, k_cumdecay, and the decayed q.k
- * attention), written into `workspace` together with the chunk table built
- * from cu_seqlens.  Reads q, k, g, beta, cu_seqlens.
+ * matrix and its triangular solve, k_cumdecay, the beta-weighted values
+ * ("value" = T diag(beta) V) and the decayed q.k attention), written into
+ * `workspace` together with the chunk table built from cu_seqlens.  Reads q,
+ * k, v, g, beta, cu_seqlens.
  *
  * gdn_prefill_scan: the state-dependent part (v_prime / v_new, attn_inter +
  * v_attn, and the chunk-end state update), chunk after chunk per sequence,
- * reading the workspace left by a prepare call with the same dims, q, k, g,
- * beta, cu_seqlens, n_seqs and total_tokens (the caller orders the two, e.g.
- * on one stream or with an event).  Reads q, k, v, the state pool; writes out
- * and the state pool.  Arguments, layouts and errors as for
- * gdn_chunked_prefill.
+ * reading only the workspace left by a prepare call with the same dims,
+ * n_seqs and total_tokens (the caller orders the two, e.g. on one stream or
+ * with an event) and the state pool; writes out and the state pool.
+ * Arguments, layouts and errors as for gdn_chunked_prefill.
  */
 gdn_status gdn_prefill_prepare(const gdn_dims *dims, const void *q, const void *k,
-                               const float *g, const float *beta,
+                               const void *v, const float *g, const float *beta,
                                const int32_t *cu_seqlens, int32_t n_seqs,
                                int64_t total_tokens, void *workspace,
                                size_t workspace_bytes, void *stream);
 
-gdn_status gdn_prefill_scan(const gdn_dims *dims, const void *q, const void *k,
-                            const void *v, const float *state_in, float *state_out,
+gdn_status gdn_prefill_scan(const gdn_dims *dims, const float *state_in, float *state_out,
                             void *out, const int32_t *slot_in, const int32_t *slot_out,
                             int32_t n_seqs, int64_t total_tokens, const void *workspace,
                             size_t workspace_bytes, void *stream);

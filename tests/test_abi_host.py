@@ -50,7 +50,9 @@ def test_workspace_size_grows_with_tokens_and_is_aligned():
     c = gdn.workspace_size(_dims(), 8, 4096)
     assert 0 < a < b and a < c
     # per (64-token chunk, value head): W, T', P fragments + scalars
-    blocks = 64 * 32 * (16 + 2 * 8 + 2 * 8 + 1) * 1024   # 64 more chunks x 32 value heads
+    # 64 more chunks x (32 value-head blocks: W 16 + P 2x8 + scalars 1 + U0 32 KiB,
+    #                   16 key-head blocks: q 16 + k^T 16 KiB)
+    blocks = 64 * (32 * (16 + 16 + 1 + 32) + 16 * 32) * 1024
     assert 0 <= (b - a) - blocks <= 64 * 16 + 256  # + their chunk-table entries
     f = gdn.workspace_size(_dims(dtype=gdn.GDN_F32), 1, 4096)
     assert f > a
@@ -111,17 +113,16 @@ def test_split_phase_validation():
     P = ctypes.c_void_p
     d = _dims()
     prep = lambda **o: gdn.lib.gdn_prefill_prepare(
-        ctypes.byref(d), P(o.get("q", FAKE)), P(o.get("k", FAKE)), P(o.get("g", FAKE)),
-        P(o.get("beta", FAKE)), P(o.get("cu", FAKE)), o.get("n", 1), o.get("T", 64),
-        P(o.get("ws", FAKE)), o.get("wsb", 1 << 40), None)
-    assert prep(q=0) == 1 and prep(cu=0) == 1 and prep(g=FAKE + 1) == 1
+        ctypes.byref(d), P(o.get("q", FAKE)), P(o.get("k", FAKE)), P(o.get("v", FAKE)),
+        P(o.get("g", FAKE)), P(o.get("beta", FAKE)), P(o.get("cu", FAKE)), o.get("n", 1),
+        o.get("T", 64), P(o.get("ws", FAKE)), o.get("wsb", 1 << 40), None)
+    assert prep(q=0) == 1 and prep(v=0) == 1 and prep(cu=0) == 1 and prep(g=FAKE + 1) == 1
     assert prep(n=0) == 1 and prep(wsb=16) == 3 and prep(ws=0) == 3
     scan = lambda **o: gdn.lib.gdn_prefill_scan(
-        ctypes.byref(d), P(o.get("q", FAKE)), P(o.get("k", FAKE)), P(o.get("v", FAKE)),
-        P(o.get("si", FAKE)), P(o.get("so", FAKE)), P(o.get("out", FAKE)), P(o.get("sin", FAKE)),
-        P(o.get("sout", FAKE)), o.get("n", 1), o.get("T", 64), P(o.get("ws", FAKE)),
-        o.get("wsb", 1 << 40), None)
-    assert scan(v=0) == 1 and scan(so=0) == 1 and scan(out=FAKE + 4) == 1
+        ctypes.byref(d), P(o.get("si", FAKE)), P(o.get("so", FAKE)), P(o.get("out", FAKE)),
+        P(o.get("sin", FAKE)), P(o.get("sout", FAKE)), o.get("n", 1), o.get("T", 64),
+        P(o.get("ws", FAKE)), o.get("wsb", 1 << 40), None)
+    assert scan(so=0) == 1 and scan(out=FAKE + 4) == 1 and scan(sin=0) == 1
     assert scan(T=-2) == 1 and scan(wsb=16) == 3
 
 

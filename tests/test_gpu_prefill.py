@@ -131,10 +131,10 @@ def test_split_phase_prefill_matches_single_call():
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     ev = torch.cuda.Event()
     torch.cuda.synchronize()
-    plan.prepare(d["q"], d["k"], d["g"], d["beta"], d["cu"], stream=s1)
+    plan.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], stream=s1)
     ev.record(s1)
     s2.wait_event(ev)
-    plan.scan(d["q"], d["k"], d["v"], d["pool"], pool, out, d["slot_in"], d["slot_out"], stream=s2)
+    plan.scan(d["pool"], pool, out, d["slot_in"], d["slot_out"], stream=s2)
     torch.cuda.synchronize()
     assert torch.equal(out, out_ref) and torch.equal(pool, pool_ref)
 
