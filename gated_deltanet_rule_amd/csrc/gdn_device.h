@@ -9,6 +9,7 @@ namespace gdn {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // raw 16-byte word
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // Storage tag for bfloat16 tensors (raw 16-bit patterns in memory).
 struct bf16_t {
@@ -32,7 +33,7 @@ template <typename E> __device__ __forceinline__ E from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
     bf16_t r;
-    r.bits = bf16_bits_rne(x);
+    r.bits = __builtin_bit_cast(uint16_t, (__bf16)x);   // v_cvt_pk_bf16_f32: round to nearest even
     return r;
 }
 

@@ -581,16 +581,47 @@ struct ScanParams {
 
 template <int DK, int DV, int CT, typename E> struct ScanLds {
     using G = Geo<DK, DV, E>;
-    // operand copy: value-head shared part | this workgroup's U0 tiles | key-head block
-    static constexpr int U0K = 4 * CT;
-    static constexpr int AK = G::SV + U0K + G::KBLK;
-    static constexpr int A_U0 = G::SV, A_Q = G::SV + U0K, A_KT = G::SV + U0K + G::NQF;
-    static constexpr size_t A = (size_t)AK * 1024;
-    static constexpr size_t U = (size_t)CT * 4 * 64 * 16;
-    static constexpr size_t S = (size_t)CT * G::NMT * 64 * 16;
-    static constexpr size_t BYTES = A + U + S;
+    // exchange only, per column tile: the state as two-term B fragments per
+    // dk block, and the chunk deltas U and ks*U as two-term B fragments per
+    // token block (each 1 KiB = 64 lanes x 16 bytes)
+    static constexpr int NSP = Split<E>::N;
+    static constexpr size_t SF = (size_t)CT * G::NKD * NSP * 1024;
+    static constexpr size_t UF = (size_t)CT * G::NKC * NSP * 1024;
+    static constexpr size_t BYTES = SF + 2 * UF;
 };
 
+// Two-term conversion of one accumulator tile (4 values per lane).  For bf16
+// operands it fills `part` (0 or 1) of a K block's 16-byte lane slot: 8 bytes
+// of hi and 8 bytes of lo bf16; fp32 operands have a single term filling the
+// whole slot.
+template <typename E> struct TileOut;
+template <> struct TileOut<bf16_t> {
+    __device__ static __forceinline__ void put(u32x4 *hi, u32x4 *lo, int lane, int part, floatx4 v) {
+        bf16x4 h, l;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            h[j] = (__bf16)v[j];
+            l[j] = (__bf16)(v[j] - (float)h[j]);
+        }
+        *reinterpret_cast<bf16x4 *>(reinterpret_cast<char *>(hi + lane) + 8 * part) = h;
+        *reinterpret_cast<bf16x4 *>(reinterpret_cast<char *>(lo + lane) + 8 * part) = l;
+    }
+};
+template <> struct TileOut<float> {
+    __device__ static __forceinline__ void put(u32x4 *hi, u32x4 *lo, int lane, int part, floatx4 v) {
+        (void)lo;
+        (void)part;
+        hi[lane] = __builtin_bit_cast(u32x4, v);
+    }
+};
+
+// Scan over a sequence's chunks for one value head and CT column tiles of 16
+// state columns.  Wave (ctl, rt): token rows 16*rt.. of column tile ctl in
+// phase A and for the output; owner of dk blocks kb = rt (mod 4) of the state.
+// Every operand of a chunk is loaded from the workspace straight into the
+// registers of the wave that uses it, re-issued for the next chunk right
+// after its last use in this one, so its latency overlaps a chunk of work;
+// LDS carries only the per-chunk exchange (state and delta fragments).
 template <int DK, int DV, int CT, typename E, typename OT>
 __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
 {
@@ -600,45 +631,48 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
     using L = ScanLds<DK, DV, CT, E>;
     using Frag = typename M::Frag;
     constexpr int KB = M::KB, TPB = M::TPB, NS = SP::N;
-    constexpr int NKD = G::NKD, NKC = G::NKC, NMT = G::NMT, NCT = G::NCT;
-    constexpr int NT = CT * 256;
-    constexpr int SV16 = G::SV * 64;              // 16-byte words in the value-head part
-    constexpr int U016 = L::U0K * 64;             // ... in this workgroup's U0 tiles
-    constexpr int A16 = L::AK * 64;               // ... in the LDS operand copy
-    constexpr int PF = (A16 + NT - 1) / NT;
+    constexpr int NKD = G::NKD, NKC = G::NKC;
+    constexpr int NOWN = (NKD + 3) / 4;           // dk blocks of the state owned per wave (max)
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    u32x4 *sA = reinterpret_cast<u32x4 *>(smem);
-    floatx4 *sU = reinterpret_cast<floatx4 *>(smem + L::A);            // [CT][4][64]
-    floatx4 *sS = reinterpret_cast<floatx4 *>(smem + L::A + L::U);     // [CT][NMT][64]
-    const float *sScal = reinterpret_cast<const float *>(sA + G::F_SCAL * 64);
+    u32x4 *sSf = reinterpret_cast<u32x4 *>(smem);                         // [CT][NKD][NS][64]
+    u32x4 *sUf = reinterpret_cast<u32x4 *>(smem + L::SF);                 // [CT][NKC][NS][64]
+    u32x4 *sKf = reinterpret_cast<u32x4 *>(smem + L::SF + L::UF);         // [CT][NKC][NS][64]
 
     const int i = blockIdx.x, h = blockIdx.y, cg = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int ctl = wv >> 2, rt = wv & 3;      // column tile in the group, token-row / dk-block role
+    const int ctl = wv >> 2, rt = wv & 3;
     const int n = lane & 15, qd = lane >> 4;
     const int kh = h / (sp.H_v / sp.H_k);
     const int ct = cg * CT + ctl;
     const int col0 = 16 * ct;
     OT *og = static_cast<OT *>(sp.out);
 
-    auto frag = [&](int f) -> Frag { return __builtin_bit_cast(Frag, sA[f * 64 + lane]); };
+    auto xfrag = [&](const u32x4 *base, int f) -> Frag { return __builtin_bit_cast(Frag, base[f * 64 + lane]); };
+    u32x4 *mySf = sSf + ctl * (NKD * NS * 64);
+    u32x4 *myUf = sUf + ctl * (NKC * NS * 64);
+    u32x4 *myKf = sKf + ctl * (NKC * NS * 64);
 
-    // initial state: each wave loads the dk blocks it owns (kb = rt mod 4)
+    // state: registers of the owning wave, published as two-term B fragments
+    floatx4 Sreg[NOWN][TPB];
     {
         const int sin = sp.state_in ? sp.slot_in[i] : -1;
         const float *base = sin >= 0 ? sp.state_in + (int64_t)sin * sp.slot_stride + (int64_t)h * DK * DV + col0 + n
                                      : nullptr;
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
-            if ((mt / TPB) % 4 != rt) continue;
-            floatx4 v = {0.f, 0.f, 0.f, 0.f};
-            if (base) {
+        for (int o = 0; o < NOWN; ++o) {
+            const int kb = rt + 4 * o;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = base[(int64_t)(16 * mt + 4 * qd + j) * DV];
+            for (int t = 0; t < TPB; ++t) {
+                floatx4 v = {0.f, 0.f, 0.f, 0.f};
+                if (base && kb < NKD) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = base[(int64_t)(16 * (kb * TPB + t) + 4 * qd + j) * DV];
+                }
+                Sreg[o][t] = v;
+                if (kb < NKD) TileOut<E>::put(mySf + (kb * NS) * 64, mySf + (kb * NS + NS - 1) * 64, lane, t, v);
             }
-            sS[(ctl * NMT + mt) * 64 + lane] = v;
         }
     }
 
@@ -647,147 +681,170 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
     const char *vbase = sp.vblocks + (size_t)h * vstride;
     const char *kbase = sp.kblocks + (size_t)kh * kstride;
     const size_t vstep = (size_t)sp.H_v * vstride, kstep = (size_t)sp.H_k * kstride;
-    const int u0_src = G::F_U0 * 64 + cg * U016;  // this workgroup's U0 tiles, in 16-byte words
+    auto vblk = [&](int c) { return reinterpret_cast<const u32x4 *>(vbase + (size_t)c * vstep); };
+    auto kblk = [&](int c) { return reinterpret_cast<const u32x4 *>(kbase + (size_t)c * kstep); };
+    auto vfrag = [&](int c, int f) -> Frag { return __builtin_bit_cast(Frag, vblk(c)[f * 64 + lane]); };
+    auto kfrag = [&](int c, int f) -> Frag { return __builtin_bit_cast(Frag, kblk(c)[f * 64 + lane]); };
+    auto scal4 = [&](int c, int off) -> floatx4 {
+        return *reinterpret_cast<const floatx4 *>(reinterpret_cast<const float *>(vblk(c) + G::F_SCAL * 64) + off);
+    };
+    auto scal1 = [&](int c, int off) -> float {
+        return reinterpret_cast<const float *>(vblk(c) + G::F_SCAL * 64)[off];
+    };
+    const int u0f = G::F_U0 + ct * 4 + rt;         // accumulator tile (ct, rt) of U0
+    const int ro = 16 * rt + 4 * qd;               // first of this lane's 4 token rows
 
-    // register prefetch of one chunk: this thread's share of the LDS operand copy
-    u32x4 pre[PF];
-    if (cs < ce) {
-        const u32x4 *vb = reinterpret_cast<const u32x4 *>(vbase + (size_t)cs * vstep);
-        const u32x4 *kb = reinterpret_cast<const u32x4 *>(kbase + (size_t)cs * kstep);
+    // operands of the current chunk (loaded for chunk cs before the loop,
+    // reloaded for the next chunk right after their last use)
+    const int c0 = cs < ce ? cs : 0;
+    Frag Wf[NKD], Qf[NKD], Ph[NKC], Pl[NKC], Kf[NOWN * TPB][NKC];
 #pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int idx = tid + p * NT;
-            if (idx < A16)
-                pre[p] = idx < SV16 ? vb[idx] : idx < SV16 + U016 ? vb[u0_src + idx - SV16]
-                                                                  : kb[idx - SV16 - U016];
-        }
+    for (int kb = 0; kb < NKD; ++kb) {
+        Wf[kb] = vfrag(c0, G::F_W + rt * NKD + kb);
+        Qf[kb] = kfrag(c0, G::F_Q + rt * NKD + kb);
     }
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+        Ph[kc] = vfrag(c0, G::F_PH + rt * NKC + kc);
+        if constexpr (NS == 2) Pl[kc] = vfrag(c0, G::F_PL + rt * NKC + kc);
+    }
+#pragma unroll
+    for (int o = 0; o < NOWN; ++o)
+#pragma unroll
+        for (int t = 0; t < TPB; ++t) {
+            const int mt = min(rt + 4 * o, NKD - 1) * TPB + t;
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) Kf[o * TPB + t][kc] = kfrag(c0, G::F_KT + mt * NKC + kc);
+        }
+    floatx4 u0 = __builtin_bit_cast(floatx4, vblk(c0)[u0f * 64 + lane]);
+    floatx4 qs4 = scal4(c0, ro), ks4 = scal4(c0, 64 + ro);
+    float gn = scal1(c0, 128);
+    // the sequence's token range; its chunks are consecutive 64-token pieces
+    const int tbeg = cs < ce ? sp.ent[cs].t0 : 0;
+    const int tend = cs < ce ? sp.ent[ce - 1].t0 + sp.ent[ce - 1].len : 0;
+    // Let the first chunk's operands land before the loop: the loop's waits
+    // then only have to account for the loads issued inside it.
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
     lds_sync();
 
-    // The output tile of chunk c is stored at the top of iteration c+1, before
-    // that iteration's prefetch loads: the only wait for memory in the loop
-    // (publishing the prefetched operands) then covers operations issued a
-    // whole chunk of work earlier.
     const uint32_t row_bytes = (uint32_t)(sp.H_v * DV * sizeof(OT));
-    floatx4 Oprev = {0.f, 0.f, 0.f, 0.f};
-    int t0prev = 0, lenprev = 0;
-    auto store_out = [&](const floatx4 &O, int t0o, int leno) {
-        // rows >= len of a partial chunk fall outside the buffer and are dropped
-        const __amdgpu_buffer_rsrc_t ob =
-            raw_buffer(og + ((size_t)t0o * sp.H_v + h) * DV + col0, (uint32_t)leno * row_bytes);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            buffer_store(from_f32<OT>(O[j]), ob,
-                         (uint32_t)(16 * rt + 4 * qd + j) * row_bytes + n * (uint32_t)sizeof(OT));
-    };
-
     for (int c = cs; c < ce; ++c) {
-        // publish this chunk's operands, store the previous chunk's output,
-        // then prefetch the next chunk's operands
-#pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int idx = tid + p * NT;
-            if (idx < A16) sA[idx] = pre[p];
-        }
-        store_out(Oprev, t0prev, lenprev);
-        if (c + 1 < ce) {
-            const u32x4 *vb = reinterpret_cast<const u32x4 *>(vbase + (size_t)(c + 1) * vstep);
-            const u32x4 *kb = reinterpret_cast<const u32x4 *>(kbase + (size_t)(c + 1) * kstep);
-#pragma unroll
-            for (int p = 0; p < PF; ++p) {
-                const int idx = tid + p * NT;
-                if (idx < A16)
-                    pre[p] = idx < SV16 ? vb[idx] : idx < SV16 + U016 ? vb[u0_src + idx - SV16]
-                                                                      : kb[idx - SV16 - U016];
-            }
-        }
-        lds_sync();
-        const int t0 = __builtin_amdgcn_readfirstlane(__float_as_int(sScal[129]));
-        const int len = __builtin_amdgcn_readfirstlane(__float_as_int(sScal[130]));
-        const floatx4 u0 = __builtin_bit_cast(floatx4, sA[(L::A_U0 + ctl * 4 + rt) * 64 + lane]);
+        const int cn = min(c + 1, ce - 1);         // next chunk (the last one reloads itself)
 
-        // phase A (token rows rt): U = U0 - W S and Q S, both with the
-        // incoming state as two-term B operands
-        floatx4 St[NMT];
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) St[mt] = sS[(ctl * NMT + mt) * 64 + lane];
-        floatx4 WS = {0.f, 0.f, 0.f, 0.f}, OQ = {0.f, 0.f, 0.f, 0.f};
+        // phase A: U = U0 - W S and the inter-chunk read-out Q S, state from LDS
+        floatx4 WSh = {0.f, 0.f, 0.f, 0.f}, WSl = WSh, OQh = WSh, OQl = WSh;
 #pragma unroll
         for (int kb = 0; kb < NKD; ++kb) {
-            Frag sh, sl;
-            SP::acc(St, kb, 1.f, sh, sl);
-            const Frag wa = frag(G::F_W + rt * NKD + kb);
-            const Frag qa = frag(L::A_Q + rt * NKD + kb);
-            M::mma(WS, wa, sh);
-            M::mma(OQ, qa, sh);
+            const Frag sh = xfrag(mySf, kb * NS);
+            M::mma(WSh, Wf[kb], sh);
+            M::mma(OQh, Qf[kb], sh);
             if constexpr (NS == 2) {
-                M::mma(WS, wa, sl);
-                M::mma(OQ, qa, sl);
+                const Frag sl = xfrag(mySf, kb * NS + 1);
+                M::mma(WSl, Wf[kb], sl);
+                M::mma(OQl, Qf[kb], sl);
             }
         }
-        const floatx4 U = u0 - WS;
-        sU[(ctl * 4 + rt) * 64 + lane] = U;
+        const floatx4 U = u0 - (WSh + WSl);
+        const floatx4 Oi = (OQh + OQl) * qs4;
+        const floatx4 Uk = U * ks4;
+        {
+            const int kc = rt / TPB, part = rt % TPB;
+            TileOut<E>::put(myUf + (kc * NS) * 64, myUf + (kc * NS + NS - 1) * 64, lane, part, U);
+            TileOut<E>::put(myKf + (kc * NS) * 64, myKf + (kc * NS + NS - 1) * 64, lane, part, Uk);
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKD; ++kb) {
+            Wf[kb] = vfrag(cn, G::F_W + rt * NKD + kb);
+            Qf[kb] = kfrag(cn, G::F_Q + rt * NKD + kb);
+        }
+        u0 = __builtin_bit_cast(floatx4, vblk(cn)[u0f * 64 + lane]);
+        qs4 = scal4(cn, ro);
+        ks4 = scal4(cn, 64 + ro);
         lds_sync();
 
-        // phase B: output rows rt, then the state update of dk block(s) rt
-        floatx4 Ut[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Ut[r] = sU[(ctl * 4 + r) * 64 + lane];
-        floatx4 O;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) O[j] = OQ[j] * sScal[16 * rt + 4 * qd + j];
+        // phase B: intra-chunk output P U, then the owned blocks of the state
+        floatx4 Oa = Oi, Ob = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
             if (kc * KB > 16 * rt + 15) continue;
-            Frag uh, ul;
-            SP::acc(Ut, kc, 1.f, uh, ul);
-            const Frag ph = frag(G::F_PH + rt * NKC + kc);
-            M::mma(O, ph, uh);
+            const Frag uh = xfrag(myUf, kc * NS);
+            M::mma(Oa, Ph[kc], uh);
             if constexpr (NS == 2) {
-                M::mma(O, ph, ul);
-                M::mma(O, frag(G::F_PL + rt * NKC + kc), uh);
+                M::mma(Ob, Ph[kc], xfrag(myUf, kc * NS + 1));
+                M::mma(Ob, Pl[kc], uh);
             }
         }
-        Oprev = O;
-        t0prev = t0;
-        lenprev = len;
+        {
+            // rows >= len of a partial chunk fall outside the buffer and are dropped
+            const int t0 = tbeg + C * (c - cs), len = min(C, tend - t0);
+            const __amdgpu_buffer_rsrc_t ob =
+                raw_buffer(og + ((size_t)t0 * sp.H_v + h) * DV + col0, (uint32_t)len * row_bytes);
+            const floatx4 O = Oa + Ob;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                buffer_store(from_f32<OT>(O[j]), ob, (uint32_t)(ro + j) * row_bytes + n * (uint32_t)sizeof(OT));
+        }
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            Ph[kc] = vfrag(cn, G::F_PH + rt * NKC + kc);
+            if constexpr (NS == 2) Pl[kc] = vfrag(cn, G::F_PL + rt * NKC + kc);
+        }
 
         if (rt < NKD) {
-            const float gn = sScal[128];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) Ut[r][j] *= sScal[64 + 16 * r + 4 * qd + j];
             Frag kh_[NKC], kl_[NKC];
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) SP::acc(Ut, kc, 1.f, kh_[kc], kl_[kc]);
+            for (int kc = 0; kc < NKC; ++kc) {
+                kh_[kc] = xfrag(myKf, kc * NS);
+                kl_[kc] = xfrag(myKf, kc * NS + NS - 1);
+            }
 #pragma unroll
-            for (int mt = 0; mt < NMT; ++mt) {
-                if ((mt / TPB) % 4 != rt) continue;
-                floatx4 Sm = St[mt] * gn;
+            for (int o = 0; o < NOWN; ++o) {
+                const int kb = rt + 4 * o;
+                if (kb >= NKD) continue;
+                floatx4 Sa[TPB], Sb[TPB];
 #pragma unroll
-                for (int kc = 0; kc < NKC; ++kc) {
-                    const Frag ka = frag(L::A_KT + mt * NKC + kc);
-                    M::mma(Sm, ka, kh_[kc]);
-                    if constexpr (NS == 2) M::mma(Sm, ka, kl_[kc]);
+                for (int t = 0; t < TPB; ++t) {
+                    Sa[t] = Sreg[o][t] * gn;
+                    Sb[t] = floatx4{0.f, 0.f, 0.f, 0.f};
                 }
-                sS[(ctl * NMT + mt) * 64 + lane] = Sm;
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                    for (int t = 0; t < TPB; ++t) {
+                        M::mma(Sa[t], Kf[o * TPB + t][kc], kh_[kc]);
+                        if constexpr (NS == 2) M::mma(Sb[t], Kf[o * TPB + t][kc], kl_[kc]);
+                    }
+#pragma unroll
+                for (int t = 0; t < TPB; ++t) {
+                    Sreg[o][t] = Sa[t] + Sb[t];
+                    TileOut<E>::put(mySf + (kb * NS) * 64, mySf + (kb * NS + NS - 1) * 64, lane, t, Sreg[o][t]);
+                }
             }
         }
+#pragma unroll
+        for (int o = 0; o < NOWN; ++o)
+#pragma unroll
+            for (int t = 0; t < TPB; ++t) {
+                const int mt = min(rt + 4 * o, NKD - 1) * TPB + t;
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) Kf[o * TPB + t][kc] = kfrag(cn, G::F_KT + mt * NKC + kc);
+            }
+        gn = scal1(cn, 128);
         lds_sync();
     }
-
-    store_out(Oprev, t0prev, lenprev);     // last chunk (a zero-length store if none)
 
     const int sout = sp.slot_out[i];
     if (sout >= 0) {
         float *base = sp.state_out + (int64_t)sout * sp.slot_stride + (int64_t)h * DK * DV + col0 + n;
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
-            if ((mt / TPB) % 4 != rt) continue;
-            const floatx4 v = sS[(ctl * NMT + mt) * 64 + lane];
+        for (int o = 0; o < NOWN; ++o) {
+            const int kb = rt + 4 * o;
+            if (kb >= NKD) continue;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) base[(int64_t)(16 * mt + 4 * qd + j) * DV] = v[j];
+            for (int t = 0; t < TPB; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    base[(int64_t)(16 * (kb * TPB + t) + 4 * qd + j) * DV] = Sreg[o][t][j];
         }
     }
 }
@@ -845,7 +902,7 @@ template <int DK, int DV, typename E, typename OT>
 hipError_t scan_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
 {
     const WsPtrs w = ws_ptrs(p, a);
-    constexpr int CT = 2;    // column tiles per workgroup (d_v >= 32 always)
+    constexpr int CT = 1;    // column tiles per workgroup
     ScanParams sp{a.state_in, a.state_out, a.out, a.slot_in, a.slot_out, w.cstart, w.ent,
                   w.vblocks, w.kblocks, p.H_k, p.H_v, p.slot_stride};
     constexpr size_t lds = ScanLds<DK, DV, CT, E>::BYTES;
