@@ -231,24 +231,54 @@ template <> __device__ __forceinline__ void store_quarter2<float>(void *hi_base,
     store_quarter<float>(hi_base, f, lane, half, v);
 }
 
-template <typename E> struct ElemVec;
-template <> struct ElemVec<bf16_t> {
-    static constexpr int N = 8;
-    __device__ static __forceinline__ float get(const uint4 &u, int e) {
-        const uint32_t w = (&u.x)[e >> 1];
-        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+// Squared norm of the 16 bytes a lane loaded from a q / k row.
+template <typename E> __device__ __forceinline__ float sumsq16(u32x4 u);
+template <> __device__ __forceinline__ float sumsq16<bf16_t>(u32x4 u) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float a = __uint_as_float(u[e] << 16), b = __uint_as_float(u[e] & 0xffff0000u);
+        s += a * a + b * b;
     }
-    __device__ static __forceinline__ bf16_t raw(const uint4 &u, int e) {
-        const uint32_t w = (&u.x)[e >> 1];
-        bf16_t r;
-        r.bits = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
-        return r;
+    return s;
+}
+template <> __device__ __forceinline__ float sumsq16<float>(u32x4 u) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += __uint_as_float(u[e]) * __uint_as_float(u[e]);
+    return s;
+}
+
+// Operand fragment read transposed out of a row-major LDS matrix X[k][n]
+// (leading dimension ld elements): lane (qd, n) receives X[k0 + 4qd + j][n0 + n]
+// (and, for bf16, X[k0 + 16 + 4qd + j][n0 + n]), j = 0..3.  That is the B
+// operand of a K block whose K index runs over X's rows, and equally the A
+// operand of X^T.  For bf16 the transpose is done by ds_read_b64_tr_b16: in
+// each group of 16 lanes, lane i receives element i % 4 of the 8-byte words
+// fetched by lanes i / 4 + 4j, so lane p of group qd fetches row
+// k0 + 4qd + p / 4, columns n0 + 4 (p % 4) .. +3.
+template <typename E> struct TrLoad;
+template <> struct TrLoad<bf16_t> {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    __device__ static __forceinline__ bf16x8 frag(const bf16_t *X, int ld, int k0, int n0, int lane) {
+        const int qd = lane >> 4, p = lane & 15;
+        const bf16_t *a = X + (k0 + 4 * qd + (p >> 2)) * ld + n0 + 4 * (p & 3);
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(void *)(a));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(void *)(a + 16 * ld));
+        const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, v);
     }
 };
-template <> struct ElemVec<float> {
-    static constexpr int N = 4;
-    __device__ static __forceinline__ float get(const uint4 &u, int e) { return __uint_as_float((&u.x)[e]); }
-    __device__ static __forceinline__ float raw(const uint4 &u, int e) { return __uint_as_float((&u.x)[e]); }
+template <> struct TrLoad<float> {
+    __device__ static __forceinline__ floatx4 frag(const float *X, int ld, int k0, int n0, int lane) {
+        const int qd = lane >> 4, n = lane & 15;
+        floatx4 f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[j] = X[(k0 + 4 * qd + j) * ld + n0 + n];
+        return f;
+    }
 };
 
 // The 10 lower 16x16 tile pairs (rt, ct), ct <= rt, of a 64x64 matrix in
@@ -270,88 +300,87 @@ struct PrepParams {
     float scale, eps;
 };
 
+// LDS of the preparation kernel.  Rows are padded so that the row stride is
+// 8 banks (mod 64): the transposed reads (4 rows x 32 bytes per 16 lanes) and
+// the row reads of 16 different rows then hit distinct banks.
 template <int DK, int DV, typename E> struct PrepLds {
-    static constexpr int VEC = 16 / (int)sizeof(E);
-    static constexpr int LDK = DK + VEC;     // row-major K, Q (elements)
-    static constexpr int LDT = C + VEC;      // transposed K and V (elements)
-    static constexpr int LDA = C + 4;        // fp32 A and T
-    static constexpr size_t R1a = 2ull * C * LDK * sizeof(E);
-    static constexpr size_t R1b = 2ull * C * LDA * sizeof(float);
-    static constexpr size_t R1 = R1a > R1b ? R1a : R1b;
-    static constexpr size_t R2 = ((size_t)DK * LDT * sizeof(E) + 15) / 16 * 16;
-    static constexpr size_t R3 = ((size_t)DV * LDT * sizeof(E) + 15) / 16 * 16;
-    static constexpr size_t SMALL = C * sizeof(double) + 5 * C * sizeof(float);
-    static constexpr size_t BYTES = R1 + R2 + R3 + SMALL;
+    static constexpr int PAD = sizeof(E) == 2 ? 16 : 4;
+    static constexpr int LDK = DK + PAD;                  // K rows
+    static constexpr int DX = DK > DV ? DK : DV;
+    static constexpr int LDX = DX + PAD;                  // Q rows, then V rows of one value head
+    static constexpr int LDA = C + 4;                     // A and T (fp32)
+    static constexpr size_t OFF_K = 0;
+    static constexpr size_t OFF_X = OFF_K + (size_t)C * LDK * sizeof(E);
+    static constexpr size_t OFF_A = OFF_X + (size_t)C * LDX * sizeof(E);
+    static constexpr size_t OFF_T = OFF_A + (size_t)C * LDA * sizeof(float);
+    static constexpr size_t OFF_G = OFF_T + (size_t)C * LDA * sizeof(float);
+    static constexpr size_t OFF_S = OFF_G + C * sizeof(double);
+    static constexpr size_t BYTES = OFF_S + 5 * C * sizeof(float);
 };
 
 // --------------------------------------------------------------------------
 // 2. per-chunk preparation (state independent)
 // --------------------------------------------------------------------------
 template <int DK, int DV, typename E>
-__global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
+__global__ __launch_bounds__(256, 2) void prep_kernel(PrepParams pp)
 {
     using M = Mfma<E>;
     using SP = Split<E>;
     using G = Geo<DK, DV, E>;
     using L = PrepLds<DK, DV, E>;
-    using V = ElemVec<E>;
+    using TR = TrLoad<E>;
     using Frag = typename M::Frag;
-    constexpr int KB = M::KB, TPB = M::TPB, VEC = L::VEC, NS = SP::N;
-    constexpr int LDK = L::LDK, LDT = L::LDT, LDA = L::LDA;
-    constexpr int NKD = G::NKD, NKC = G::NKC, NCT = G::NCT;
+    constexpr int KB = M::KB, TPB = M::TPB, NS = SP::N;
+    constexpr int VEC = 16 / (int)sizeof(E);
+    constexpr int LDK = L::LDK, LDX = L::LDX, LDA = L::LDA;
+    constexpr int NKD = G::NKD, NKC = G::NKC, NMT = DK / 16, NCT = DV / 16;
     constexpr int VPR = DK / VEC;         // 16-byte vectors per q/k row
     constexpr int VPRV = DV / VEC;        // 16-byte vectors per v row
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    E *sK = reinterpret_cast<E *>(smem);
-    E *sQ = sK + C * LDK;
-    float *sA = reinterpret_cast<float *>(smem);
-    float *sT = sA + C * LDA;
-    E *sKT = reinterpret_cast<E *>(smem + L::R1);
-    E *sVT = reinterpret_cast<E *>(smem + L::R1 + L::R2);
-    double *sG = reinterpret_cast<double *>(smem + L::R1 + L::R2 + L::R3);
-    float *sBeta = reinterpret_cast<float *>(sG + C);
-    float *srk = sBeta + C;
-    float *srq = srk + C;
-    float *scol = srq + C;
+    E *sK = reinterpret_cast<E *>(smem + L::OFF_K);
+    E *sX = reinterpret_cast<E *>(smem + L::OFF_X);
+    float *sA = reinterpret_cast<float *>(smem + L::OFF_A);
+    float *sT = reinterpret_cast<float *>(smem + L::OFF_T);
+    double *sG = reinterpret_cast<double *>(smem + L::OFF_G);
+    float *sRK = reinterpret_cast<float *>(smem + L::OFF_S);   // 1 / |k_r|
+    float *sRQ = sRK + C;                                      // scale / |q_r|
+    float *sRA = sRQ + C;                                      // beta_r / |k_r|  (rows of A)
+    float *sBeta = sRA + C;                                    // beta_c          (columns of T for U0)
+    float *sCol = sBeta + C;                                   // beta_c e^{G_c} / |k_c|  (columns of T for W)
 
     const int chunk = blockIdx.x, kh = blockIdx.y;
     if (chunk >= pp.hdr[0]) return;
     const ChunkEntry ce = pp.ent[chunk];
     const int t0 = ce.t0, len = ce.len;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, qd = lane >> 4;
     const E *qg = static_cast<const E *>(pp.q);
     const E *kg = static_cast<const E *>(pp.k);
     const E *vg = static_cast<const E *>(pp.v);
 
-    // 1. stage K, Q (row-major) and K^T; inverse row norms
+    // 1. K and Q rows of the chunk (row-major, zero past the end) and their
+    //    inverse norms; a row's VPR vectors sit in VPR adjacent lanes
     for (int vi = tid; vi < C * VPR; vi += 256) {
         const int r = vi / VPR, cv = vi % VPR;
-        uint4 kv = make_uint4(0, 0, 0, 0), qv = kv;
+        u32x4 kv = {0u, 0u, 0u, 0u}, qv = kv;
         if (r < len) {
             const size_t off = ((size_t)(t0 + r) * pp.H_k + kh) * DK + (size_t)cv * VEC;
-            kv = *reinterpret_cast<const uint4 *>(kg + off);
-            qv = *reinterpret_cast<const uint4 *>(qg + off);
+            kv = *reinterpret_cast<const u32x4 *>(kg + off);
+            qv = *reinterpret_cast<const u32x4 *>(qg + off);
         }
-        *reinterpret_cast<uint4 *>(sK + r * LDK + cv * VEC) = kv;
-        *reinterpret_cast<uint4 *>(sQ + r * LDK + cv * VEC) = qv;
-        float k2 = 0.f, q2 = 0.f;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            sKT[(cv * VEC + e) * LDT + r] = V::raw(kv, e);
-            const float a = V::get(kv, e), b = V::get(qv, e);
-            k2 += a * a;
-            q2 += b * b;
-        }
+        *reinterpret_cast<u32x4 *>(sK + r * LDK + cv * VEC) = kv;
+        *reinterpret_cast<u32x4 *>(sX + r * LDX + cv * VEC) = qv;
+        float k2 = sumsq16<E>(kv), q2 = sumsq16<E>(qv);
 #pragma unroll
         for (int off = VPR / 2; off >= 1; off >>= 1) {
             k2 += __shfl_xor(k2, off, 64);
             q2 += __shfl_xor(q2, off, 64);
         }
         if (cv == 0) {
-            srk[r] = r < len ? rsqrtf(k2 + pp.eps) : 0.f;
-            srq[r] = r < len ? rsqrtf(q2 + pp.eps) * pp.scale : 0.f;
+            sRK[r] = r < len ? rsqrtf(k2 + pp.eps) : 0.f;
+            sRQ[r] = r < len ? rsqrtf(q2 + pp.eps) * pp.scale : 0.f;
         }
     }
     lds_sync();
@@ -361,11 +390,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
         char *kb_blk = pp.kblocks + ((size_t)chunk * pp.H_k + kh) * ((size_t)G::KBLK * 1024);
         for (int f = w; f < G::NQF; f += 4) {
             const int rt = f / NKD, kb = f % NKD;
-            store_frag<E>(kb_blk + G::F_Q * 1024, f, lane, M::load_rm(sQ + (16 * rt + n) * LDK, kb * KB, qd));
+            store_frag<E>(kb_blk + G::F_Q * 1024, f, lane, M::load_rm(sX + (16 * rt + n) * LDX, kb * KB, qd));
         }
         for (int f = w; f < G::NKF; f += 4) {
             const int mt = f / NKC, kc = f % NKC;
-            store_frag<E>(kb_blk + G::F_KT * 1024, f, lane, M::load_rm(sKT + (16 * mt + n) * LDT, kc * KB, qd));
+            store_frag<E>(kb_blk + G::F_KT * 1024, f, lane, TR::frag(sK, LDK, kc * KB, 16 * mt, lane));
         }
     }
 
@@ -378,13 +407,13 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
         const int it = w + 4 * s;
         const int pr = it < 10 ? it : it - 10;
         const int rt = low_r(pr), ct = low_c(pr);
-        const E *ra = it < 10 ? sK + (16 * rt + n) * LDK : sK + (16 * ct + n) * LDK;
-        const E *rb = it < 10 ? sK + (16 * ct + n) * LDK : sQ + (16 * rt + n) * LDK;
+        const E *ra = sK + (16 * (it < 10 ? rt : ct) + n) * LDK;
+        const E *rb = it < 10 ? sK + (16 * ct + n) * LDK : sX + (16 * rt + n) * LDX;
 #pragma unroll
         for (int kb = 0; kb < NKD; ++kb)
             M::mma(acc[s], M::load_rm(ra, kb * KB, qd), M::load_rm(rb, kb * KB, qd));
     }
-    lds_sync();   // sK / sQ are dead from here on (sA / sT alias them)
+    lds_sync();   // Q is dead: sX holds V from here on
 
     const int ratio = pp.H_v / pp.H_k;
     // V rows, g and beta of the next value head are loaded one head ahead
@@ -415,16 +444,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
         float *scal = reinterpret_cast<float *>(blk + G::F_SCAL * 1024);
         char *U0f = blk + G::F_U0 * 1024;
 
-        // 4a. V^T of this value head; cumulative log-decay in fp64, row scalars
+        // 4a. V rows; cumulative log-decay in fp64 and the per-row scalars
 #pragma unroll
         for (int p = 0; p < VL; ++p) {
             const int vi = tid + 256 * p;
-            const int r = vi / VPRV, cv = vi % VPRV;
-            if (vi < C * VPRV) {
-                const uint4 vv = __builtin_bit_cast(uint4, vpre[p]);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) sVT[(cv * VEC + e) * LDT + r] = V::raw(vv, e);
-            }
+            if (vi < C * VPRV)
+                *reinterpret_cast<u32x4 *>(sX + (vi / VPRV) * LDX + (vi % VPRV) * VEC) = vpre[p];
         }
         const float gv = gpre, bv = bpre;
         if (jv + 1 < ratio) load_head(h + 1);
@@ -437,44 +462,58 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
                 if (lane >= off) Gc += y;
             }
             const double Gn = __shfl(Gc, 63, 64);
-            sG[r] = Gc;
-            sBeta[r] = bv;
+            const float rk = sRK[r];
             const float eG = expf((float)Gc);
-            scal[r] = srq[r] * eG;                              // qs: q scale * e^{G_r}
-            scal[64 + r] = srk[r] * expf((float)(Gn - Gc));     // ks: e^{G_n - G_r} / |k_r|
+            sG[r] = Gc;
+            sRA[r] = bv * rk;
+            sBeta[r] = bv;
+            sCol[r] = bv * eG * rk;
+            scal[r] = sRQ[r] * eG;                              // qs: q scale * e^{G_r}
+            scal[64 + r] = rk * expf((float)(Gn - Gc));         // ks: e^{G_n - G_r} / |k_r|
             if (r == 0) {
                 scal[128] = expf((float)Gn);                    // gn: e^{G_n}
                 scal[129] = __int_as_float(t0);                 // the chunk's first token
                 scal[130] = __int_as_float(len);                // and length
             }
-            scol[r] = bv * eG * srk[r];                         // columns of T'' = T diag(beta e^G / |k|)
         }
         lds_sync();
 
-        // 4b. A (strictly lower) -> LDS; masked, decayed Q.K -> P fragments
+        // 4b. A (strictly lower) -> LDS; masked, decayed Q.K -> P fragments.
+        //     exp is always taken of G_r - G_c <= 0 (fp64 difference).
 #pragma unroll
         for (int s = 0; s < 5; ++s) {
             const int it = w + 4 * s;
             if (it < 10) {
+                // lane: column c, rows r0 + j
                 const int rt = low_r(it), ct = low_c(it);
-                const int c = 16 * ct + n;
+                const int c = 16 * ct + n, r0 = 16 * rt + 4 * qd;
+                const double gc = sG[c];
+                const float fc = sRK[c];
+                const double2 g01 = *reinterpret_cast<const double2 *>(sG + r0);
+                const double2 g23 = *reinterpret_cast<const double2 *>(sG + r0 + 2);
+                const floatx4 fr = *reinterpret_cast<const floatx4 *>(sRA + r0);
+                const double gr[4] = {g01.x, g01.y, g23.x, g23.y};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * rt + 4 * qd + j;
-                    float val = 0.f;
-                    if (c < r)
-                        val = sBeta[r] * srk[r] * srk[c] * acc[s][j] * expf((float)(sG[r] - sG[c]));
-                    sA[r * LDA + c] = val;
+                    const float e = expf((float)(gr[j] - gc));
+                    sA[(r0 + j) * LDA + c] = (c < r0 + j) ? fr[j] * fc * acc[s][j] * e : 0.f;
                 }
             } else {
+                // lane: row r, columns c0 + j
                 const int pr = it - 10;
                 const int rt = low_r(pr), ct = low_c(pr);
-                const int r = 16 * rt + n;
+                const int r = 16 * rt + n, c0 = 16 * ct + 4 * qd;
+                const double gr = sG[r];
+                const float fr = sRQ[r];
+                const double2 g01 = *reinterpret_cast<const double2 *>(sG + c0);
+                const double2 g23 = *reinterpret_cast<const double2 *>(sG + c0 + 2);
+                const floatx4 fc = *reinterpret_cast<const floatx4 *>(sRK + c0);
+                const double gc[4] = {g01.x, g01.y, g23.x, g23.y};
                 floatx4 pv;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int c = 16 * ct + 4 * qd + j;
-                    pv[j] = (c <= r) ? srq[r] * srk[c] * acc[s][j] * expf((float)(sG[r] - sG[c])) : 0.f;
+                    const float e = expf((float)(gr - gc[j]));
+                    pv[j] = (c0 + j <= r) ? fr * fc[j] * acc[s][j] * e : 0.f;
                 }
                 store_quarter2<E>(Pf, Plf, rt * NKC + ct / TPB, lane, ct % TPB, pv);
             }
@@ -482,11 +521,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
         for (int z = w; z < 6; z += 4) {
             const int rt = up_r(z), ct = up_c(z);
             store_quarter2<E>(Pf, Plf, rt * NKC + ct / TPB, lane, ct % TPB, floatx4{0.f, 0.f, 0.f, 0.f});
+            // the products with T read whole K blocks: its upper blocks are zero
+            *reinterpret_cast<floatx4 *>(sT + (16 * rt + (lane >> 2)) * LDA + 16 * ct + 4 * (lane & 3)) =
+                floatx4{0.f, 0.f, 0.f, 0.f};
         }
         lds_sync();
 
         // 4c. T = (I + A)^-1: diagonal 16x16 blocks by forward substitution
-        //     (wave 0, one lane per column); other waves zero the upper blocks.
+        //     (wave 0, one lane per column of one block)
         if (w == 0) {
             const int b = lane >> 4, j = lane & 15;
             const float *Ab = sA + (16 * b) * LDA + 16 * b;
@@ -495,16 +537,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
             for (int i = 0; i < 16; ++i) {
                 float a = (i == j) ? 1.f : 0.f;
 #pragma unroll
-                for (int c = 0; c < i; ++c) a -= Ab[i * LDA + c] * t[c];
+                for (int c4 = 0; c4 < i; c4 += 4) {
+                    const floatx4 av = *reinterpret_cast<const floatx4 *>(Ab + i * LDA + c4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (c4 + e < i) a -= av[e] * t[c4 + e];
+                }
                 t[i] = a;
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) sT[(16 * b + i) * LDA + 16 * b + j] = t[i];
-        } else {
-            for (int e = tid - 64; e < 6 * 256; e += 192) {
-                const int z = e >> 8, within = e & 255;
-                sT[(16 * up_r(z) + (within >> 4)) * LDA + 16 * up_c(z) + (within & 15)] = 0.f;
-            }
         }
         lds_sync();
         //     off-diagonal blocks by distance: T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
@@ -513,15 +555,13 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
                 const int bi = w + d, bj = w;
                 floatx4 X = {0.f, 0.f, 0.f, 0.f};
                 for (int m = bj; m < bi; ++m) {
-                    const float4 av = *reinterpret_cast<const float4 *>(sA + (16 * bi + n) * LDA + 16 * m + 4 * qd);
-                    floatx4 a = {av.x, av.y, av.z, av.w};
+                    const floatx4 a = *reinterpret_cast<const floatx4 *>(sA + (16 * bi + n) * LDA + 16 * m + 4 * qd);
                     floatx4 bt;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) bt[j] = sT[(16 * m + 4 * qd + j) * LDA + 16 * bj + n];
                     mma_f32_k16(X, a, bt);
                 }
-                const float4 tv = *reinterpret_cast<const float4 *>(sT + (16 * bi + n) * LDA + 16 * bi + 4 * qd);
-                floatx4 a = {-tv.x, -tv.y, -tv.z, -tv.w};
+                const floatx4 a = -*reinterpret_cast<const floatx4 *>(sT + (16 * bi + n) * LDA + 16 * bi + 4 * qd);
                 floatx4 Y = {0.f, 0.f, 0.f, 0.f};
                 mma_f32_k16(Y, a, X);
 #pragma unroll
@@ -530,35 +570,49 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams pp)
             lds_sync();
         }
 
-        // 4d. W^T = K^T T''^T tiles (dk tile dt, token tile tt) -> W fragments
-        for (int item = w; item < (DK / 16) * 4; item += 4) {
-            const int dt = item % (DK / 16), tt = item / (DK / 16);
-            floatx4 a4 = {0.f, 0.f, 0.f, 0.f};
+        // 4d. W^T = K^T T''^T, T'' = T diag(beta e^G / |k|): wave w takes token
+        //     tile tt = w (B operand loaded once, all dk tiles).
+        //     U0 = T diag(beta) V: wave w takes token tile 3 - w, so every
+        //     wave runs the same number of products.
+        {
+            const int tt = w;
+            const int nkb = (16 * tt + 15) / KB + 1;    // K blocks reaching the diagonal
+            Frag bh[NKC], bl[NKC];
 #pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) {
-                if (kb * KB > 16 * tt + 15) break;
-                const Frag a = M::load_rm(sKT + (16 * dt + n) * LDT, kb * KB, qd);
-                Frag hi, lo;
-                SP::rm_f32(sT + (16 * tt + n) * LDA, kb * KB, qd, scol, hi, lo);
-                M::mma(a4, a, hi);
-                if constexpr (NS == 2) M::mma(a4, a, lo);
+            for (int kb = 0; kb < NKC; ++kb)
+                if (kb < nkb) SP::rm_f32(sT + (16 * tt + n) * LDA, kb * KB, qd, sCol, bh[kb], bl[kb]);
+#pragma unroll
+            for (int dt = 0; dt < NMT; ++dt) {
+                floatx4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKC; ++kb) {
+                    if (kb >= nkb) break;
+                    const Frag a = TR::frag(sK, LDK, kb * KB, 16 * dt, lane);
+                    M::mma(a4, a, bh[kb]);
+                    if constexpr (NS == 2) M::mma(a4, a, bl[kb]);
+                }
+                store_quarter<E>(Wf, tt * NKD + dt / TPB, lane, dt % TPB, a4);
             }
-            store_quarter<E>(Wf, tt * NKD + dt / TPB, lane, dt % TPB, a4);
         }
-        //     U0 = T diag(beta) V tiles (token tile rt, value-column tile ct)
-        for (int item = w; item < 4 * NCT; item += 4) {
-            const int ct = item % NCT, rt = item / NCT;
-            floatx4 a4 = {0.f, 0.f, 0.f, 0.f};
+        {
+            const int rt = 3 - w;
+            const int nkb = (16 * rt + 15) / KB + 1;
+            Frag ah[NKC], al[NKC];
 #pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) {
-                if (kb * KB > 16 * rt + 15) break;
-                Frag hi, lo;
-                SP::rm_f32(sT + (16 * rt + n) * LDA, kb * KB, qd, sBeta, hi, lo);
-                const Frag b = M::load_rm(sVT + (16 * ct + n) * LDT, kb * KB, qd);
-                M::mma(a4, hi, b);
-                if constexpr (NS == 2) M::mma(a4, lo, b);
+            for (int kb = 0; kb < NKC; ++kb)
+                if (kb < nkb) SP::rm_f32(sT + (16 * rt + n) * LDA, kb * KB, qd, sBeta, ah[kb], al[kb]);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                floatx4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKC; ++kb) {
+                    if (kb >= nkb) break;
+                    const Frag b = TR::frag(sX, LDX, kb * KB, 16 * ct, lane);
+                    M::mma(a4, ah[kb], b);
+                    if constexpr (NS == 2) M::mma(a4, al[kb], b);
+                }
+                *(reinterpret_cast<floatx4 *>(U0f) + (size_t)(ct * 4 + rt) * 64 + lane) = a4;
             }
-            *(reinterpret_cast<floatx4 *>(U0f) + (size_t)(ct * 4 + rt) * 64 + lane) = a4;
         }
         lds_sync();
     }
