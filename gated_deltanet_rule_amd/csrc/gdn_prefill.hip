@@ -199,7 +199,9 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(
 // helpers
 // --------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return (uint32_t)bf16_bits_rne(a) | ((uint32_t)bf16_bits_rne(b) << 16);
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = {(__bf16)a, (__bf16)b};      // v_cvt_pk_bf16_f32, round to nearest even
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Write 4 consecutive k-values (one accumulator column) into half `half` of
@@ -217,14 +219,15 @@ template <> __device__ __forceinline__ void store_quarter<float>(void *base, int
 // Same, for a two-term operand: hi into `hi_base`, lo into `lo_base`.
 template <typename E> __device__ __forceinline__ void store_quarter2(void *hi_base, void *lo_base, int f, int lane, int half, floatx4 v);
 template <> __device__ __forceinline__ void store_quarter2<bf16_t>(void *hi_base, void *lo_base, int f, int lane, int half, floatx4 v) {
-    floatx4 h, l;
+    bf16x4 h, l;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        h[j] = __uint_as_float((uint32_t)bf16_bits_rne(v[j]) << 16);
-        l[j] = v[j] - h[j];
+        h[j] = (__bf16)v[j];
+        l[j] = (__bf16)(v[j] - (float)h[j]);
     }
-    store_quarter<bf16_t>(hi_base, f, lane, half, h);
-    store_quarter<bf16_t>(lo_base, f, lane, half, l);
+    const size_t off = ((size_t)f * 64 + lane) * 16 + half * 8;
+    *reinterpret_cast<bf16x4 *>(reinterpret_cast<char *>(hi_base) + off) = h;
+    *reinterpret_cast<bf16x4 *>(reinterpret_cast<char *>(lo_base) + off) = l;
 }
 template <> __device__ __forceinline__ void store_quarter2<float>(void *hi_base, void *lo_base, int f, int lane, int half, floatx4 v) {
     (void)lo_base;
@@ -322,7 +325,7 @@ template <int DK, int DV, typename E> struct PrepLds {
 // 2. per-chunk preparation (state independent)
 // --------------------------------------------------------------------------
 template <int DK, int DV, typename E>
-__global__ __launch_bounds__(256, 2) void prep_kernel(PrepParams pp)
+__global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepParams pp)
 {
     using M = Mfma<E>;
     using SP = Split<E>;
@@ -532,18 +535,27 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrepParams pp)
         if (w == 0) {
             const int b = lane >> 4, j = lane & 15;
             const float *Ab = sA + (16 * b) * LDA + 16 * b;
+            // row i of the block is read two rows ahead of its use, so the
+            // dependent chain never waits for LDS (the scheduling barriers
+            // keep the compiler from hoisting every read to the top)
+            floatx4 win[3][4];
+            auto rd = [&](int i) {
+#pragma unroll
+                for (int c4 = 0; c4 < i; c4 += 4) win[i % 3][c4 / 4] = *reinterpret_cast<const floatx4 *>(Ab + i * LDA + c4);
+            };
+            rd(1);
             float t[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
+                if (i + 2 < 16) rd(i + 2);
                 float a = (i == j) ? 1.f : 0.f;
 #pragma unroll
-                for (int c4 = 0; c4 < i; c4 += 4) {
-                    const floatx4 av = *reinterpret_cast<const floatx4 *>(Ab + i * LDA + c4);
+                for (int c4 = 0; c4 < i; c4 += 4)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (c4 + e < i) a -= av[e] * t[c4 + e];
-                }
+                        if (c4 + e < i) a -= win[i % 3][c4 / 4][e] * t[c4 + e];
                 t[i] = a;
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) sT[(16 * b + i) * LDA + 16 * b + j] = t[i];
