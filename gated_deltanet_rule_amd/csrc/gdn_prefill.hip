@@ -284,6 +284,13 @@ template <> struct TrLoad<float> {
     }
 };
 
+// e^d for d = G_r - G_c <= 0 given in fp64: the difference is scaled to
+// base 2 in fp64 and rounded once to fp32 for v_exp_f32 (about 1 ulp; the
+// result underflows to 0 for d below about -103).
+__device__ __forceinline__ float exp_neg(double d) {
+    return __builtin_amdgcn_exp2f((float)(d * 1.4426950408889634));
+}
+
 // The 10 lower 16x16 tile pairs (rt, ct), ct <= rt, of a 64x64 matrix in
 // row order, and the 6 strictly upper ones.  Computed, not tabulated: a table
 // indexed per wave becomes a vector memory load, and on gfx9 waiting for it
@@ -317,8 +324,9 @@ template <int DK, int DV, typename E> struct PrepLds {
     static constexpr size_t OFF_A = OFF_X + (size_t)C * LDX * sizeof(E);
     static constexpr size_t OFF_T = OFF_A + (size_t)C * LDA * sizeof(float);
     static constexpr size_t OFF_G = OFF_T + (size_t)C * LDA * sizeof(float);
-    static constexpr size_t OFF_S = OFF_G + C * sizeof(double);
-    static constexpr size_t BYTES = OFF_S + 5 * C * sizeof(float);
+    static constexpr int NH = 4;                          // value heads whose row scalars are held at once
+    static constexpr size_t OFF_S = OFF_G + NH * C * sizeof(double);
+    static constexpr size_t BYTES = OFF_S + (2 + 3 * NH) * C * sizeof(float);
 };
 
 // --------------------------------------------------------------------------
@@ -345,12 +353,13 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
     E *sX = reinterpret_cast<E *>(smem + L::OFF_X);
     float *sA = reinterpret_cast<float *>(smem + L::OFF_A);
     float *sT = reinterpret_cast<float *>(smem + L::OFF_T);
-    double *sG = reinterpret_cast<double *>(smem + L::OFF_G);
-    float *sRK = reinterpret_cast<float *>(smem + L::OFF_S);   // 1 / |k_r|
-    float *sRQ = sRK + C;                                      // scale / |q_r|
-    float *sRA = sRQ + C;                                      // beta_r / |k_r|  (rows of A)
-    float *sBeta = sRA + C;                                    // beta_c          (columns of T for U0)
-    float *sCol = sBeta + C;                                   // beta_c e^{G_c} / |k_c|  (columns of T for W)
+    constexpr int NH = L::NH;
+    double *sGh = reinterpret_cast<double *>(smem + L::OFF_G);  // [NH][C] G_r = cumsum of g
+    float *sRK = reinterpret_cast<float *>(smem + L::OFF_S);    // 1 / |k_r|
+    float *sRQ = sRK + C;                                       // scale / |q_r|
+    float *sRAh = sRQ + C;                                      // [NH][C] beta_r / |k_r|  (rows of A)
+    float *sBetah = sRAh + NH * C;                              // [NH][C] beta_c          (columns of T for U0)
+    float *sColh = sBetah + NH * C;                             // [NH][C] beta_c e^{G_c} / |k_c|  (columns of T for W)
 
     const int chunk = blockIdx.x, kh = blockIdx.y;
     if (chunk >= pp.hdr[0]) return;
@@ -362,17 +371,88 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
     const E *qg = static_cast<const E *>(pp.q);
     const E *kg = static_cast<const E *>(pp.k);
     const E *vg = static_cast<const E *>(pp.v);
+    const int ratio = pp.H_v / pp.H_k;
+
+    // g and beta of up to NH value heads (wave w: head j0 + w, lane: row)
+    // Loads here are unconditional (clamped row / head, zero selected
+    // afterwards): a load inside a branch leaves the compiler unable to count
+    // outstanding memory operations, and the next wait for it then also waits
+    // for every store issued before.  A wave past the last head repeats the
+    // last one (identical values written twice).
+    float gq = 0.f, bq = 0.f;
+    const int lrow = min(lane, len - 1);
+    auto load_gb = [&](int j0) {
+        const int hh = kh * ratio + min(j0 + w, ratio - 1);
+        const float gl = pp.g[(size_t)(t0 + lrow) * pp.H_v + hh];
+        const float bl = pp.beta[(size_t)(t0 + lrow) * pp.H_v + hh];
+        gq = lane < len ? gl : 0.f;
+        bq = lane < len ? bl : 0.f;
+    };
+    // cumulative log-decay (fp64) and the per-row scalars of those heads
+    auto head_scalars = [&](int j0) {
+        const int jw = min(j0 + w, ratio - 1);
+        const int hh = kh * ratio + jw, hs = jw % NH;
+        float *scal = reinterpret_cast<float *>(pp.vblocks + ((size_t)chunk * pp.H_v + hh) * ((size_t)G::VBLK * 1024) +
+                                                G::F_SCAL * 1024);
+        const int r = lane;
+        double Gc = gq;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const double y = __shfl_up(Gc, off, 64);
+            if (lane >= off) Gc += y;
+        }
+        const double Gn = __shfl(Gc, 63, 64);
+        const float rk = sRK[r];
+        const float eG = expf((float)Gc);
+        sGh[hs * C + r] = Gc;
+        sRAh[hs * C + r] = bq * rk;
+        sBetah[hs * C + r] = bq;
+        sColh[hs * C + r] = bq * eG * rk;
+        scal[r] = sRQ[r] * eG;                              // qs: q scale * e^{G_r}
+        scal[64 + r] = rk * expf((float)(Gn - Gc));         // ks: e^{G_n - G_r} / |k_r|
+        // gn = e^{G_n}, the chunk's first token and length (int bits): lanes
+        // 0..2; the others fall outside the 12-byte buffer and are dropped
+        const float tail = lane == 0 ? expf((float)Gn) : __int_as_float(lane == 1 ? t0 : len);
+        buffer_store(tail, raw_buffer(scal + 128, 12), (uint32_t)lane * 4u);
+    };
+    // V rows of one value head, loaded one head ahead into registers
+    constexpr int VL = (C * VPRV + 255) / 256;
+    u32x4 vpre[VL];
+    static_assert(C * VPRV % 256 == 0 && C * VPR % 256 == 0, "whole vectors per thread");
+    auto load_v = [&](int hh) {
+#pragma unroll
+        for (int p = 0; p < VL; ++p) {
+            const int vi = tid + 256 * p;
+            const int r = vi / VPRV, cv = vi % VPRV;
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(vg + ((size_t)(t0 + min(r, len - 1)) * pp.H_v + hh) * DV + cv * VEC);
+            vpre[p] = r < len ? x : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
 
     // 1. K and Q rows of the chunk (row-major, zero past the end) and their
     //    inverse norms; a row's VPR vectors sit in VPR adjacent lanes
-    for (int vi = tid; vi < C * VPR; vi += 256) {
+    constexpr int KL = C * VPR / 256;     // 16-byte vectors of K (and of Q) per thread
+    u32x4 kx[KL], qx[KL];
+#pragma unroll
+    for (int p = 0; p < KL; ++p) {
+        const int vi = tid + 256 * p;
         const int r = vi / VPR, cv = vi % VPR;
-        u32x4 kv = {0u, 0u, 0u, 0u}, qv = kv;
-        if (r < len) {
-            const size_t off = ((size_t)(t0 + r) * pp.H_k + kh) * DK + (size_t)cv * VEC;
-            kv = *reinterpret_cast<const u32x4 *>(kg + off);
-            qv = *reinterpret_cast<const u32x4 *>(qg + off);
-        }
+        const size_t off = ((size_t)(t0 + min(r, len - 1)) * pp.H_k + kh) * DK + (size_t)cv * VEC;
+        kx[p] = *reinterpret_cast<const u32x4 *>(kg + off);
+        qx[p] = *reinterpret_cast<const u32x4 *>(qg + off);
+    }
+    // the first value head's g, beta and V: issued after K and Q (the
+    // scheduling barrier keeps that order), so that waiting for K and Q does
+    // not wait for these too
+    __builtin_amdgcn_sched_barrier(0);
+    load_gb(0);
+    load_v(kh * ratio);
+#pragma unroll
+    for (int p = 0; p < KL; ++p) {
+        const int vi = tid + 256 * p;
+        const int r = vi / VPR, cv = vi % VPR;
+        const u32x4 kv = r < len ? kx[p] : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 qv = r < len ? qx[p] : u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4 *>(sK + r * LDK + cv * VEC) = kv;
         *reinterpret_cast<u32x4 *>(sX + r * LDX + cv * VEC) = qv;
         float k2 = sumsq16<E>(kv), q2 = sumsq16<E>(qv);
@@ -387,6 +467,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
         }
     }
     lds_sync();
+    head_scalars(0);
 
     // 2. raw q and k^T of this key head as operand fragments for the scan
     {
@@ -418,76 +499,36 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
     }
     lds_sync();   // Q is dead: sX holds V from here on
 
-    const int ratio = pp.H_v / pp.H_k;
-    // V rows, g and beta of the next value head are loaded one head ahead
-    constexpr int VL = (C * VPRV + 255) / 256;
-    u32x4 vpre[VL];
-    float gpre = 0.f, bpre = 0.f;
-    auto load_head = [&](int hh) {
-#pragma unroll
-        for (int p = 0; p < VL; ++p) {
-            const int vi = tid + 256 * p;
-            const int r = vi / VPRV, cv = vi % VPRV;
-            vpre[p] = u32x4{0u, 0u, 0u, 0u};
-            if (vi < C * VPRV && r < len)
-                vpre[p] = *reinterpret_cast<const u32x4 *>(vg + ((size_t)(t0 + r) * pp.H_v + hh) * DV + cv * VEC);
-        }
-        if (w == 0 && lane < len) {
-            gpre = pp.g[(size_t)(t0 + lane) * pp.H_v + hh];
-            bpre = pp.beta[(size_t)(t0 + lane) * pp.H_v + hh];
-        }
-    };
-    load_head(kh * ratio);
     for (int jv = 0; jv < ratio; ++jv) {
         const int h = kh * ratio + jv;
         char *blk = pp.vblocks + ((size_t)chunk * pp.H_v + h) * ((size_t)G::VBLK * 1024);
         char *Wf = blk + G::F_W * 1024;
         char *Pf = blk + G::F_PH * 1024;
         char *Plf = blk + G::F_PL * 1024;
-        float *scal = reinterpret_cast<float *>(blk + G::F_SCAL * 1024);
         char *U0f = blk + G::F_U0 * 1024;
+        const int hs = jv % NH;
+        const double *sG = sGh + hs * C;
+        const float *sRA = sRAh + hs * C, *sBeta = sBetah + hs * C, *sCol = sColh + hs * C;
 
-        // 4a. V rows; cumulative log-decay in fp64 and the per-row scalars
+        // 4a. V rows of this head; row scalars of the next NH heads
 #pragma unroll
         for (int p = 0; p < VL; ++p) {
             const int vi = tid + 256 * p;
             if (vi < C * VPRV)
                 *reinterpret_cast<u32x4 *>(sX + (vi / VPRV) * LDX + (vi % VPRV) * VEC) = vpre[p];
         }
-        const float gv = gpre, bv = bpre;
-        if (jv + 1 < ratio) load_head(h + 1);
-        if (w == 0) {
-            const int r = lane;
-            double Gc = gv;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const double y = __shfl_up(Gc, off, 64);
-                if (lane >= off) Gc += y;
-            }
-            const double Gn = __shfl(Gc, 63, 64);
-            const float rk = sRK[r];
-            const float eG = expf((float)Gc);
-            sG[r] = Gc;
-            sRA[r] = bv * rk;
-            sBeta[r] = bv;
-            sCol[r] = bv * eG * rk;
-            scal[r] = sRQ[r] * eG;                              // qs: q scale * e^{G_r}
-            scal[64 + r] = rk * expf((float)(Gn - Gc));         // ks: e^{G_n - G_r} / |k_r|
-            if (r == 0) {
-                scal[128] = expf((float)Gn);                    // gn: e^{G_n}
-                scal[129] = __int_as_float(t0);                 // the chunk's first token
-                scal[130] = __int_as_float(len);                // and length
-            }
+        load_v(kh * ratio + min(jv + 1, ratio - 1));   // next head (the last reloads itself)
+        if (jv > 0 && hs == 0) {
+            load_gb(jv);
+            head_scalars(jv);
         }
         lds_sync();
 
         // 4b. A (strictly lower) -> LDS; masked, decayed Q.K -> P fragments.
         //     exp is always taken of G_r - G_c <= 0 (fp64 difference).
-#pragma unroll
-        for (int s = 0; s < 5; ++s) {
-            const int it = w + 4 * s;
-            if (it < 10) {
+        auto a_tile = [&](int s) {
                 // lane: column c, rows r0 + j
+                const int it = w + 4 * s;
                 const int rt = low_r(it), ct = low_c(it);
                 const int c = 16 * ct + n, r0 = 16 * rt + 4 * qd;
                 const double gc = sG[c];
@@ -498,12 +539,13 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
                 const double gr[4] = {g01.x, g01.y, g23.x, g23.y};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float e = expf((float)(gr[j] - gc));
+                    const float e = exp_neg(gr[j] - gc);
                     sA[(r0 + j) * LDA + c] = (c < r0 + j) ? fr[j] * fc * acc[s][j] * e : 0.f;
                 }
-            } else {
+        };
+        auto p_tile = [&](int s) {
                 // lane: row r, columns c0 + j
-                const int pr = it - 10;
+                const int pr = w + 4 * s - 10;
                 const int rt = low_r(pr), ct = low_c(pr);
                 const int r = 16 * rt + n, c0 = 16 * ct + 4 * qd;
                 const double gr = sG[r];
@@ -515,12 +557,18 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
                 floatx4 pv;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float e = expf((float)(gr - gc[j]));
+                    const float e = exp_neg(gr - gc[j]);
                     pv[j] = (c0 + j <= r) ? fr * fc[j] * acc[s][j] * e : 0.f;
                 }
                 store_quarter2<E>(Pf, Plf, rt * NKC + ct / TPB, lane, ct % TPB, pv);
-            }
-        }
+        };
+        // tiles w and w + 4 are A tiles for every wave, w + 12 and w + 16 P
+        // tiles, w + 8 is an A tile for waves 0, 1 and a P tile for 2, 3
+        a_tile(0);
+        a_tile(1);
+        p_tile(3);
+        p_tile(4);
+        if (w < 2) a_tile(2); else p_tile(2);
         for (int z = w; z < 6; z += 4) {
             const int rt = up_r(z), ct = up_c(z);
             store_quarter2<E>(Pf, Plf, rt * NKC + ct / TPB, lane, ct % TPB, floatx4{0.f, 0.f, 0.f, 0.f});
