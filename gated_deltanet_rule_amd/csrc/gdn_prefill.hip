@@ -842,6 +842,13 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
     lds_sync();
 
     const uint32_t row_bytes = (uint32_t)(sp.H_v * DV * sizeof(OT));
+    // The per-CU vector memory path, not the matrix cores, bounds a chunk:
+    // every wave moves ~16 KiB of operands per chunk.  The loads for the next
+    // chunk are therefore spread between this chunk's matrix-core ops
+    // (scheduling groups below) rather than issued in bursts, which would
+    // stall the issuing waves.  W and q are reloaded right after their last
+    // use in phase A, P after phase B and k^T after the state update: each
+    // a whole chunk before it is needed again.
     for (int c = cs; c < ce; ++c) {
         const int cn = min(c + 1, ce - 1);         // next chunk (the last one reloads itself)
 
@@ -850,30 +857,31 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
 #pragma unroll
         for (int kb = 0; kb < NKD; ++kb) {
             const Frag sh = xfrag(mySf, kb * NS);
+            const Frag sl = xfrag(mySf, kb * NS + NS - 1);
             M::mma(WSh, Wf[kb], sh);
+            if constexpr (NS == 2) M::mma(WSl, Wf[kb], sl);
+            Wf[kb] = vfrag(cn, G::F_W + rt * NKD + kb);
             M::mma(OQh, Qf[kb], sh);
-            if constexpr (NS == 2) {
-                const Frag sl = xfrag(mySf, kb * NS + 1);
-                M::mma(WSl, Wf[kb], sl);
-                M::mma(OQl, Qf[kb], sl);
-            }
+            if constexpr (NS == 2) M::mma(OQl, Qf[kb], sl);
+            Qf[kb] = kfrag(cn, G::F_Q + rt * NKD + kb);
         }
         const floatx4 U = u0 - (WSh + WSl);
         const floatx4 Oi = (OQh + OQl) * qs4;
         const floatx4 Uk = U * ks4;
+        u0 = __builtin_bit_cast(floatx4, vblk(cn)[u0f * 64 + lane]);
+        qs4 = scal4(cn, ro);
+        ks4 = scal4(cn, 64 + ro);
         {
             const int kc = rt / TPB, part = rt % TPB;
             TileOut<E>::put(myUf + (kc * NS) * 64, myUf + (kc * NS + NS - 1) * 64, lane, part, U);
             TileOut<E>::put(myKf + (kc * NS) * 64, myKf + (kc * NS + NS - 1) * 64, lane, part, Uk);
         }
+        // region order: matrix-core op, load, alternately
 #pragma unroll
-        for (int kb = 0; kb < NKD; ++kb) {
-            Wf[kb] = vfrag(cn, G::F_W + rt * NKD + kb);
-            Qf[kb] = kfrag(cn, G::F_Q + rt * NKD + kb);
+        for (int q = 0; q < 2 * NKD; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
-        u0 = __builtin_bit_cast(floatx4, vblk(cn)[u0f * 64 + lane]);
-        qs4 = scal4(cn, ro);
-        ks4 = scal4(cn, 64 + ro);
         lds_sync();
 
         // phase B: intra-chunk output P U, then the owned blocks of the state
@@ -927,6 +935,7 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
                     for (int t = 0; t < TPB; ++t) {
                         M::mma(Sa[t], Kf[o * TPB + t][kc], kh_[kc]);
                         if constexpr (NS == 2) M::mma(Sb[t], Kf[o * TPB + t][kc], kl_[kc]);
+                        Kf[o * TPB + t][kc] = kfrag(cn, G::F_KT + ((rt + 4 * o) * TPB + t) * NKC + kc);
                     }
 #pragma unroll
                 for (int t = 0; t < TPB; ++t) {
@@ -935,15 +944,13 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
                 }
             }
         }
-#pragma unroll
-        for (int o = 0; o < NOWN; ++o)
-#pragma unroll
-            for (int t = 0; t < TPB; ++t) {
-                const int mt = min(rt + 4 * o, NKD - 1) * TPB + t;
-#pragma unroll
-                for (int kc = 0; kc < NKC; ++kc) Kf[o * TPB + t][kc] = kfrag(cn, G::F_KT + mt * NKC + kc);
-            }
         gn = scal1(cn, 128);
+        // region order: matrix-core op, load, alternately
+#pragma unroll
+        for (int q = 0; q < 12; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
         lds_sync();
     }
 
