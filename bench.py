@@ -49,6 +49,25 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 C = 64
 
+# HBM bytes per launch of the prefill kernels on the T=4096 workload: rocprofv3
+# FETCH_SIZE and WRITE_SIZE (one run each, profiles/prefill_T4096_hbm_traffic.md),
+# scaled by what the same counters read for a 256 MiB device copy (x2.000 and
+# x1.000).  They hold only for the kernel source they were taken on; after any
+# change to it the bench reports traffic as null until the counters are retaken.
+PREFILL_SRC = os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", "gdn_prefill.hip")
+MEASURED_TRAFFIC = {
+    "source_sha256": "c5355043caf7f8c104e8de3b3f6d7f65234b4ad9743400f3ee0e4c28c603b1e7",
+    "scan": (100010 * 2.000 + 67584 * 1.000) * 1024,
+    "prepare": (47834 * 2.000 + 165047 * 1.000) * 1024,
+}
+
+
+def measured_traffic(kernel):
+    import hashlib
+    with open(PREFILL_SRC, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    return MEASURED_TRAFFIC.get(kernel) if sha == MEASURED_TRAFFIC["source_sha256"] else None
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -124,7 +143,8 @@ def bench_prefill(gdn, dev, steps, warmup):
     dom = "scan" if scan_ms >= prep_ms else "prepare"
     ach = kern[dom]["tflops"]
     roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "kernel": kern[dom]["kernels"],
+            "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom),
+            "traffic_unit": "bytes per launch", "kernel": kern[dom]["kernels"],
             "flops_per_launch": kern[dom]["flops_per_token_head"] * units,
             "mean_launch_ms": kern[dom]["mean_ms"]}
     whole = (fp + fs) * units / (ms_step * 1e-3) / 1e12
@@ -284,6 +304,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline prefill + decode only")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="headline prefill only (for hardware-counter runs)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run 3 plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -296,9 +320,20 @@ def main():
     import gated_deltanet_rule_amd as gdn
     dev = torch.device("cuda:0")
 
+    if args.copy_mib:
+        n = args.copy_mib << 18
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration: 3 copies of {args.copy_mib} MiB")
+        del src, dst
     log("prefill T=4096 ...")
     case, pf = bench_prefill(gdn, dev, args.steps, args.warmup)
     log(f"  {pf['ms_step']:.4f} ms/step, {pf['tokens_s']:.4g} tok/s")
+    if args.prefill_only:
+        return
     log("decode 64x128 ...")
     dec = bench_decode(gdn, dev)
     log(f"  {dec['ms_per_step']*1e3:.2f} us/step, {dec['roofline']['achieved']:.0f} GB/s")
