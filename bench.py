@@ -53,20 +53,32 @@ C = 64
 # FETCH_SIZE and WRITE_SIZE (one run each, profiles/prefill_T4096_hbm_traffic.md),
 # scaled by what the same counters read for a 256 MiB device copy (x2.000 and
 # x1.000).  They hold only for the kernel source they were taken on; after any
-# change to it the bench reports traffic as null until the counters are retaken.
+# change to its code (comments aside) the bench reports traffic as null until
+# the counters are retaken.
 PREFILL_SRC = os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", "gdn_prefill.hip")
 MEASURED_TRAFFIC = {
-    "source_sha256": "c5355043caf7f8c104e8de3b3f6d7f65234b4ad9743400f3ee0e4c28c603b1e7",
+    "source_sha256": "0fcc6550fecc97ee8453fe684ab6901812137b784f1eef4b7c05576eec60e5ba",
     "scan": (100010 * 2.000 + 67584 * 1.000) * 1024,
     "prepare": (47834 * 2.000 + 165047 * 1.000) * 1024,
 }
 
 
-def measured_traffic(kernel):
+def source_digest(path):
+    """SHA-256 of a C/HIP source with comments and blank space removed, so
+    that edits to comments alone do not invalidate measurements."""
     import hashlib
-    with open(PREFILL_SRC, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    return MEASURED_TRAFFIC.get(kernel) if sha == MEASURED_TRAFFIC["source_sha256"] else None
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = "\n".join(line.strip() for line in text.splitlines() if line.strip())
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
+def measured_traffic(kernel):
+    ok = source_digest(PREFILL_SRC) == MEASURED_TRAFFIC["source_sha256"]
+    return MEASURED_TRAFFIC.get(kernel) if ok else None
 
 
 def log(*a):

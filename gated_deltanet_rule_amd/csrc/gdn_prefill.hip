@@ -28,17 +28,16 @@
 //      attention P and U0 = T diag(beta) V.  Results go to the workspace as
 //      ready-made MFMA operand fragments (W, P, and q / k^T of the key head)
 //      and accumulator tiles (U0).
-//   3. scan_kernel, one workgroup per (sequence, value head, 2 column tiles
-//      of 16 state columns): walks the sequence's chunks in order with the
-//      state on chip for the whole sequence.  Inside a column tile the four
-//      token-row tiles of a chunk are split over four waves, so each wave
-//      runs ~30 matrix-core ops per chunk on the state chain:
-//        phase A (wave = token rows rt):  U = U0 - W S,  Q S
-//        phase B (wave = token rows rt):  O = qs * (Q S) + P U
-//                (wave = dk block rt):    S = gn * S + K^T (ks * U)
-//      U and S are exchanged through LDS between the phases; the chunk's
-//      shared operands are copied into LDS once per workgroup, prefetched one
-//      chunk ahead.
+//   3. scan_kernel, one workgroup per (sequence, value head, 16 state
+//      columns): walks the sequence's chunks in order with the state in
+//      registers for the whole sequence.  Each of the four waves takes 16
+//      token rows of a chunk and owns 32 rows of the state:
+//        phase A (token rows):  U = U0 - W S,  Q S
+//        phase B (token rows):  O = qs * (Q S) + P U
+//                (state rows):  S = gn * S + K^T (ks * U)
+//      U and S are exchanged through LDS as ready-made operand fragments;
+//      each wave loads its own operands from the workspace straight into
+//      registers, one chunk ahead.
 //
 // Norms, scale, beta and decay are folded into per-row / per-column scalars
 // of raw (bf16) operands, so the inputs are used as MFMA operands exactly as
