@@ -28,6 +28,10 @@ SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_prefill.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # matrix-core results in ordinary VGPRs: the kernels feed accumulators
+          # straight into vector arithmetic, which AGPRs would route through
+          # a copy per register
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 
 
