@@ -131,14 +131,20 @@ def bench_prefill(gdn, dev, steps, warmup):
 
     for _ in range(warmup):
         step()
-    timers = [Timer(stream, 3) for _ in range(steps)]
+    # the step rate: steps issued back to back, nothing else on the stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(timers[i])
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
+    # per-kernel launch durations, from HIP events around each launch on the
+    # launch stream (a separate pass: the event records add gaps of their own)
+    timers = [Timer(stream, 3) for _ in range(steps)]
+    for i in range(steps):
+        step(timers[i])
+    torch.cuda.synchronize()
     prep_ms = statistics.mean(t.ms(0, 1) for t in timers)
     scan_ms = statistics.mean(t.ms(1, 2) for t in timers)
     assert torch.isfinite(out).all() and torch.isfinite(state_out).all()

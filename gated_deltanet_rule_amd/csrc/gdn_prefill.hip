@@ -307,6 +307,7 @@ struct PrepParams {
     char *vblocks, *kblocks;
     int H_k, H_v;
     float scale, eps;
+    int single_T;      // >= 0: one sequence of this many tokens, no chunk table
 };
 
 // LDS of the preparation kernel.  Rows are padded so that the row stride is
@@ -361,9 +362,18 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
     float *sColh = sBetah + NH * C;                             // [NH][C] beta_c e^{G_c} / |k_c|  (columns of T for W)
 
     const int chunk = blockIdx.x, kh = blockIdx.y;
-    if (chunk >= pp.hdr[0]) return;
-    const ChunkEntry ce = pp.ent[chunk];
-    const int t0 = ce.t0, len = ce.len;
+    int t0, len;
+    if (pp.single_T >= 0) {
+        // a single sequence covers tokens [0, T): chunk c is [64c, min(64c + 64, T))
+        if (chunk * C >= pp.single_T) return;
+        t0 = chunk * C;
+        len = min(C, pp.single_T - t0);
+    } else {
+        if (chunk >= pp.hdr[0]) return;
+        const ChunkEntry ce = pp.ent[chunk];
+        t0 = ce.t0;
+        len = ce.len;
+    }
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, qd = lane >> 4;
@@ -690,6 +700,7 @@ struct ScanParams {
     const char *vblocks, *kblocks;
     int H_k, H_v;
     int64_t slot_stride;
+    int single_T;      // >= 0: one sequence of this many tokens, no chunk table
 };
 
 template <int DK, int DV, int CT, typename E> struct ScanLds {
@@ -789,7 +800,9 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
         }
     }
 
-    const int cs = sp.cstart[i], ce = sp.cstart[i + 1];
+    const bool single = sp.single_T >= 0;
+    const int cs = single ? 0 : sp.cstart[i];
+    const int ce = single ? (sp.single_T + C - 1) / C : sp.cstart[i + 1];
     const size_t vstride = (size_t)G::VBLK * 1024, kstride = (size_t)G::KBLK * 1024;
     const char *vbase = sp.vblocks + (size_t)h * vstride;
     const char *kbase = sp.kblocks + (size_t)kh * kstride;
@@ -833,8 +846,8 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
     floatx4 qs4 = scal4(c0, ro), ks4 = scal4(c0, 64 + ro);
     float gn = scal1(c0, 128);
     // the sequence's token range; its chunks are consecutive 64-token pieces
-    const int tbeg = cs < ce ? sp.ent[cs].t0 : 0;
-    const int tend = cs < ce ? sp.ent[ce - 1].t0 + sp.ent[ce - 1].len : 0;
+    const int tbeg = single || cs >= ce ? 0 : sp.ent[cs].t0;
+    const int tend = single ? sp.single_T : cs < ce ? sp.ent[ce - 1].t0 + sp.ent[ce - 1].len : 0;
     // Let the first chunk's operands land before the loop: the loop's waits
     // then only have to account for the loads issued inside it.
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
@@ -1005,16 +1018,23 @@ template <int DK, int DV, typename E>
 hipError_t prepare_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
 {
     const WsPtrs w = ws_ptrs(p, a);
-    hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.n_seqs,
-                       (int)a.total_tokens, w.L.max_chunks, w.hdr, w.ent, w.cstart);
-    hipError_t e = hipGetLastError();
+    // one sequence: cu_seqlens is [0, total_tokens] by contract, and both
+    // kernels derive the chunks arithmetically (no chunk-table launch)
+    const bool single = a.n_seqs == 1;
+    hipError_t e = hipSuccess;
+    if (!single) {
+        hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.n_seqs,
+                           (int)a.total_tokens, w.L.max_chunks, w.hdr, w.ent, w.cstart);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess || a.total_tokens == 0) return e;
     PrepParams pp{a.q, a.k, a.v, a.g, a.beta, w.hdr, w.ent, w.vblocks, w.kblocks,
-                  p.H_k, p.H_v, p.scale, p.eps};
+                  p.H_k, p.H_v, p.scale, p.eps, single ? (int)a.total_tokens : -1};
     constexpr size_t lds = PrepLds<DK, DV, E>::BYTES;
     e = set_lds(prep_kernel<DK, DV, E>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prep_kernel<DK, DV, E>), dim3(w.L.max_chunks, p.H_k), dim3(256), lds, st, pp);
+    const int chunks = single ? (int)((a.total_tokens + C - 1) / C) : w.L.max_chunks;
+    hipLaunchKernelGGL((prep_kernel<DK, DV, E>), dim3(chunks, p.H_k), dim3(256), lds, st, pp);
     return hipGetLastError();
 }
 
@@ -1024,7 +1044,8 @@ hipError_t scan_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
     const WsPtrs w = ws_ptrs(p, a);
     constexpr int CT = 1;    // column tiles per workgroup
     ScanParams sp{a.state_in, a.state_out, a.out, a.slot_in, a.slot_out, w.cstart, w.ent,
-                  w.vblocks, w.kblocks, p.H_k, p.H_v, p.slot_stride};
+                  w.vblocks, w.kblocks, p.H_k, p.H_v, p.slot_stride,
+                  a.n_seqs == 1 ? (int)a.total_tokens : -1};
     constexpr size_t lds = ScanLds<DK, DV, CT, E>::BYTES;
     hipError_t e = set_lds(scan_kernel<DK, DV, CT, E, OT>, lds);
     if (e != hipSuccess) return e;

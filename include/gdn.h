@@ -164,8 +164,10 @@ gdn_status gdn_chunked_prefill(const gdn_dims *dims,
  * (build_delta_net_chunking: g_cumsum, decay_mask, the beta*(k k^T)*decay
  * matrix and its triangular solve, k_cumdecay, the beta-weighted values
  * ("value" = T diag(beta) V) and the decayed q.k attention), written into
- * `workspace` together with the chunk table built from cu_seqlens.  Reads q,
- * k, v, g, beta, cu_seqlens.
+ * `workspace` together with the chunk table built from cu_seqlens (with
+ * n_seqs == 1 no table is built: cu_seqlens is [0, total_tokens] by contract
+ * and the chunks follow from total_tokens).  Reads q, k, v, g, beta and, for
+ * n_seqs > 1, cu_seqlens.
  *
  * gdn_prefill_scan: the state-dependent part (v_prime / v_new, attn_inter +
  * v_attn, and the chunk-end state update), chunk after chunk per sequence,
