@@ -763,7 +763,10 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
     u32x4 *sUf = reinterpret_cast<u32x4 *>(smem + L::SF);                 // [CT][NKC][NS][64]
     u32x4 *sKf = reinterpret_cast<u32x4 *>(smem + L::SF + L::UF);         // [CT][NKC][NS][64]
 
-    const int i = blockIdx.x, h = blockIdx.y, cg = blockIdx.z;
+    // grid (value head, column tile, sequence): the column tiles of a head sit
+    // H_v workgroups apart, so with H_v a multiple of 8 they share an XCD
+    // (and its L2, which serves their common operand fragments)
+    const int h = blockIdx.x, cg = blockIdx.y, i = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int ctl = wv >> 2, rt = wv & 3;
@@ -1046,10 +1049,15 @@ hipError_t scan_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
     ScanParams sp{a.state_in, a.state_out, a.out, a.slot_in, a.slot_out, w.cstart, w.ent,
                   w.vblocks, w.kblocks, p.H_k, p.H_v, p.slot_stride,
                   a.n_seqs == 1 ? (int)a.total_tokens : -1};
-    constexpr size_t lds = ScanLds<DK, DV, CT, E>::BYTES;
-    hipError_t e = set_lds(scan_kernel<DK, DV, CT, E, OT>, lds);
+    // With several sequences, one scan workgroup per CU: two workgroups on
+    // one CU each run about 3x slower per chunk (they contend for its vector
+    // memory path and VALU), so the reservation below (more LDS than half a
+    // CU holds) keeps them apart.
+    constexpr size_t lds_min = ScanLds<DK, DV, CT, E>::BYTES;
+    const size_t lds = a.n_seqs > 1 ? std::max<size_t>(lds_min, 96 * 1024) : lds_min;
+    hipError_t e = set_lds(scan_kernel<DK, DV, CT, E, OT>, 96 * 1024);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_kernel<DK, DV, CT, E, OT>), dim3(a.n_seqs, p.H_v, DV / (16 * CT)),
+    hipLaunchKernelGGL((scan_kernel<DK, DV, CT, E, OT>), dim3(p.H_v, DV / (16 * CT), a.n_seqs),
                        dim3(CT * 256), lds, st, sp);
     return hipGetLastError();
 }
