@@ -21,6 +21,8 @@ Alongside (same JSON line):
                 128 MiB, in place), tokens/s and state bytes / kernel time
                 against the 8 TB/s HBM peak; also a ping-pong run (two pools,
                 256 MiB footprint).
+  decode_multi  gdn_recurrent_multi on 64 sequences x 4 tokens (speculative
+                verification), state in place; HBM roofline on state + I/O.
   varlen        8 packed sequences of 17..8192 tokens (12221), one call.
   stream        65536 tokens as 128 calls of 512 with the state carried.
   cpu_baseline  the fp64 oracle (test infrastructure, never tuned) on the
@@ -234,6 +236,38 @@ def bench_decode(gdn, dev, reps=3):
             "ping_pong": res["ping_pong"], "in_place": ip}
 
 
+def bench_decode_multi(gdn, dev, tokens=4, reps=20):
+    """gdn_recurrent_multi: 64 sequences x `tokens` tokens (speculative
+    verification), state pool in place; HBM roofline on state + I/O bytes."""
+    case = gi.make_case(f"spec64x{tokens}", [tokens] * 64, dtype="bf16", seed=40 + tokens,
+                        **gi.QWEN3_NEXT_HEADS)
+    d = to_dev(case, dev)
+    out = torch.empty(d["v"].shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    call = lambda: gdn.decode_multi(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"],
+                                    d["pool"], out, d["cu"], d["slot_in"], d["slot_out"],
+                                    stream=stream)
+    for _ in range(3):
+        call()
+    t = Timer(stream, reps + 1)
+    torch.cuda.synchronize()
+    t.mark(0)
+    for r in range(reps):
+        call()
+        t.mark(r + 1)
+    torch.cuda.synchronize()
+    ms = statistics.median(t.ms(r, r + 1) for r in range(reps))
+    N, H_k, H_v, dk, dv, T = 64, case.H_k, case.H_v, case.d_k, case.d_v, case.total_tokens
+    by = N * H_v * dk * dv * 4 * 2 + T * (2 * H_k * dk * 2 + H_v * dv * 2 + H_v * dv * 4 + H_v * 8)
+    gbs = by / (ms * 1e-3) / 1e9
+    return {"workload": f"multi-token decode: 64 sequences x {tokens} tokens, H_k=16 H_v=32 "
+                        "d=128, bf16 in, fp32 out, state slots in place",
+            "ms_per_call": ms, "tokens_s": T / (ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "kernel": "decode_multi_kernel",
+                         "bytes_per_launch": by}}
+
+
 def bench_varlen(gdn, dev, reps=10):
     case = gi.config3()
     d = to_dev(case, dev)
@@ -356,6 +390,10 @@ def main():
     dec = bench_decode(gdn, dev)
     log(f"  {dec['ms_per_step']*1e3:.2f} us/step, {dec['roofline']['achieved']:.0f} GB/s")
     extra = {}
+    log("multi-token decode 64x4 ...")
+    extra["decode_multi"] = bench_decode_multi(gdn, dev)
+    log(f"  {extra['decode_multi']['ms_per_call']*1e3:.1f} us/call, "
+        f"{extra['decode_multi']['roofline']['achieved']:.0f} GB/s")
     if not args.quick:
         log("varlen ...")
         extra["varlen"] = bench_varlen(gdn, dev)

@@ -64,6 +64,8 @@ def _load() -> ctypes.CDLL:
     lib.gdn_prefill_prepare.restype = ctypes.c_int
     lib.gdn_prefill_scan.argtypes = [D, P, P, P, P, P, I32, I64, P, SZ, P]
     lib.gdn_prefill_scan.restype = ctypes.c_int
+    lib.gdn_recurrent_multi.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, I32, I64, P]
+    lib.gdn_recurrent_multi.restype = ctypes.c_int
     return lib
 
 
@@ -71,7 +73,7 @@ lib = _load()
 
 EXPORTED = ["gdn_version", "gdn_status_string", "gdn_last_error",
             "gdn_prefill_workspace_size", "gdn_chunked_prefill", "gdn_prefill_prepare",
-            "gdn_prefill_scan", "gdn_recurrent_step"]
+            "gdn_prefill_scan", "gdn_recurrent_step", "gdn_recurrent_multi"]
 
 
 def version() -> int:
@@ -234,3 +236,24 @@ def decode_step(q, k, v, g, beta, state_in, state_out, out, slot_in, slot_out, *
                                   _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
                                   _ptr(slot_in), _ptr(slot_out), slot_out.shape[0],
                                   _stream(stream)))
+
+
+def decode_multi(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in, slot_out, *,
+                 scale: float = 0.0, eps: float = 1e-6, stream=None) -> None:
+    """gdn_recurrent_multi on torch tensors: a few tokens per sequence, packed
+    by cu_seqlens as for prefill, recurrent form, no workspace."""
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, q.dtype, dev)
+    _need(out, "out", None, dev)
+    for t, name in ((g, "g"), (beta, "beta"), (state_out, "state_out")):
+        _need(t, name, torch.float32, dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, dev)
+    for t, name in ((cu_seqlens, "cu_seqlens"), (slot_in, "slot_in"), (slot_out, "slot_out")):
+        _need(t, name, torch.int32, dev)
+    dims = _dims_from(q, v, out, scale, eps, state_out)
+    _check(lib.gdn_recurrent_multi(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                   _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
+                                   _ptr(cu_seqlens), _ptr(slot_in), _ptr(slot_out),
+                                   slot_out.shape[0], q.shape[0], _stream(stream)))

@@ -245,4 +245,27 @@ gdn_status gdn_recurrent_step(const gdn_dims *dims, const void *q, const void *k
     return GDN_OK;
 }
 
+gdn_status gdn_recurrent_multi(const gdn_dims *dims, const void *q, const void *k,
+                               const void *v, const float *g, const float *beta,
+                               const float *state_in, float *state_out, void *out,
+                               const int32_t *cu_seqlens, const int32_t *slot_in,
+                               const int32_t *slot_out, int32_t n_seqs,
+                               int64_t total_tokens, void *stream)
+{
+    g_last_error[0] = 0;
+    gdn::Problem p;
+    gdn_status st = resolve(dims, &p);
+    if (st == GDN_OK) st = check_counts(n_seqs, total_tokens);
+    if (st == GDN_OK) st = check_prepare_inputs(q, k, v, g, beta, cu_seqlens);
+    if (st == GDN_OK) st = check_scan_inputs(state_in, state_out, out, slot_in, slot_out);
+    if (st != GDN_OK) return st;
+    if (n_seqs > 0x7fffffff / 2) return fail(GDN_ERR_UNSUPPORTED, "n_seqs too large");
+    if (p.H_v > 65535) return fail(GDN_ERR_UNSUPPORTED, "H_v above 65535");
+    gdn::DecodeMultiArgs a{q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in,
+                           slot_out, n_seqs, total_tokens};
+    hipError_t e = gdn::launch_decode_multi(p, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "multi-token decode launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
 }  // extern "C"

@@ -29,6 +29,20 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const Problem &p, const DecodeArgs &a, hipStream_t s);
 
+// several tokens per sequence, recurrent form, no workspace
+struct DecodeMultiArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const float *state_in;     // may be null: every sequence starts at zero
+    float *state_out;
+    void *out;
+    const int32_t *cu_seqlens, *slot_in, *slot_out;
+    int32_t n_seqs;
+    int64_t total_tokens;
+};
+
+hipError_t launch_decode_multi(const Problem &p, const DecodeMultiArgs &a, hipStream_t s);
+
 struct PrefillArgs {
     const void *q, *k, *v;
     const float *g, *beta;

@@ -23,7 +23,8 @@
  * chunked graph otherwise):
  *   gdn_chunked_prefill  -- any number of tokens per sequence, chunked (64)
  *                           WY form on matrix cores (build_delta_net_chunking);
- *   gdn_recurrent_step   -- exactly one token per sequence.
+ *   gdn_recurrent_step   -- exactly one token per sequence;
+ *   gdn_recurrent_multi  -- a few tokens per sequence, recurrent form.
  * State slots follow build_layer_attn_linear_core of the ik_llama.cpp page: the
  * state is read from a per-sequence slot (or starts at zero when the sequence
  * starts) and the new state is written back into a slot.
@@ -201,6 +202,28 @@ gdn_status gdn_recurrent_step(const gdn_dims *dims,
                               void *out, const int32_t *slot_in,
                               const int32_t *slot_out, int32_t n_seqs,
                               void *stream);
+
+/*
+ * Several tokens per sequence in the recurrent form: the single-chunk case
+ * the page "Optimization: Qwen3 next autoregressive pass (#17996)" removed
+ * from build_layer_attn_linear (build_delta_net_recurrent, used when a
+ * sequence brings at most one chunk), here for short multi-token batches such
+ * as speculative-decoding verification.  Same arguments, layouts and slot
+ * semantics as gdn_chunked_prefill (tokens packed by cu_seqlens), no
+ * workspace.  The tokens of a sequence are processed one after the other with
+ * the state block in registers: each state is read and written once per call,
+ * and the work per token is that of gdn_recurrent_step.  Correct for any
+ * length; for sequences longer than about one chunk gdn_chunked_prefill is
+ * faster.  Empty sequences pass their state through (zero if slot_in < 0).
+ */
+gdn_status gdn_recurrent_multi(const gdn_dims *dims,
+                               const void *q, const void *k, const void *v,
+                               const float *g, const float *beta,
+                               const float *state_in, float *state_out,
+                               void *out, const int32_t *cu_seqlens,
+                               const int32_t *slot_in, const int32_t *slot_out,
+                               int32_t n_seqs, int64_t total_tokens,
+                               void *stream);
 
 #ifdef __cplusplus
 }

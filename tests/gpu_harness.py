@@ -66,6 +66,18 @@ def gpu_prefill(case, d=None, inplace=True, chunks=None, out_dtype=torch.float32
     return out, pool_out
 
 
+def gpu_decode_multi(case, d=None, inplace=True, out_dtype=torch.float32):
+    """Run a Case (tokens packed by cu_seqlens) through gdn.decode_multi."""
+    import gated_deltanet_rule_amd as gdn
+    d = d or dev_case(case)
+    out = torch.empty(d["v"].shape, dtype=out_dtype, device=d["v"].device)
+    pool_out = d["pool"] if inplace else d["pool"].clone()
+    gdn.decode_multi(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], pool_out, out,
+                     d["cu"], d["slot_in"], d["slot_out"])
+    torch.cuda.synchronize()
+    return out, pool_out
+
+
 def oracle_case(case, heads=None):
     return oracle.run_case(case, heads=heads)
 

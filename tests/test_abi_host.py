@@ -143,3 +143,26 @@ def test_decode_validation():
     assert call(n=0) == 1
     assert call(sout=FAKE + 1) == 1
     assert gdn.lib.gdn_recurrent_step(None, *([None] * 10), 1, None) == 1
+
+
+def test_multi_decode_validation():
+    P = ctypes.c_void_p
+    d = _dims()
+
+    def call(**over):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, si=FAKE, so=FAKE, out=FAKE,
+                 cu=FAKE, sin=FAKE, sout=FAKE, n=4, T=16)
+        a.update(over)
+        return gdn.lib.gdn_recurrent_multi(
+            ctypes.byref(d), P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]),
+            P(a["si"]), P(a["so"]), P(a["out"]), P(a["cu"]), P(a["sin"]), P(a["sout"]),
+            a["n"], a["T"], None)
+    assert call(q=0) == 1
+    assert call(cu=0) == 1
+    assert call(so=0) == 1
+    assert call(out=FAKE + 2) == 1
+    assert call(n=0) == 1
+    assert call(T=-1) == 1
+    assert call(sout=FAKE + 1) == 1
+    assert gdn.lib.gdn_recurrent_multi(None, *([None] * 11), 1, 4, None) == 1
+
