@@ -27,6 +27,8 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_OK = 0
 GDN_F32 = 0
 GDN_BF16 = 1
+GDN_GATES_FINAL = 0
+GDN_GATES_RAW = 1
 
 
 class GdnError(RuntimeError):
@@ -40,7 +42,8 @@ class Dims(ctypes.Structure):
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("slot_stride", ctypes.c_int64), ("scale", ctypes.c_float),
-                ("eps", ctypes.c_float)]
+                ("eps", ctypes.c_float), ("gate_mode", ctypes.c_int32),
+                ("ssm_a", ctypes.c_void_p), ("ssm_dt", ctypes.c_void_p)]
 
 
 def _load() -> ctypes.CDLL:
@@ -95,19 +98,32 @@ def _code(dtype: torch.dtype, what: str) -> int:
 
 def make_dims(H_k: int, H_v: int, d_k: int, d_v: int, dtype: torch.dtype,
               out_dtype: torch.dtype = torch.float32, scale: float = 0.0,
-              eps: float = 1e-6, slot_stride: int = 0) -> Dims:
-    return Dims(H_k, H_v, d_k, d_v, _code(dtype, "q/k/v"), _code(out_dtype, "out"),
-                slot_stride, scale, eps)
+              eps: float = 1e-6, slot_stride: int = 0, gates=None) -> Dims:
+    """gates: None (g and beta given as the operator takes them) or a pair
+    (ssm_a, ssm_dt) of fp32 [H_v] device tensors, with g and beta then holding
+    the raw projections a and b (the kernels apply the activations)."""
+    d = Dims(H_k, H_v, d_k, d_v, _code(dtype, "q/k/v"), _code(out_dtype, "out"),
+             slot_stride, scale, eps, GDN_GATES_FINAL, None, None)
+    if gates is not None:
+        ssm_a, ssm_dt = gates
+        for t, name in ((ssm_a, "ssm_a"), (ssm_dt, "ssm_dt")):
+            _need(t, name, torch.float32)
+            if t.numel() != H_v:
+                raise ValueError(f"{name} must hold H_v={H_v} values")
+        d.gate_mode = GDN_GATES_RAW
+        d.ssm_a = ssm_a.data_ptr()
+        d.ssm_dt = ssm_dt.data_ptr()
+    return d
 
 
-def _dims_from(q, v, out, scale, eps, state) -> Dims:
+def _dims_from(q, v, out, scale, eps, state, gates=None) -> Dims:
     if q.dim() != 3 or v.dim() != 3 or out.shape != v.shape:
         raise ValueError("q must be [T, H_k, d_k], v and out [T, H_v, d_v]")
     stride = 0
     if state is not None:
         stride = state.stride(0) if state.dim() == 4 else 0
     return make_dims(q.shape[1], v.shape[1], q.shape[2], v.shape[2], q.dtype, out.dtype,
-                     scale, eps, stride)
+                     scale, eps, stride, gates)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -140,8 +156,9 @@ def workspace_size(dims: Dims, n_seqs: int, total_tokens: int) -> int:
 
 def prefill(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in, slot_out,
             workspace: Optional[torch.Tensor] = None, *, scale: float = 0.0,
-            eps: float = 1e-6, stream=None) -> None:
-    """gdn_chunked_prefill on torch tensors (asynchronous on `stream`)."""
+            eps: float = 1e-6, stream=None, gates=None) -> None:
+    """gdn_chunked_prefill on torch tensors (asynchronous on `stream`).
+    gates=(ssm_a, ssm_dt): g and beta are the raw projections a, b."""
     dev = q.device
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, name, q.dtype, dev)
@@ -152,7 +169,7 @@ def prefill(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in, slo
         _need(state_in, "state_in", torch.float32, dev)
     for t, name in ((cu_seqlens, "cu_seqlens"), (slot_in, "slot_in"), (slot_out, "slot_out")):
         _need(t, name, torch.int32, dev)
-    dims = _dims_from(q, v, out, scale, eps, state_out)
+    dims = _dims_from(q, v, out, scale, eps, state_out, gates)
     n_seqs = slot_out.shape[0]
     T = q.shape[0]
     need = workspace_size(dims, n_seqs, T)
@@ -186,8 +203,8 @@ class PrefillPlan:
     ``prepare(...)`` then ``scan(...)`` (ordered on the caller's streams)."""
 
     def __init__(self, q, v, out, n_seqs: int, *, state=None, scale: float = 0.0,
-                 eps: float = 1e-6, workspace: Optional[torch.Tensor] = None):
-        self.dims = _dims_from(q, v, out, scale, eps, state)
+                 eps: float = 1e-6, workspace: Optional[torch.Tensor] = None, gates=None):
+        self.dims = _dims_from(q, v, out, scale, eps, state, gates)
         self.n_seqs = n_seqs
         self.T = q.shape[0]
         need = workspace_size(self.dims, n_seqs, self.T)
@@ -219,7 +236,7 @@ class PrefillPlan:
 
 
 def decode_step(q, k, v, g, beta, state_in, state_out, out, slot_in, slot_out, *,
-                scale: float = 0.0, eps: float = 1e-6, stream=None) -> None:
+                scale: float = 0.0, eps: float = 1e-6, stream=None, gates=None) -> None:
     """gdn_recurrent_step on torch tensors: one token per sequence."""
     dev = q.device
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
@@ -231,7 +248,7 @@ def decode_step(q, k, v, g, beta, state_in, state_out, out, slot_in, slot_out, *
         _need(state_in, "state_in", torch.float32, dev)
     for t, name in ((slot_in, "slot_in"), (slot_out, "slot_out")):
         _need(t, name, torch.int32, dev)
-    dims = _dims_from(q, v, out, scale, eps, state_out)
+    dims = _dims_from(q, v, out, scale, eps, state_out, gates)
     _check(lib.gdn_recurrent_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                   _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
                                   _ptr(slot_in), _ptr(slot_out), slot_out.shape[0],
@@ -239,7 +256,7 @@ def decode_step(q, k, v, g, beta, state_in, state_out, out, slot_in, slot_out, *
 
 
 def decode_multi(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in, slot_out, *,
-                 scale: float = 0.0, eps: float = 1e-6, stream=None) -> None:
+                 scale: float = 0.0, eps: float = 1e-6, stream=None, gates=None) -> None:
     """gdn_recurrent_multi on torch tensors: a few tokens per sequence, packed
     by cu_seqlens as for prefill, recurrent form, no workspace."""
     dev = q.device
@@ -252,7 +269,7 @@ def decode_multi(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in
         _need(state_in, "state_in", torch.float32, dev)
     for t, name in ((cu_seqlens, "cu_seqlens"), (slot_in, "slot_in"), (slot_out, "slot_out")):
         _need(t, name, torch.int32, dev)
-    dims = _dims_from(q, v, out, scale, eps, state_out)
+    dims = _dims_from(q, v, out, scale, eps, state_out, gates)
     _check(lib.gdn_recurrent_multi(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                    _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
                                    _ptr(cu_seqlens), _ptr(slot_in), _ptr(slot_out),

@@ -55,6 +55,17 @@ gdn_status resolve(const gdn_dims *d, gdn::Problem *p)
     p->slot_stride = stride;
     p->scale = d->scale == 0.f ? 1.0f / sqrtf((float)d->d_k) : d->scale;
     p->eps = d->eps;
+    if (d->gate_mode != GDN_GATES_FINAL && d->gate_mode != GDN_GATES_RAW)
+        return fail(GDN_ERR_INVALID_ARG, "unknown gate_mode %d", d->gate_mode);
+    p->ssm_a = p->ssm_dt = nullptr;
+    if (d->gate_mode == GDN_GATES_RAW) {
+        if (!d->ssm_a || !d->ssm_dt)
+            return fail(GDN_ERR_INVALID_ARG, "GDN_GATES_RAW needs ssm_a and ssm_dt");
+        if (!aligned(d->ssm_a, 4) || !aligned(d->ssm_dt, 4))
+            return fail(GDN_ERR_INVALID_ARG, "ssm_a / ssm_dt are not 4-byte aligned");
+        p->ssm_a = d->ssm_a;
+        p->ssm_dt = d->ssm_dt;
+    }
     return GDN_OK;
 }
 

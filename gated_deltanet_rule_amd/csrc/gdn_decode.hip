@@ -20,13 +20,22 @@ namespace {
 
 constexpr int kDecodeThreads = 256;
 
+// Without raw gates the per-head parameters are never used, but they are
+// still loaded (unconditional loads keep the compiler's count of outstanding
+// memory operations exact): point them at g, which holds at least H_v values
+// whenever a token exists.
+Gates gates_of(const Problem &p, const float *g)
+{
+    return p.ssm_a ? Gates{p.ssm_a, p.ssm_dt, 1} : Gates{g, g, 0};
+}
+
 template <int DK, int DV, int DVB, typename E, typename OT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const float *state_in, float *state_out, OT *__restrict__ out,
     const int32_t *__restrict__ slot_in, const int32_t *__restrict__ slot_out,
-    int H_k, int H_v, int64_t slot_stride, float scale, float eps)
+    int H_k, int H_v, int64_t slot_stride, float scale, float eps, Gates gates)
 {
     constexpr int CG = DVB / 4;                 // float4 column groups
     constexpr int RG = kDecodeThreads / CG;     // row groups
@@ -65,8 +74,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const int64_t qk_off = ((int64_t)i * H_k + kh) * DK;
     if (tid < DK) sk[tid] = to_f32(k[qk_off + tid]);
     else if (tid < 2 * DK) sq[tid - DK] = to_f32(q[qk_off + tid - DK]);
-    const float gi = g[(int64_t)i * H_v + h];
-    const float bi = beta[(int64_t)i * H_v + h];
+    float gi = g[(int64_t)i * H_v + h];
+    float bi = beta[(int64_t)i * H_v + h];
+    {
+        const float rate = gates.rate[h], bias = gates.bias[h];
+        gi = gates.raw ? gate_g(gi, bias, rate) : gi;
+        bi = gates.raw ? gate_beta(bi) : bi;
+    }
     const E *vp = v + ((int64_t)i * H_v + h) * DV + col;
     const float v0 = to_f32(vp[0]), v1 = to_f32(vp[1]), v2 = to_f32(vp[2]), v3 = to_f32(vp[3]);
     __syncthreads();
@@ -152,7 +166,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(
     const float *state_in, float *state_out, OT *__restrict__ out,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ slot_in,
     const int32_t *__restrict__ slot_out, int T, int H_k, int H_v, int64_t slot_stride,
-    float scale, float eps)
+    float scale, float eps, Gates gates)
 {
     constexpr int CG = DV / 4;                  // float4 column groups
     constexpr int RG = kDecodeThreads / CG;     // row groups
@@ -201,6 +215,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(
         r.kq = tid < DK ? to_f32(k[qk_off + tid]) : tid < 2 * DK ? to_f32(q[qk_off + tid - DK]) : 0.f;
         r.gt = g[(int64_t)t * H_v + h];
         r.bt = beta[(int64_t)t * H_v + h];
+        const float rate = gates.rate[h], bias = gates.bias[h];
+        r.gt = gates.raw ? gate_g(r.gt, bias, rate) : r.gt;
+        r.bt = gates.raw ? gate_beta(r.bt) : r.bt;
         const E *vp = v + ((int64_t)t * H_v + h) * DV + col;
 #pragma unroll
         for (int j = 0; j < 4; ++j) r.vv[j] = to_f32(vp[j]);
@@ -292,7 +309,8 @@ hipError_t launch_multi_t(const Problem &p, const DecodeMultiArgs &a, hipStream_
                        st, static_cast<const E *>(a.q), static_cast<const E *>(a.k),
                        static_cast<const E *>(a.v), a.g, a.beta, a.state_in, a.state_out,
                        static_cast<OT *>(a.out), a.cu_seqlens, a.slot_in, a.slot_out,
-                       (int)a.total_tokens, p.H_k, p.H_v, p.slot_stride, p.scale, p.eps);
+                       (int)a.total_tokens, p.H_k, p.H_v, p.slot_stride, p.scale, p.eps,
+                       gates_of(p, a.g));
     return hipGetLastError();
 }
 
@@ -325,7 +343,7 @@ hipError_t launch_t(const Problem &p, const DecodeArgs &a, hipStream_t st)
                        static_cast<const E *>(a.q), static_cast<const E *>(a.k),
                        static_cast<const E *>(a.v), a.g, a.beta, a.state_in, a.state_out,
                        static_cast<OT *>(a.out), a.slot_in, a.slot_out, p.H_k, p.H_v,
-                       p.slot_stride, p.scale, p.eps);
+                       p.slot_stride, p.scale, p.eps, gates_of(p, a.g));
     return hipGetLastError();
 }
 

@@ -62,6 +62,21 @@ __device__ __forceinline__ void lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// The layer's gate activations, raw projections -> operator inputs:
+// beta = sigmoid(b) and g = softplus(a + bias) * rate, with softplus(x) =
+// log(1 + e^x) evaluated as max(x, 0) + log1p(e^-|x|) so that nothing
+// overflows.  `raw` selects them; otherwise a and b pass through unchanged.
+struct Gates {
+    const float *rate;     // [H_v] decay rate (<= 0)
+    const float *bias;     // [H_v] gate bias
+    int raw;
+};
+__device__ __forceinline__ float gate_g(float a, float bias, float rate) {
+    const float x = a + bias;
+    return (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))) * rate;
+}
+__device__ __forceinline__ float gate_beta(float b) { return 1.f / (1.f + expf(-b)); }
+
 // Wave-wide (64 lanes) sum.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

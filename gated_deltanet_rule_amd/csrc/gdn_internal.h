@@ -15,6 +15,9 @@ struct Problem {
     int out_bf16;          // 1: out is bfloat16, 0: fp32
     int64_t slot_stride;   // elements
     float scale, eps;
+    // raw gates: beta = sigmoid(b), g = softplus(a + ssm_dt[h]) * ssm_a[h]
+    const float *ssm_a;    // null: g and beta are given as the operator takes them
+    const float *ssm_dt;
 };
 
 struct DecodeArgs {

@@ -308,6 +308,7 @@ struct PrepParams {
     int H_k, H_v;
     float scale, eps;
     int single_T;      // >= 0: one sequence of this many tokens, no chunk table
+    Gates gates;       // raw gate projections, or g and beta as given
 };
 
 // LDS of the preparation kernel.  Rows are padded so that the row stride is
@@ -392,8 +393,11 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
     const int lrow = min(lane, len - 1);
     auto load_gb = [&](int j0) {
         const int hh = kh * ratio + min(j0 + w, ratio - 1);
-        const float gl = pp.g[(size_t)(t0 + lrow) * pp.H_v + hh];
-        const float bl = pp.beta[(size_t)(t0 + lrow) * pp.H_v + hh];
+        float gl = pp.g[(size_t)(t0 + lrow) * pp.H_v + hh];
+        float bl = pp.beta[(size_t)(t0 + lrow) * pp.H_v + hh];
+        const float rate = pp.gates.rate[hh], bias = pp.gates.bias[hh];
+        gl = pp.gates.raw ? gate_g(gl, bias, rate) : gl;
+        bl = pp.gates.raw ? gate_beta(bl) : bl;
         gq = lane < len ? gl : 0.f;
         bq = lane < len ? bl : 0.f;
     };
@@ -1032,7 +1036,9 @@ hipError_t prepare_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
     }
     if (e != hipSuccess || a.total_tokens == 0) return e;
     PrepParams pp{a.q, a.k, a.v, a.g, a.beta, w.hdr, w.ent, w.vblocks, w.kblocks,
-                  p.H_k, p.H_v, p.scale, p.eps, single ? (int)a.total_tokens : -1};
+                  p.H_k, p.H_v, p.scale, p.eps, single ? (int)a.total_tokens : -1,
+                  // without raw gates the parameter loads read g (see gates_of in gdn_decode.hip)
+                  p.ssm_a ? Gates{p.ssm_a, p.ssm_dt, 1} : Gates{a.g, a.g, 0}};
     constexpr size_t lds = PrepLds<DK, DV, E>::BYTES;
     e = set_lds(prep_kernel<DK, DV, E>, lds);
     if (e != hipSuccess) return e;

@@ -14,12 +14,15 @@ distributions are:
 * q, k ~ N(0, 1), then scaled to unit L2 norm per head (fp64), then rounded to
   the storage dtype;
 * v ~ N(0, 1);
-* beta = sigmoid(N(0, 1))  (the op takes beta after the sigmoid);
-* g = -exp(A_log) * softplus(N(0, 1)), A_log = log U(lo, hi) per value head
-  (strong decay: lo, hi = 1, 16; weak decay: 0.001, 0.01);
+* per value head a decay rate ssm_a = -U(lo, hi) (strong decay: lo, hi = 1, 16;
+  weak decay: 0.001, 0.01) and a gate bias ssm_dt = U(-1, 1);
+* the op's gate inputs g = ssm_a * E with E ~ Exponential(1) (so g <= 0), and
+  beta ~ U(0, 1);
+* the raw projections a, b ~ N(0, 1) for the in-kernel activation path (the
+  oracle, not this module, turns them into g and beta);
 * initial states ~ N(0, 0.02) (or zero).
 
-Draw order is fixed: A_log, q, k, v, g-noise, beta-noise, initial states,
+Draw order is fixed: ssm_a, q, k, v, E, beta, a, b, ssm_dt, initial states,
 slots.  bf16 storage is round-to-nearest-even of the fp32 value; arrays are
 returned as float32 numpy arrays that hold the exactly rounded values, so the
 oracle (which upcasts to fp64) and the GPU (which converts to bf16 without
@@ -50,14 +53,6 @@ def _unit_rows(x: np.ndarray) -> np.ndarray:
     return x / n
 
 
-def _softplus(x: np.ndarray) -> np.ndarray:
-    return np.logaddexp(0.0, x)
-
-
-def _sigmoid(x: np.ndarray) -> np.ndarray:
-    return 1.0 / (1.0 + np.exp(-x))
-
-
 @dataclasses.dataclass
 class Case:
     """One prefill workload: packed varlen tokens + a pool of state slots."""
@@ -76,7 +71,10 @@ class Case:
     pool: np.ndarray           # [n_slots][H_v][d_k][d_v] float32 initial state pool
     slot_in: np.ndarray        # [N] int32 (-1 = zero initial state)
     slot_out: np.ndarray       # [N] int32
-    A_log: np.ndarray          # [H_v] (recorded for documentation)
+    ssm_a: np.ndarray          # [H_v] float32 decay rate (<= 0)
+    raw_a: np.ndarray          # [T][H_v] float32 raw gate projection
+    raw_b: np.ndarray          # [T][H_v] float32 raw write-strength projection
+    ssm_dt: np.ndarray         # [H_v] float32 gate bias
 
     @property
     def n_seqs(self) -> int:
@@ -93,29 +91,32 @@ class Case:
 
 def _draw(rng, T, H_k, H_v, d_k, d_v, dtype, decay, beta_mode, a_lo, a_hi):
     if decay == "strong":
-        A_log = np.log(rng.uniform(1.0, 16.0, size=H_v))
+        ssm_a = -rng.uniform(1.0, 16.0, size=H_v)
     elif decay == "weak":
-        A_log = np.log(rng.uniform(0.001, 0.01, size=H_v))
+        ssm_a = -rng.uniform(0.001, 0.01, size=H_v)
     elif decay == "custom":
-        A_log = np.log(rng.uniform(a_lo, a_hi, size=H_v))
+        ssm_a = -rng.uniform(a_lo, a_hi, size=H_v)
     elif decay == "zero":
-        A_log = np.full(H_v, -np.inf)
+        ssm_a = np.zeros(H_v)
     else:
         raise ValueError(decay)
     q = _unit_rows(rng.standard_normal((T, H_k, d_k)))
     k = _unit_rows(rng.standard_normal((T, H_k, d_k)))
     v = rng.standard_normal((T, H_v, d_v))
-    gn = rng.standard_normal((T, H_v))
-    bn = rng.standard_normal((T, H_v))
-    g = -np.exp(A_log)[None, :] * _softplus(gn)
+    e = rng.exponential(1.0, size=(T, H_v))
+    bu = rng.uniform(0.0, 1.0, size=(T, H_v))
+    raw_a = rng.standard_normal((T, H_v))
+    raw_b = rng.standard_normal((T, H_v))
+    ssm_dt = rng.uniform(-1.0, 1.0, size=H_v)
+    g = ssm_a[None, :] * e
     if decay == "zero":
-        g = np.zeros_like(gn)
-    if beta_mode == "sigmoid":
-        beta = _sigmoid(bn)
+        g = np.zeros_like(e)
+    if beta_mode == "random":
+        beta = bu
     elif beta_mode == "zero":
-        beta = np.zeros_like(bn)
+        beta = np.zeros_like(bu)
     elif beta_mode == "one":
-        beta = np.ones_like(bn)
+        beta = np.ones_like(bu)
     else:
         raise ValueError(beta_mode)
     q = q.astype(np.float32)
@@ -125,12 +126,13 @@ def _draw(rng, T, H_k, H_v, d_k, d_v, dtype, decay, beta_mode, a_lo, a_hi):
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     elif dtype != "f32":
         raise ValueError(dtype)
-    return A_log, q, k, v, g.astype(np.float32), beta.astype(np.float32)
+    f32 = lambda x: np.ascontiguousarray(x, dtype=np.float32)
+    return (f32(ssm_a), q, k, v, f32(g), f32(beta), f32(raw_a), f32(raw_b), f32(ssm_dt))
 
 
 def make_case(name: str, lengths, H_k: int, H_v: int, d_k: int, d_v: int,
               dtype: str, seed: int, decay: str = "strong",
-              beta_mode: str = "sigmoid", s0_std: float = 0.02,
+              beta_mode: str = "random", s0_std: float = 0.02,
               n_slots: Optional[int] = None, scatter_slots: bool = False,
               a_lo: float = 1.0, a_hi: float = 16.0) -> Case:
     """Generic generator. s0_std == 0 gives zero initial states (slot_in = -1)."""
@@ -138,8 +140,8 @@ def make_case(name: str, lengths, H_k: int, H_v: int, d_k: int, d_v: int,
     N = len(lengths)
     T = int(sum(lengths))
     rng = np.random.default_rng(seed)
-    A_log, q, k, v, g, beta = _draw(rng, T, H_k, H_v, d_k, d_v, dtype, decay,
-                                    beta_mode, a_lo, a_hi)
+    ssm_a, q, k, v, g, beta, raw_a, raw_b, ssm_dt = _draw(
+        rng, T, H_k, H_v, d_k, d_v, dtype, decay, beta_mode, a_lo, a_hi)
     if n_slots is None:
         n_slots = N
     if s0_std > 0:
@@ -153,7 +155,7 @@ def make_case(name: str, lengths, H_k: int, H_v: int, d_k: int, d_v: int,
         slots = np.arange(N, dtype=np.int32)
     slot_in = slots.copy() if s0_std > 0 else np.full(N, -1, np.int32)
     return Case(name, H_k, H_v, d_k, d_v, dtype, lengths, q, k, v, g, beta,
-                pool, slot_in, slots.copy(), A_log)
+                pool, slot_in, slots.copy(), ssm_a, raw_a, raw_b, ssm_dt)
 
 
 # ---------------------------------------------------------------------------
@@ -202,16 +204,20 @@ class DecodeCase:
     beta: np.ndarray   # [steps][N][H_v]
     pool: np.ndarray   # [n_slots][H_v][d_k][d_v]
     slots: np.ndarray  # [N] int32: slot of sequence i (read and written in place)
+    ssm_a: np.ndarray  # [H_v] decay rate (<= 0)
+    raw_a: np.ndarray  # [steps][N][H_v] raw gate projection
+    raw_b: np.ndarray  # [steps][N][H_v] raw write-strength projection
+    ssm_dt: np.ndarray  # [H_v] gate bias
 
 
 def make_decode(name: str, n_seqs: int, n_steps: int, H_k: int, H_v: int,
                 d_k: int, d_v: int, dtype: str, seed: int,
-                decay: str = "strong", beta_mode: str = "sigmoid",
+                decay: str = "strong", beta_mode: str = "random",
                 s0_std: float = 0.02, n_slots: Optional[int] = None,
                 scatter_slots: bool = False) -> DecodeCase:
     rng = np.random.default_rng(seed)
-    A_log, q, k, v, g, beta = _draw(rng, n_steps * n_seqs, H_k, H_v, d_k, d_v,
-                                    dtype, decay, beta_mode, 1.0, 16.0)
+    ssm_a, q, k, v, g, beta, raw_a, raw_b, ssm_dt = _draw(
+        rng, n_steps * n_seqs, H_k, H_v, d_k, d_v, dtype, decay, beta_mode, 1.0, 16.0)
     if n_slots is None:
         n_slots = n_seqs
     pool = (rng.standard_normal((n_slots, H_v, d_k, d_v)) * s0_std).astype(np.float32)
@@ -223,7 +229,8 @@ def make_decode(name: str, n_seqs: int, n_steps: int, H_k: int, H_v: int,
     return DecodeCase(name, H_k, H_v, d_k, d_v, dtype, N, S,
                       q.reshape(S, N, H_k, d_k), k.reshape(S, N, H_k, d_k),
                       v.reshape(S, N, H_v, d_v), g.reshape(S, N, H_v),
-                      beta.reshape(S, N, H_v), pool, slots)
+                      beta.reshape(S, N, H_v), pool, slots, ssm_a,
+                      raw_a.reshape(S, N, H_v), raw_b.reshape(S, N, H_v), ssm_dt)
 
 
 def config2(n_steps: int = 128) -> DecodeCase:

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 1
+#define GDN_VERSION 2
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -87,7 +87,22 @@ typedef enum gdn_dtype {
     GDN_BF16 = 1               /* bfloat16                                  */
 } gdn_dtype;
 
-/* Problem dimensions shared by both entry points. */
+/*
+ * Gate inputs.  GDN_GATES_FINAL: g is the log-decay and beta the write
+ * strength, as the operator consumes them.  GDN_GATES_RAW: the g and beta
+ * arguments carry the layer's raw projections a and b ([T][H_v] fp32) and the
+ * kernels apply the activations of build_layer_attn_linear on the page
+ * "Optimization: Qwen3 next autoregressive pass (#17996)" themselves:
+ *     beta = sigmoid(b),    g = softplus(a + ssm_dt[h]) * ssm_a[h]
+ * (softplus(x) = log(1 + e^x)), so the two small activation passes over
+ * [T][H_v] never run.
+ */
+typedef enum gdn_gate_mode {
+    GDN_GATES_FINAL = 0,
+    GDN_GATES_RAW = 1
+} gdn_gate_mode;
+
+/* Problem dimensions shared by every entry point. */
 typedef struct gdn_dims {
     int32_t H_k;          /* key heads (q and k)                            */
     int32_t H_v;          /* value heads; H_v % H_k == 0                    */
@@ -102,6 +117,12 @@ typedef struct gdn_dims {
                              H_v*d_k*d_v; else >= that and a multiple of 4  */
     float scale;          /* q scale; 0 means 1/sqrt(d_k)                   */
     float eps;            /* L2-norm epsilon, >= 0 (1e-6 for Qwen3-Next)    */
+    int32_t gate_mode;    /* gdn_gate_mode: what the g and beta arguments
+                             hold                                           */
+    const float *ssm_a;   /* [H_v] device, fp32: per-value-head decay rate
+                             (<= 0); read only with GDN_GATES_RAW          */
+    const float *ssm_dt;  /* [H_v] device, fp32: per-value-head gate bias;
+                             read only with GDN_GATES_RAW                   */
 } gdn_dims;
 
 /* Library version (GDN_VERSION). */

@@ -10,6 +10,8 @@ does, and shares no code with it.
   chunked graph, in fp64 (C), for the chunked-vs-sequential pin.
 * ``bruteforce.materialised(...)``: the whole-sequence O(T^2) materialised
   form solved with a library triangular solver (numpy/scipy).
+* ``gates(...)``: the gate activations of the layer (raw projections to the
+  operator's g and beta), in fp64.
 """
 from __future__ import annotations
 
@@ -69,6 +71,35 @@ def _f32(a):
     return np.ascontiguousarray(a, dtype=np.float32)
 
 
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def softplus(x):
+    """log(1 + e^x) in fp64, written as max(x, 0) + log1p(e^-|x|) so that
+    neither branch overflows."""
+    x = np.asarray(x, np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def sigmoid(x):
+    """1 / (1 + e^-x) in fp64, evaluated through e^-|x| (no overflow)."""
+    x = np.asarray(x, np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def gates(a, b, ssm_a, ssm_dt):
+    """The layer's gate activations ("Optimization: Qwen3 next autoregressive
+    pass (#17996)", build_layer_attn_linear): beta = sigmoid(b) and
+    gate = softplus(a + ssm_dt) * ssm_a, with the per-value-head bias ssm_dt
+    and decay rate ssm_a (<= 0) broadcast over tokens.  a, b: [T, H_v];
+    returns (g, beta) [T, H_v] in fp64."""
+    a = np.asarray(a, np.float64)
+    g = softplus(a + np.asarray(ssm_dt, np.float64)[None, :]) * np.asarray(ssm_a, np.float64)[None, :]
+    return g, sigmoid(b)
+
+
 def _ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
 
@@ -84,7 +115,7 @@ def run(q, k, v, g, beta, cu_seqlens, s0=None, *, scale: Optional[float] = None,
     ``heads``, only those value heads are computed (others are zero).
     chunk=0 is the sequential recurrence; chunk>0 the chunked WY form.
     """
-    q, k, v, g, beta = _f32(q), _f32(k), _f32(v), _f32(g), _f32(beta)
+    q, k, v, g, beta = _f32(q), _f32(k), _f32(v), _f64(g), _f64(beta)
     T, H_k, d_k = q.shape
     H_v, d_v = v.shape[1], v.shape[2]
     assert k.shape == q.shape and v.shape[0] == T
@@ -127,12 +158,18 @@ def chunked(*args, chunk: int = 64, **kw):
     return run(*args, **kw)
 
 
-def run_case(case, heads=None, threads=None, chunk: int = 0, lib_path=None):
-    """Oracle on a gdn_inputs.Case: maps slots to per-sequence initial states."""
+def run_case(case, heads=None, threads=None, chunk: int = 0, lib_path=None,
+             raw_gates: bool = False):
+    """Oracle on a gdn_inputs.Case: maps slots to per-sequence initial states.
+    With raw_gates, g and beta come from the case's raw projections through
+    ``gates`` (the in-kernel activation path) instead of the case's g, beta."""
     N = case.n_seqs
     s0 = np.zeros((N, case.H_v, case.d_k, case.d_v), np.float64)
     for i in range(N):
         if case.slot_in[i] >= 0:
             s0[i] = case.pool[case.slot_in[i]]
-    return run(case.q, case.k, case.v, case.g, case.beta, case.cu_seqlens, s0,
+    g, beta = case.g, case.beta
+    if raw_gates:
+        g, beta = gates(case.raw_a, case.raw_b, case.ssm_a, case.ssm_dt)
+    return run(case.q, case.k, case.v, g, beta, case.cu_seqlens, s0,
                heads=heads, threads=threads, chunk=chunk, lib_path=lib_path)

@@ -45,7 +45,8 @@
  * Layouts (all row-major, token-major, the same as the library's):
  *   q, k   [T][H_k][d_k]   float32 values (exact bf16 or fp32 inputs)
  *   v      [T][H_v][d_v]
- *   g,beta [T][H_v]
+ *   g,beta [T][H_v]         fp64 (exact fp32 inputs, or fp64 values from the
+ *                           gate activations of oracle/__init__.py)
  *   s0     [n_seqs][H_v][d_k][d_v] fp64 (NULL = zero state)
  *   out    [T][H_v][d_v]  fp64
  *   s_out  [n_seqs][H_v][d_k][d_v] fp64
@@ -62,7 +63,8 @@ typedef struct {
     int32_t n_seqs;
     const int64_t *cu;
     int32_t H_k, H_v, d_k, d_v;
-    const float *q, *k, *v, *g, *beta;
+    const float *q, *k, *v;
+    const double *g, *beta;
     const double *s0;
     double scale, eps;
     const int32_t *heads;
@@ -94,8 +96,8 @@ static void run_sequential(const job_t *J, int s, int h, double *S,
     for (int64_t t = J->cu[s]; t < J->cu[s + 1]; ++t) {
         l2_normalise(J->q + (t * J->H_k + hk) * dk, dk, J->eps, J->scale, qh);
         l2_normalise(J->k + (t * J->H_k + hk) * dk, dk, J->eps, 1.0, kh);
-        const double a = exp((double)J->g[t * J->H_v + h]);
-        const double b = (double)J->beta[t * J->H_v + h];
+        const double a = exp(J->g[t * J->H_v + h]);
+        const double b = J->beta[t * J->H_v + h];
         const float *vt = J->v + (t * J->H_v + h) * dv;
         /* decay first */
         for (int i = 0; i < dk * dv; ++i) S[i] *= a;
@@ -154,7 +156,7 @@ static void run_chunked(const job_t *J, int s, int h, double *S, double *wk)
             l2_normalise(J->k + (t * J->H_k + hk) * dk, dk, J->eps, 1.0, K + a * dk);
             for (int j = 0; j < dv; ++j) V[a * dv + j] = J->v[(t * J->H_v + h) * dv + j];
             B[a] = J->beta[t * J->H_v + h];
-            G[a] = (a ? G[a - 1] : 0.0) + (double)J->g[t * J->H_v + h];
+            G[a] = (a ? G[a - 1] : 0.0) + J->g[t * J->H_v + h];
         }
         for (int a = 0; a < n; ++a)
             for (int c = 0; c < n; ++c)
@@ -293,7 +295,7 @@ static int run(job_t *J)
 int gdn_oracle_run(int32_t n_seqs, const int64_t *cu_seqlens,
                    int32_t H_k, int32_t H_v, int32_t d_k, int32_t d_v,
                    const float *q, const float *k, const float *v,
-                   const float *g, const float *beta, const double *s0,
+                   const double *g, const double *beta, const double *s0,
                    double scale, double eps,
                    const int32_t *heads, int32_t n_heads,
                    double *out, double *s_out,

@@ -11,6 +11,7 @@ error <= 2^-9), so each output element is held to
 """
 from __future__ import annotations
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -37,10 +38,20 @@ def dev_case(case, device="cuda"):
     return dict(
         q=f(case.q, dt), k=f(case.k, dt), v=f(case.v, dt), g=f(case.g), beta=f(case.beta),
         pool=f(case.pool), cu=f(case.cu_seqlens, torch.int32),
-        slot_in=f(case.slot_in, torch.int32), slot_out=f(case.slot_out, torch.int32))
+        slot_in=f(case.slot_in, torch.int32), slot_out=f(case.slot_out, torch.int32),
+        raw_a=f(case.raw_a), raw_b=f(case.raw_b), ssm_a=f(case.ssm_a), ssm_dt=f(case.ssm_dt))
 
 
-def gpu_prefill(case, d=None, inplace=True, chunks=None, out_dtype=torch.float32):
+def _gate_args(d, raw_gates):
+    """(g, beta, gates) for the binding: the final gates, or the raw
+    projections plus (ssm_a, ssm_dt) for the in-kernel activations."""
+    if raw_gates:
+        return d["raw_a"], d["raw_b"], (d["ssm_a"], d["ssm_dt"])
+    return d["g"], d["beta"], None
+
+
+def gpu_prefill(case, d=None, inplace=True, chunks=None, out_dtype=torch.float32,
+                raw_gates=False):
     """Run a Case through gdn.prefill.  `chunks`: split a single-sequence case
     into consecutive calls of that many tokens (state carried in place)."""
     import gated_deltanet_rule_amd as gdn
@@ -51,35 +62,37 @@ def gpu_prefill(case, d=None, inplace=True, chunks=None, out_dtype=torch.float32
     if not inplace:
         # slots that are not written must keep whatever the output pool held
         pool_out.copy_(d["pool"])
+    g, beta, gates = _gate_args(d, raw_gates)
     if chunks is None:
-        gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], pool_out, out,
-                    d["cu"], d["slot_in"], d["slot_out"])
+        gdn.prefill(d["q"], d["k"], d["v"], g, beta, d["pool"], pool_out, out,
+                    d["cu"], d["slot_in"], d["slot_out"], gates=gates)
     else:
         assert case.n_seqs == 1 and inplace
         for s in range(0, T, chunks):
             e = min(T, s + chunks)
             cu = torch.tensor([0, e - s], dtype=torch.int32, device=d["q"].device)
             sl_in = d["slot_in"] if s == 0 else d["slot_out"]
-            gdn.prefill(d["q"][s:e], d["k"][s:e], d["v"][s:e], d["g"][s:e], d["beta"][s:e],
-                        d["pool"], d["pool"], out[s:e], cu, sl_in, d["slot_out"])
+            gdn.prefill(d["q"][s:e], d["k"][s:e], d["v"][s:e], g[s:e], beta[s:e],
+                        d["pool"], d["pool"], out[s:e], cu, sl_in, d["slot_out"], gates=gates)
     torch.cuda.synchronize()
     return out, pool_out
 
 
-def gpu_decode_multi(case, d=None, inplace=True, out_dtype=torch.float32):
+def gpu_decode_multi(case, d=None, inplace=True, out_dtype=torch.float32, raw_gates=False):
     """Run a Case (tokens packed by cu_seqlens) through gdn.decode_multi."""
     import gated_deltanet_rule_amd as gdn
     d = d or dev_case(case)
     out = torch.empty(d["v"].shape, dtype=out_dtype, device=d["v"].device)
     pool_out = d["pool"] if inplace else d["pool"].clone()
-    gdn.decode_multi(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], pool_out, out,
-                     d["cu"], d["slot_in"], d["slot_out"])
+    g, beta, gates = _gate_args(d, raw_gates)
+    gdn.decode_multi(d["q"], d["k"], d["v"], g, beta, d["pool"], pool_out, out,
+                     d["cu"], d["slot_in"], d["slot_out"], gates=gates)
     torch.cuda.synchronize()
     return out, pool_out
 
 
-def oracle_case(case, heads=None):
-    return oracle.run_case(case, heads=heads)
+def oracle_case(case, heads=None, raw_gates=False):
+    return oracle.run_case(case, heads=heads, raw_gates=raw_gates)
 
 
 def rel_err(gpu, ref, bf16_out=False):
@@ -112,26 +125,33 @@ def compare_prefill(case, out, pool_out, ref_out, ref_state, heads=None, tol=Non
     return eo, es
 
 
-def run_decode(dc, device="cuda", inplace=True, out_dtype=torch.float32):
+def run_decode(dc, device="cuda", inplace=True, out_dtype=torch.float32, raw_gates=False):
     """Run a DecodeCase step by step; returns (outs [steps, N, H_v, d_v], pool)."""
     import gated_deltanet_rule_amd as gdn
     dt = tdt(dc.dtype)
     f = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(device).to(t)
     q, k, v = f(dc.q, dt), f(dc.k, dt), f(dc.v, dt)
-    g, b = f(dc.g), f(dc.beta)
+    g, b = (f(dc.raw_a), f(dc.raw_b)) if raw_gates else (f(dc.g), f(dc.beta))
+    gates = (f(dc.ssm_a), f(dc.ssm_dt)) if raw_gates else None
     pool = f(dc.pool)
     slots = f(dc.slots, torch.int32)
     outs = torch.empty(v.shape, dtype=out_dtype, device=device)
     pool_b = pool if inplace else pool.clone()
     for s in range(dc.n_steps):
         src, dst = (pool, pool) if inplace else ((pool, pool_b) if s % 2 == 0 else (pool_b, pool))
-        gdn.decode_step(q[s], k[s], v[s], g[s], b[s], src, dst, outs[s], slots, slots)
+        gdn.decode_step(q[s], k[s], v[s], g[s], b[s], src, dst, outs[s], slots, slots,
+                        gates=gates)
     torch.cuda.synchronize()
     final = pool if (inplace or dc.n_steps % 2 == 0) else pool_b
     return outs, final
 
 
-def oracle_decode(dc, heads=None):
+def oracle_decode(dc, heads=None, raw_gates=False):
+    if raw_gates:
+        g, b = oracle.gates(dc.raw_a.reshape(-1, dc.H_v), dc.raw_b.reshape(-1, dc.H_v),
+                            dc.ssm_a, dc.ssm_dt)
+        shape = (dc.n_steps, dc.n_seqs, dc.H_v)
+        dc = dataclasses.replace(dc, g=g.reshape(shape), beta=b.reshape(shape))
     q, k, v, g, b, cu = gi.decode_as_sequences(dc)
     s0 = np.stack([dc.pool[dc.slots[i]] for i in range(dc.n_seqs)]).astype(np.float64)
     out, sf = oracle.run(q, k, v, g, b, cu, s0, heads=heads)

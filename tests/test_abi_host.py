@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert gdn.version() == 1
+    assert gdn.version() == 2
     for st in range(5):
         assert gdn.lib.gdn_status_string(st)
     assert gdn.lib.gdn_status_string(99) == b"unknown status"
@@ -63,12 +63,27 @@ def test_workspace_size_grows_with_tokens_and_is_aligned():
     (dict(d_k=96), 2), (dict(d_v=256), 2), (dict(dtype=7), 2), (dict(out_dtype=3), 2),
     (dict(slot_stride=100), 1), (dict(slot_stride=32 * 128 * 128 + 2), 1),
     (dict(eps=-1.0), 1), (dict(scale=float("nan")), 1),
+    (dict(gate_mode=2), 1), (dict(gate_mode=-1), 1),
+    (dict(gate_mode=gdn.GDN_GATES_RAW), 1),                       # no ssm_a / ssm_dt
+    (dict(gate_mode=gdn.GDN_GATES_RAW, ssm_a=0x1000), 1),         # ssm_dt missing
+    (dict(gate_mode=gdn.GDN_GATES_RAW, ssm_a=0x1002, ssm_dt=0x2000), 1),  # misaligned
 ])
 def test_bad_dims_rejected(kw, status):
     n = ctypes.c_size_t(0)
     st = gdn.lib.gdn_prefill_workspace_size(ctypes.byref(_dims(**kw)), 1, 64, ctypes.byref(n))
     assert st == status
     assert gdn.lib.gdn_last_error()
+
+
+def test_raw_gates_accepted_by_sizing():
+    # With both pointers present and aligned the dims are valid; the sizing
+    # call never dereferences them.
+    n = ctypes.c_size_t(0)
+    d = _dims(gate_mode=gdn.GDN_GATES_RAW, ssm_a=0x1000, ssm_dt=0x2000)
+    assert gdn.lib.gdn_prefill_workspace_size(ctypes.byref(d), 1, 64, ctypes.byref(n)) == 0
+    m = ctypes.c_size_t(0)
+    assert gdn.lib.gdn_prefill_workspace_size(ctypes.byref(_dims()), 1, 64, ctypes.byref(m)) == 0
+    assert n.value == m.value
 
 
 def test_null_dims_and_counts():

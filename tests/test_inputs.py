@@ -42,8 +42,12 @@ def test_recipe_shapes_and_ranges():
     # bf16 storage: low 16 bits are zero
     assert not (b.q.view(np.uint32) & 0xFFFF).any()
     assert not (b.v.view(np.uint32) & 0xFFFF).any()
-    # strong decay: A_log = log U(1, 16)
-    assert np.all(np.exp(b.A_log) >= 1) and np.all(np.exp(b.A_log) <= 16)
+    # strong decay: ssm_a = -U(1, 16); gate bias U(-1, 1); raw projections per token-head
+    assert np.all(b.ssm_a <= -1) and np.all(b.ssm_a >= -16)
+    assert np.all(np.abs(b.ssm_dt) <= 1)
+    assert b.raw_a.shape == (70, 4) and b.raw_b.shape == (70, 4)
+    w = gi.make_case("w", [70], 2, 4, 32, 32, "bf16", seed=3, decay="weak")
+    assert np.all(w.ssm_a <= -0.001) and np.all(w.ssm_a >= -0.01)
 
 
 def test_decode_repacking():

@@ -16,11 +16,11 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "gdn_oracle.c")
 # (id, exact text in the oracle, replacement, pins to run: "seq" or "chunk")
 MUTATIONS = [
     ("drop_decay", "for (int i = 0; i < dk * dv; ++i) S[i] *= a;", ";", "seq"),
-    ("no_exp_on_g", "const double a = exp((double)J->g[t * J->H_v + h]);",
-     "const double a = (double)J->g[t * J->H_v + h] + 1.0;", "seq"),
+    ("no_exp_on_g", "const double a = exp(J->g[t * J->H_v + h]);",
+     "const double a = J->g[t * J->H_v + h] + 1.0;", "seq"),
     ("delta_sign", "kv[j] = b * ((double)vt[j] - kv[j]);",
      "kv[j] = b * ((double)vt[j] + kv[j]);", "seq"),
-    ("drop_beta", "const double b = (double)J->beta[t * J->H_v + h];",
+    ("drop_beta", "const double b = J->beta[t * J->H_v + h];",
      "const double b = 1.0;", "seq"),
     ("transposed_state_read", "kv[j] += S[i * dv + j] * kh[i];",
      "kv[j] += S[j * dv + i] * kh[i];", "seq"),
