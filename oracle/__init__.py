@@ -67,10 +67,6 @@ def default_threads() -> int:
         return os.cpu_count() or 1
 
 
-def _f32(a):
-    return np.ascontiguousarray(a, dtype=np.float32)
-
-
 def _f64(a):
     return np.ascontiguousarray(a, dtype=np.float64)
 
@@ -115,7 +111,7 @@ def run(q, k, v, g, beta, cu_seqlens, s0=None, *, scale: Optional[float] = None,
     ``heads``, only those value heads are computed (others are zero).
     chunk=0 is the sequential recurrence; chunk>0 the chunked WY form.
     """
-    q, k, v, g, beta = _f32(q), _f32(k), _f32(v), _f64(g), _f64(beta)
+    q, k, v, g, beta = _f64(q), _f64(k), _f64(v), _f64(g), _f64(beta)
     T, H_k, d_k = q.shape
     H_v, d_v = v.shape[1], v.shape[2]
     assert k.shape == q.shape and v.shape[0] == T

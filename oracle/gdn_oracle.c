@@ -43,8 +43,9 @@
  * mistakes planted and check that some pin fails.
  *
  * Layouts (all row-major, token-major, the same as the library's):
- *   q, k   [T][H_k][d_k]   float32 values (exact bf16 or fp32 inputs)
- *   v      [T][H_v][d_v]
+ *   q, k   [T][H_k][d_k]   fp64 (exact bf16 or fp32 inputs, or fp64 values
+ *                           from the convolution prologue of oracle/layer.py)
+ *   v      [T][H_v][d_v]   fp64, likewise
  *   g,beta [T][H_v]         fp64 (exact fp32 inputs, or fp64 values from the
  *                           gate activations of oracle/__init__.py)
  *   s0     [n_seqs][H_v][d_k][d_v] fp64 (NULL = zero state)
@@ -63,7 +64,7 @@ typedef struct {
     int32_t n_seqs;
     const int64_t *cu;
     int32_t H_k, H_v, d_k, d_v;
-    const float *q, *k, *v;
+    const double *q, *k, *v;
     const double *g, *beta;
     const double *s0;
     double scale, eps;
@@ -78,12 +79,12 @@ typedef struct {
 } job_t;
 
 /* [NORM] x_hat = x / sqrt(sum(x^2) + eps), times an extra factor */
-static void l2_normalise(const float *x, int n, double eps, double factor, double *y)
+static void l2_normalise(const double *x, int n, double eps, double factor, double *y)
 {
     double ss = 0.0;
-    for (int i = 0; i < n; ++i) ss += (double)x[i] * (double)x[i];
+    for (int i = 0; i < n; ++i) ss += x[i] * x[i];
     double inv = factor / sqrt(ss + eps);
-    for (int i = 0; i < n; ++i) y[i] = (double)x[i] * inv;
+    for (int i = 0; i < n; ++i) y[i] = x[i] * inv;
 }
 
 /* One (sequence, value head) chain, token by token: [AR]. */
@@ -98,7 +99,7 @@ static void run_sequential(const job_t *J, int s, int h, double *S,
         l2_normalise(J->k + (t * J->H_k + hk) * dk, dk, J->eps, 1.0, kh);
         const double a = exp(J->g[t * J->H_v + h]);
         const double b = J->beta[t * J->H_v + h];
-        const float *vt = J->v + (t * J->H_v + h) * dv;
+        const double *vt = J->v + (t * J->H_v + h) * dv;
         /* decay first */
         for (int i = 0; i < dk * dv; ++i) S[i] *= a;
         /* kv_mem[j] = sum_i S[i][j] k[i]  (from the decayed state) */
@@ -294,7 +295,7 @@ static int run(job_t *J)
 
 int gdn_oracle_run(int32_t n_seqs, const int64_t *cu_seqlens,
                    int32_t H_k, int32_t H_v, int32_t d_k, int32_t d_v,
-                   const float *q, const float *k, const float *v,
+                   const double *q, const double *k, const double *v,
                    const double *g, const double *beta, const double *s0,
                    double scale, double eps,
                    const int32_t *heads, int32_t n_heads,

@@ -30,8 +30,8 @@ MUTATIONS = [
      "l2_normalise(J->q + (t * J->H_k + hk) * dk, dk, J->eps, 1.0, qh);", "seq"),
     ("tiled_gqa", "const int hk = h / r;                                   /* [GQA] */",
      "const int hk = h % J->H_k;", "seq"),
-    ("v_indexed_by_key_head", "const float *vt = J->v + (t * J->H_v + h) * dv;",
-     "const float *vt = J->v + (t * J->H_v + h / r) * dv;", "seq"),
+    ("v_indexed_by_key_head", "const double *vt = J->v + (t * J->H_v + h) * dv;",
+     "const double *vt = J->v + (t * J->H_v + h / r) * dv;", "seq"),
     ("no_k_norm", "l2_normalise(J->k + (t * J->H_k + hk) * dk, dk, J->eps, 1.0, kh);",
      "for (int i = 0; i < dk; ++i) kh[i] = J->k[(t * J->H_k + hk) * dk + i];", "seq"),
     # chunked form
