@@ -248,3 +248,44 @@ def decode_as_sequences(dc: DecodeCase):
     perm = lambda a: np.ascontiguousarray(np.swapaxes(a, 0, 1)).reshape((-1,) + a.shape[2:])
     cu = (np.arange(dc.n_seqs + 1) * dc.n_steps).astype(np.int32)
     return perm(dc.q), perm(dc.k), perm(dc.v), perm(dc.g), perm(dc.beta), cu
+
+
+# ---------------------------------------------------------------------------
+# Layer inputs for the fused prologue / epilogue ("ik_llama.cpp
+# src/llama-delta-net.cpp", build_layer_attn_linear_core): the mixed q|k|v
+# projection rows that the short causal convolution reads, its taps and
+# per-slot convolution states, and the gate z and weight of the gated RMSNorm.
+# ---------------------------------------------------------------------------
+
+D_CONV = 4      # taps of the short convolution
+
+
+@dataclasses.dataclass
+class LayerInputs:
+    qkv: np.ndarray        # [T][conv_dim] float32 (exact in dtype): q channels, k channels, v channels
+    conv_w: np.ndarray     # [conv_dim][D_CONV] float32, oldest tap first
+    conv_pool: np.ndarray  # [n_slots][conv_dim][D_CONV-1] float32 (exact in dtype), oldest first
+    z: np.ndarray          # [T][H_v][d_v] float32 (exact in dtype)
+    norm_w: np.ndarray     # [d_v] float32
+
+
+def conv_dim(H_k: int, H_v: int, d_k: int, d_v: int) -> int:
+    return 2 * H_k * d_k + H_v * d_v
+
+
+def make_layer_inputs(T: int, n_slots: int, H_k: int, H_v: int, d_k: int, d_v: int,
+                      dtype: str, seed: int, w_std: float = 0.5) -> LayerInputs:
+    """Draws, from a stream of their own (so a workload's other inputs are
+    unchanged): qkv rows ~ N(0, 1); taps ~ N(0, w_std^2) (w_std = 0.5 keeps the
+    convolution's output near unit variance); convolution states ~ N(0, 1)
+    (they hold earlier rows); z ~ N(0, 1); norm weight 1 + 0.1 N(0, 1)."""
+    rng = np.random.default_rng([seed, 7])
+    C = conv_dim(H_k, H_v, d_k, d_v)
+    qkv = rng.standard_normal((T, C)).astype(np.float32)
+    conv_w = (rng.standard_normal((C, D_CONV)) * w_std).astype(np.float32)
+    conv_pool = rng.standard_normal((n_slots, C, D_CONV - 1)).astype(np.float32)
+    z = rng.standard_normal((T, H_v, d_v)).astype(np.float32)
+    norm_w = (1.0 + 0.1 * rng.standard_normal(d_v)).astype(np.float32)
+    if dtype == "bf16":
+        qkv, conv_pool, z = round_to_bf16(qkv), round_to_bf16(conv_pool), round_to_bf16(z)
+    return LayerInputs(qkv, conv_w, conv_pool, z, norm_w)

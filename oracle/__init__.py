@@ -12,6 +12,9 @@ does, and shares no code with it.
   form solved with a library triangular solver (numpy/scipy).
 * ``gates(...)``: the gate activations of the layer (raw projections to the
   operator's g and beta), in fp64.
+* ``layer``: the steps of the layer right before and after the operator (the
+  short causal convolution + SiLU prologue with its per-slot state, the gated
+  RMSNorm epilogue) and ``layer.run_layer`` chaining them around ``run``.
 """
 from __future__ import annotations
 

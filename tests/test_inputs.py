@@ -55,3 +55,24 @@ def test_decode_repacking():
     q, k, v, g, beta, cu = gi.decode_as_sequences(dc)
     assert list(cu) == [0, 5, 10, 15]
     assert np.array_equal(q[5 + 2], dc.q[2, 1]) and np.array_equal(v[10 + 4], dc.v[4, 2])
+
+
+def test_layer_inputs_recipe():
+    a = gi.make_layer_inputs(33, 5, 2, 4, 32, 64, "bf16", seed=9)
+    b = gi.make_layer_inputs(33, 5, 2, 4, 32, 64, "bf16", seed=9)
+    C = gi.conv_dim(2, 4, 32, 64)
+    assert C == 2 * 2 * 32 + 4 * 64
+    assert a.qkv.shape == (33, C) and a.conv_w.shape == (C, gi.D_CONV)
+    assert a.conv_pool.shape == (5, C, gi.D_CONV - 1) and a.z.shape == (33, 4, 64)
+    assert a.norm_w.shape == (64,)
+    for f in ("qkv", "conv_w", "conv_pool", "z", "norm_w"):
+        assert np.array_equal(getattr(a, f), getattr(b, f)), f
+    # bf16 storage: values survive a bf16 round trip unchanged
+    for f in ("qkv", "conv_pool", "z"):
+        x = getattr(a, f)
+        assert np.array_equal(gi.round_to_bf16(x), x), f
+    # a stream of its own: the operator inputs of the same seed are unchanged
+    c1 = gi.make_case("x", [33], 2, 4, 32, 64, "bf16", seed=9)
+    c2 = gi.make_case("x", [33], 2, 4, 32, 64, "bf16", seed=9)
+    assert np.array_equal(c1.q, c2.q)
+    assert abs(float(np.std(a.qkv)) - 1.0) < 0.05
