@@ -29,6 +29,7 @@ GDN_F32 = 0
 GDN_BF16 = 1
 GDN_GATES_FINAL = 0
 GDN_GATES_RAW = 1
+D_CONV = 4          # taps of the fused convolution prologue
 
 
 class GdnError(RuntimeError):
@@ -43,7 +44,9 @@ class Dims(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("slot_stride", ctypes.c_int64), ("scale", ctypes.c_float),
                 ("eps", ctypes.c_float), ("gate_mode", ctypes.c_int32),
-                ("ssm_a", ctypes.c_void_p), ("ssm_dt", ctypes.c_void_p)]
+                ("ssm_a", ctypes.c_void_p), ("ssm_dt", ctypes.c_void_p),
+                ("d_conv", ctypes.c_int32), ("conv_w", ctypes.c_void_p),
+                ("z", ctypes.c_void_p), ("norm_w", ctypes.c_void_p)]
 
 
 def _load() -> ctypes.CDLL:
@@ -96,14 +99,38 @@ def _code(dtype: torch.dtype, what: str) -> int:
     raise TypeError(f"{what} dtype must be float32 or bfloat16, got {dtype}")
 
 
+def conv_state_size(H_k: int, H_v: int, d_k: int, d_v: int) -> int:
+    """fp32 values of convolution state at the start of each slot row."""
+    return (D_CONV - 1) * (2 * H_k * d_k + H_v * d_v)
+
+
 def make_dims(H_k: int, H_v: int, d_k: int, d_v: int, dtype: torch.dtype,
               out_dtype: torch.dtype = torch.float32, scale: float = 0.0,
-              eps: float = 1e-6, slot_stride: int = 0, gates=None) -> Dims:
+              eps: float = 1e-6, slot_stride: int = 0, gates=None, conv_w=None,
+              z=None, norm_w=None) -> Dims:
     """gates: None (g and beta given as the operator takes them) or a pair
     (ssm_a, ssm_dt) of fp32 [H_v] device tensors, with g and beta then holding
-    the raw projections a and b (the kernels apply the activations)."""
+    the raw projections a and b (the kernels apply the activations).
+    conv_w: [conv_dim, 4] fp32 taps of the fused convolution prologue (q then
+    carries the mixed q|k|v rows, k and v are None, state rows start with the
+    convolution state).  z, norm_w: the gated RMSNorm epilogue."""
     d = Dims(H_k, H_v, d_k, d_v, _code(dtype, "q/k/v"), _code(out_dtype, "out"),
-             slot_stride, scale, eps, GDN_GATES_FINAL, None, None)
+             slot_stride, scale, eps, GDN_GATES_FINAL, None, None, 0, None, None, None)
+    if conv_w is not None:
+        _need(conv_w, "conv_w", torch.float32)
+        if tuple(conv_w.shape) != (2 * H_k * d_k + H_v * d_v, D_CONV):
+            raise ValueError(f"conv_w must be [{2 * H_k * d_k + H_v * d_v}, {D_CONV}]")
+        d.d_conv = D_CONV
+        d.conv_w = conv_w.data_ptr()
+    if z is not None:
+        _need(z, "z", dtype)
+        if norm_w is None:
+            raise ValueError("the epilogue needs norm_w")
+        _need(norm_w, "norm_w", torch.float32)
+        if norm_w.numel() != d_v or z.shape[-1] != d_v:
+            raise ValueError("z and norm_w must end in d_v")
+        d.z = z.data_ptr()
+        d.norm_w = norm_w.data_ptr()
     if gates is not None:
         ssm_a, ssm_dt = gates
         for t, name in ((ssm_a, "ssm_a"), (ssm_dt, "ssm_dt")):
@@ -116,14 +143,36 @@ def make_dims(H_k: int, H_v: int, d_k: int, d_v: int, dtype: torch.dtype,
     return d
 
 
-def _dims_from(q, v, out, scale, eps, state, gates=None) -> Dims:
+def _dims_from(q, v, out, scale, eps, state, gates=None, conv=None, z=None, norm_w=None) -> Dims:
+    """conv: None, or (conv_w, H_k, d_k) with q the mixed rows [T, conv_dim]
+    and v None; the state pools are then [n_slots, row] (convolution state,
+    then recurrent state)."""
+    stride = 0
+    if state is not None and state.dim() in (2, 4):
+        stride = state.stride(0)
+    if conv is not None:
+        conv_w, H_k, d_k = conv
+        if v is not None:
+            raise ValueError("with the convolution prologue q carries q|k|v: pass k = v = None")
+        if q.dim() != 2 or out.dim() != 3:
+            raise ValueError("q must be [T, conv_dim], out [T, H_v, d_v]")
+        return make_dims(H_k, out.shape[1], d_k, out.shape[2], q.dtype, out.dtype, scale, eps,
+                         stride, gates, conv_w, z, norm_w)
     if q.dim() != 3 or v.dim() != 3 or out.shape != v.shape:
         raise ValueError("q must be [T, H_k, d_k], v and out [T, H_v, d_v]")
-    stride = 0
-    if state is not None:
-        stride = state.stride(0) if state.dim() == 4 else 0
     return make_dims(q.shape[1], v.shape[1], q.shape[2], v.shape[2], q.dtype, out.dtype,
-                     scale, eps, stride, gates)
+                     scale, eps, stride, gates, None, z, norm_w)
+
+
+def _need_qkv(q, k, v, conv):
+    dev = q.device
+    if conv is None:
+        for t, name in ((q, "q"), (k, "k"), (v, "v")):
+            _need(t, name, q.dtype, dev)
+    else:
+        _need(q, "q (mixed rows)", None, dev)
+        if k is not None or v is not None:
+            raise ValueError("with the convolution prologue k and v must be None")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -156,12 +205,13 @@ def workspace_size(dims: Dims, n_seqs: int, total_tokens: int) -> int:
 
 def prefill(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in, slot_out,
             workspace: Optional[torch.Tensor] = None, *, scale: float = 0.0,
-            eps: float = 1e-6, stream=None, gates=None) -> None:
+            eps: float = 1e-6, stream=None, gates=None, conv=None, z=None, norm_w=None) -> None:
     """gdn_chunked_prefill on torch tensors (asynchronous on `stream`).
-    gates=(ssm_a, ssm_dt): g and beta are the raw projections a, b."""
+    gates=(ssm_a, ssm_dt): g and beta are the raw projections a, b.
+    conv=(conv_w, H_k, d_k): q holds the mixed rows (k = v = None).
+    z, norm_w: gated RMSNorm epilogue."""
     dev = q.device
-    for t, name in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, name, q.dtype, dev)
+    _need_qkv(q, k, v, conv)
     _need(out, "out", None, dev)
     for t, name in ((g, "g"), (beta, "beta"), (state_out, "state_out")):
         _need(t, name, torch.float32, dev)
@@ -169,7 +219,7 @@ def prefill(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in, slo
         _need(state_in, "state_in", torch.float32, dev)
     for t, name in ((cu_seqlens, "cu_seqlens"), (slot_in, "slot_in"), (slot_out, "slot_out")):
         _need(t, name, torch.int32, dev)
-    dims = _dims_from(q, v, out, scale, eps, state_out, gates)
+    dims = _dims_from(q, v, out, scale, eps, state_out, gates, conv, z, norm_w)
     n_seqs = slot_out.shape[0]
     T = q.shape[0]
     need = workspace_size(dims, n_seqs, T)
@@ -203,8 +253,9 @@ class PrefillPlan:
     ``prepare(...)`` then ``scan(...)`` (ordered on the caller's streams)."""
 
     def __init__(self, q, v, out, n_seqs: int, *, state=None, scale: float = 0.0,
-                 eps: float = 1e-6, workspace: Optional[torch.Tensor] = None, gates=None):
-        self.dims = _dims_from(q, v, out, scale, eps, state, gates)
+                 eps: float = 1e-6, workspace: Optional[torch.Tensor] = None, gates=None,
+                 z=None, norm_w=None):
+        self.dims = _dims_from(q, v, out, scale, eps, state, gates, None, z, norm_w)
         self.n_seqs = n_seqs
         self.T = q.shape[0]
         need = workspace_size(self.dims, n_seqs, self.T)
@@ -236,11 +287,11 @@ class PrefillPlan:
 
 
 def decode_step(q, k, v, g, beta, state_in, state_out, out, slot_in, slot_out, *,
-                scale: float = 0.0, eps: float = 1e-6, stream=None, gates=None) -> None:
+                scale: float = 0.0, eps: float = 1e-6, stream=None, gates=None, conv=None,
+                z=None, norm_w=None) -> None:
     """gdn_recurrent_step on torch tensors: one token per sequence."""
     dev = q.device
-    for t, name in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, name, q.dtype, dev)
+    _need_qkv(q, k, v, conv)
     _need(out, "out", None, dev)
     for t, name in ((g, "g"), (beta, "beta"), (state_out, "state_out")):
         _need(t, name, torch.float32, dev)
@@ -248,7 +299,7 @@ def decode_step(q, k, v, g, beta, state_in, state_out, out, slot_in, slot_out, *
         _need(state_in, "state_in", torch.float32, dev)
     for t, name in ((slot_in, "slot_in"), (slot_out, "slot_out")):
         _need(t, name, torch.int32, dev)
-    dims = _dims_from(q, v, out, scale, eps, state_out, gates)
+    dims = _dims_from(q, v, out, scale, eps, state_out, gates, conv, z, norm_w)
     _check(lib.gdn_recurrent_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                   _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
                                   _ptr(slot_in), _ptr(slot_out), slot_out.shape[0],
@@ -256,12 +307,12 @@ def decode_step(q, k, v, g, beta, state_in, state_out, out, slot_in, slot_out, *
 
 
 def decode_multi(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in, slot_out, *,
-                 scale: float = 0.0, eps: float = 1e-6, stream=None, gates=None) -> None:
+                 scale: float = 0.0, eps: float = 1e-6, stream=None, gates=None, conv=None,
+                 z=None, norm_w=None) -> None:
     """gdn_recurrent_multi on torch tensors: a few tokens per sequence, packed
     by cu_seqlens as for prefill, recurrent form, no workspace."""
     dev = q.device
-    for t, name in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, name, q.dtype, dev)
+    _need_qkv(q, k, v, conv)
     _need(out, "out", None, dev)
     for t, name in ((g, "g"), (beta, "beta"), (state_out, "state_out")):
         _need(t, name, torch.float32, dev)
@@ -269,7 +320,7 @@ def decode_multi(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in
         _need(state_in, "state_in", torch.float32, dev)
     for t, name in ((cu_seqlens, "cu_seqlens"), (slot_in, "slot_in"), (slot_out, "slot_out")):
         _need(t, name, torch.int32, dev)
-    dims = _dims_from(q, v, out, scale, eps, state_out, gates)
+    dims = _dims_from(q, v, out, scale, eps, state_out, gates, conv, z, norm_w)
     _check(lib.gdn_recurrent_multi(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                    _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
                                    _ptr(cu_seqlens), _ptr(slot_in), _ptr(slot_out),

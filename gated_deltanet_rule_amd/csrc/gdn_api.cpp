@@ -39,7 +39,12 @@ gdn_status resolve(const gdn_dims *d, gdn::Problem *p)
         return fail(GDN_ERR_UNSUPPORTED, "unknown dtype %d", d->dtype);
     if (d->out_dtype != GDN_F32 && d->out_dtype != GDN_BF16)
         return fail(GDN_ERR_UNSUPPORTED, "unknown out_dtype %d", d->out_dtype);
-    const int64_t slot = (int64_t)d->H_v * d->d_k * d->d_v;
+    if (d->d_conv != 0 && d->d_conv != gdn::kConv)
+        return fail(GDN_ERR_UNSUPPORTED, "d_conv must be 0 or %d (got %d)", gdn::kConv, d->d_conv);
+    const int64_t conv_dim = 2 * (int64_t)d->H_k * d->d_k + (int64_t)d->H_v * d->d_v;
+    if (conv_dim > INT32_MAX / gdn::kConv) return fail(GDN_ERR_UNSUPPORTED, "too many channels");
+    const int64_t conv_state = d->d_conv ? (gdn::kConv - 1) * conv_dim : 0;
+    const int64_t slot = conv_state + (int64_t)d->H_v * d->d_k * d->d_v;
     int64_t stride = d->slot_stride == 0 ? slot : d->slot_stride;
     if (stride < slot || stride % 4 != 0)
         return fail(GDN_ERR_INVALID_ARG, "slot_stride %lld must be 0 or a multiple of 4 >= %lld",
@@ -66,6 +71,48 @@ gdn_status resolve(const gdn_dims *d, gdn::Problem *p)
         p->ssm_a = d->ssm_a;
         p->ssm_dt = d->ssm_dt;
     }
+    p->conv_dim = (int)conv_dim;
+    p->conv_state = conv_state;
+    p->conv_w = nullptr;
+    if (d->d_conv) {
+        if (!d->conv_w) return fail(GDN_ERR_INVALID_ARG, "d_conv = %d needs conv_w", d->d_conv);
+        if (!aligned(d->conv_w, 16)) return fail(GDN_ERR_INVALID_ARG, "conv_w is not 16-byte aligned");
+        p->conv_w = d->conv_w;
+    }
+    p->rs_qk = d->d_conv ? conv_dim : (int64_t)d->H_k * d->d_k;
+    p->rs_v = d->d_conv ? conv_dim : (int64_t)d->H_v * d->d_v;
+    p->z = d->z;
+    p->norm_w = nullptr;
+    if (d->z) {
+        if (!aligned(d->z, 16)) return fail(GDN_ERR_INVALID_ARG, "z is not 16-byte aligned");
+        if (!d->norm_w) return fail(GDN_ERR_INVALID_ARG, "the epilogue (z) needs norm_w");
+        if (!aligned(d->norm_w, 16)) return fail(GDN_ERR_INVALID_ARG, "norm_w is not 16-byte aligned");
+        p->norm_w = d->norm_w;
+    }
+    return GDN_OK;
+}
+
+// With the prologue, `q` carries the mixed rows and k, v are its channel
+// ranges; the caller must leave k and v NULL.
+gdn_status mixed_rows(const gdn::Problem &p, const void *&q, const void *&k, const void *&v)
+{
+    if (!p.conv_w) return GDN_OK;
+    if (k || v) return fail(GDN_ERR_INVALID_ARG, "with d_conv, q carries the mixed q|k|v rows: k and v must be NULL");
+    if (!q) return fail(GDN_ERR_INVALID_ARG, "q (the mixed rows) is NULL");
+    const size_t es = p.bf16 ? 2 : 4;
+    const char *b = static_cast<const char *>(q);
+    k = b + es * (size_t)p.H_k * p.d_k;
+    v = b + es * 2 * (size_t)p.H_k * p.d_k;
+    return GDN_OK;
+}
+
+// The recurrent part of a slot row follows its convolution state.
+const float *ssm_part(const gdn::Problem &p, const float *s) { return s ? s + p.conv_state : nullptr; }
+float *ssm_part(const gdn::Problem &p, float *s) { return s ? s + p.conv_state : nullptr; }
+
+gdn_status hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
     return GDN_OK;
 }
 
@@ -178,15 +225,15 @@ gdn_status gdn_prefill_prepare(const gdn_dims *dims, const void *q, const void *
     g_last_error[0] = 0;
     gdn::Problem p;
     gdn_status st = resolve(dims, &p);
+    if (st == GDN_OK && p.conv_w)
+        st = fail(GDN_ERR_UNSUPPORTED, "the convolution prologue reads the slot state: use gdn_chunked_prefill");
     if (st == GDN_OK) st = check_counts(n_seqs, total_tokens);
     if (st == GDN_OK) st = check_prepare_inputs(q, k, v, g, beta, cu_seqlens);
     if (st == GDN_OK) st = check_workspace(p, n_seqs, total_tokens, workspace, workspace_bytes);
     if (st != GDN_OK) return st;
     gdn::PrefillArgs a{q, k, v, g, beta, nullptr, nullptr, nullptr, cu_seqlens, nullptr,
-                       nullptr, n_seqs, total_tokens, workspace};
-    hipError_t e = gdn::launch_prepare(p, a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(GDN_ERR_HIP, "prepare launch failed: %s", hipGetErrorString(e));
-    return GDN_OK;
+                       nullptr, n_seqs, total_tokens, workspace, nullptr, nullptr};
+    return hip_status(gdn::launch_prepare(p, a, static_cast<hipStream_t>(stream)), "prepare");
 }
 
 gdn_status gdn_prefill_scan(const gdn_dims *dims, const float *state_in, float *state_out,
@@ -197,16 +244,17 @@ gdn_status gdn_prefill_scan(const gdn_dims *dims, const float *state_in, float *
     g_last_error[0] = 0;
     gdn::Problem p;
     gdn_status st = resolve(dims, &p);
+    if (st == GDN_OK && p.conv_w)
+        st = fail(GDN_ERR_UNSUPPORTED, "the convolution prologue reads the slot state: use gdn_chunked_prefill");
     if (st == GDN_OK) st = check_counts(n_seqs, total_tokens);
     if (st == GDN_OK) st = check_scan_inputs(state_in, state_out, out, slot_in, slot_out);
     if (st == GDN_OK) st = check_workspace(p, n_seqs, total_tokens, workspace, workspace_bytes);
     if (st != GDN_OK) return st;
     if (p.H_v > 65535) return fail(GDN_ERR_UNSUPPORTED, "H_v above 65535");
     gdn::PrefillArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, state_in, state_out, out, nullptr, slot_in,
-                       slot_out, n_seqs, total_tokens, const_cast<void *>(workspace)};
-    hipError_t e = gdn::launch_scan(p, a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(GDN_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
-    return GDN_OK;
+                       slot_out, n_seqs, total_tokens, const_cast<void *>(workspace), nullptr, nullptr};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return hip_status(gdn::launch_scan(p, a, s), "scan");
 }
 
 gdn_status gdn_chunked_prefill(const gdn_dims *dims, const void *q, const void *k,
@@ -220,19 +268,26 @@ gdn_status gdn_chunked_prefill(const gdn_dims *dims, const void *q, const void *
     g_last_error[0] = 0;
     gdn::Problem p;
     gdn_status st = resolve(dims, &p);
+    const void *qkv = q;
+    if (st == GDN_OK) st = mixed_rows(p, q, k, v);
     if (st == GDN_OK) st = check_counts(n_seqs, total_tokens);
     if (st == GDN_OK) st = check_prepare_inputs(q, k, v, g, beta, cu_seqlens);
     if (st == GDN_OK) st = check_scan_inputs(state_in, state_out, out, slot_in, slot_out);
     if (st == GDN_OK) st = check_workspace(p, n_seqs, total_tokens, workspace, workspace_bytes);
     if (st != GDN_OK) return st;
     if (p.H_v > 65535) return fail(GDN_ERR_UNSUPPORTED, "H_v above 65535");
-    gdn::PrefillArgs a{q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in,
-                       slot_out, n_seqs, total_tokens, workspace};
+    gdn::PrefillArgs a{q, k, v, g, beta, ssm_part(p, state_in), ssm_part(p, state_out), out,
+                       cu_seqlens, slot_in, slot_out, n_seqs, total_tokens, workspace,
+                       state_in, state_out};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = gdn::launch_prepare(p, a, s);
-    if (e == hipSuccess) e = gdn::launch_scan(p, a, s);
-    if (e != hipSuccess) return fail(GDN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
-    return GDN_OK;
+    st = hip_status(gdn::launch_prepare(p, a, s), "prepare");
+    if (st == GDN_OK) st = hip_status(gdn::launch_scan(p, a, s), "scan");
+    // the convolution state is replaced only after the preparation has read it
+    if (st == GDN_OK && p.conv_w)
+        st = hip_status(gdn::launch_conv_state(p, qkv, cu_seqlens, n_seqs == 1 ? (int)total_tokens : -1,
+                                               n_seqs, total_tokens, state_in, state_out, slot_in,
+                                               slot_out, s), "convolution state");
+    return st;
 }
 
 gdn_status gdn_recurrent_step(const gdn_dims *dims, const void *q, const void *k,
@@ -248,12 +303,18 @@ gdn_status gdn_recurrent_step(const gdn_dims *dims, const void *q, const void *k
     if (n_seqs < 1) return fail(GDN_ERR_INVALID_ARG, "n_seqs must be >= 1 (got %d)", n_seqs);
     if (n_seqs > INT32_MAX / 2) return fail(GDN_ERR_UNSUPPORTED, "n_seqs too large");
     if (p.H_v > 65535) return fail(GDN_ERR_UNSUPPORTED, "H_v above 65535");
-    st = check_tensors(q, k, v, g, beta, state_in, state_out, out, slot_in, slot_out);
+    const void *qkv = q;
+    st = mixed_rows(p, q, k, v);
+    if (st == GDN_OK) st = check_tensors(q, k, v, g, beta, state_in, state_out, out, slot_in, slot_out);
     if (st != GDN_OK) return st;
-    gdn::DecodeArgs a{q, k, v, g, beta, state_in, state_out, out, slot_in, slot_out, n_seqs};
-    hipError_t e = gdn::launch_decode(p, a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(GDN_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
-    return GDN_OK;
+    gdn::DecodeArgs a{q, k, v, g, beta, ssm_part(p, state_in), ssm_part(p, state_out), out,
+                      slot_in, slot_out, n_seqs, state_in, state_out};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(gdn::launch_decode(p, a, s), "decode");
+    if (st == GDN_OK && p.conv_w)
+        st = hip_status(gdn::launch_conv_state(p, qkv, nullptr, -1, n_seqs, n_seqs, state_in, state_out,
+                                               slot_in, slot_out, s), "convolution state");
+    return st;
 }
 
 gdn_status gdn_recurrent_multi(const gdn_dims *dims, const void *q, const void *k,
@@ -266,17 +327,22 @@ gdn_status gdn_recurrent_multi(const gdn_dims *dims, const void *q, const void *
     g_last_error[0] = 0;
     gdn::Problem p;
     gdn_status st = resolve(dims, &p);
+    const void *qkv = q;
+    if (st == GDN_OK) st = mixed_rows(p, q, k, v);
     if (st == GDN_OK) st = check_counts(n_seqs, total_tokens);
     if (st == GDN_OK) st = check_prepare_inputs(q, k, v, g, beta, cu_seqlens);
     if (st == GDN_OK) st = check_scan_inputs(state_in, state_out, out, slot_in, slot_out);
     if (st != GDN_OK) return st;
     if (n_seqs > 0x7fffffff / 2) return fail(GDN_ERR_UNSUPPORTED, "n_seqs too large");
     if (p.H_v > 65535) return fail(GDN_ERR_UNSUPPORTED, "H_v above 65535");
-    gdn::DecodeMultiArgs a{q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in,
-                           slot_out, n_seqs, total_tokens};
-    hipError_t e = gdn::launch_decode_multi(p, a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(GDN_ERR_HIP, "multi-token decode launch failed: %s", hipGetErrorString(e));
-    return GDN_OK;
+    gdn::DecodeMultiArgs a{q, k, v, g, beta, ssm_part(p, state_in), ssm_part(p, state_out), out,
+                           cu_seqlens, slot_in, slot_out, n_seqs, total_tokens, state_in, state_out};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(gdn::launch_decode_multi(p, a, s), "multi-token decode");
+    if (st == GDN_OK && p.conv_w)
+        st = hip_status(gdn::launch_conv_state(p, qkv, cu_seqlens, -1, n_seqs, total_tokens, state_in,
+                                               state_out, slot_in, slot_out, s), "convolution state");
+    return st;
 }
 
 }  // extern "C"

@@ -77,6 +77,9 @@ __device__ __forceinline__ float gate_g(float a, float bias, float rate) {
 }
 __device__ __forceinline__ float gate_beta(float b) { return 1.f / (1.f + expf(-b)); }
 
+// silu(x) = x * sigmoid(x) = x / (1 + e^-x) (e^-x overflowing to inf gives -0).
+__device__ __forceinline__ float silu(float x) { return x / (1.f + expf(-x)); }
+
 // Wave-wide (64 lanes) sum.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

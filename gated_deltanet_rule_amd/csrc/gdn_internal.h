@@ -18,8 +18,25 @@ struct Problem {
     // raw gates: beta = sigmoid(b), g = softplus(a + ssm_dt[h]) * ssm_a[h]
     const float *ssm_a;    // null: g and beta are given as the operator takes them
     const float *ssm_dt;
+    // row strides (elements) of q / k and of v: H_k d_k and H_v d_v, or
+    // conv_dim when the three are channel ranges of the mixed rows
+    int64_t rs_qk, rs_v;
+    // prologue: x = silu(causal conv(qkv)), convolution state at the start of
+    // each slot row (conv_state floats); conv_w null = off
+    const float *conv_w;   // [conv_dim][kConv]
+    int conv_dim;
+    int64_t conv_state;    // (kConv - 1) * conv_dim, 0 when off
+    // epilogue: out = o / sqrt(mean(o^2) + eps) * norm_w * silu(z); z null = off
+    const void *z;
+    const float *norm_w;
 };
 
+// Taps of the fused convolution prologue.
+constexpr int kConv = 4;
+
+// State pointers below address the recurrent state of slot 0; with the
+// prologue, conv_in / conv_out address the slot rows themselves (the
+// convolution state at their start).
 struct DecodeArgs {
     const void *q, *k, *v;
     const float *g, *beta;
@@ -28,6 +45,8 @@ struct DecodeArgs {
     void *out;
     const int32_t *slot_in, *slot_out;
     int32_t n_seqs;
+    const float *conv_in;
+    float *conv_out;
 };
 
 hipError_t launch_decode(const Problem &p, const DecodeArgs &a, hipStream_t s);
@@ -42,6 +61,8 @@ struct DecodeMultiArgs {
     const int32_t *cu_seqlens, *slot_in, *slot_out;
     int32_t n_seqs;
     int64_t total_tokens;
+    const float *conv_in;
+    float *conv_out;
 };
 
 hipError_t launch_decode_multi(const Problem &p, const DecodeMultiArgs &a, hipStream_t s);
@@ -56,6 +77,8 @@ struct PrefillArgs {
     int32_t n_seqs;
     int64_t total_tokens;
     void *workspace;
+    const float *conv_in;
+    float *conv_out;
 };
 
 // Chunk size of the WY form.
@@ -70,7 +93,21 @@ inline int64_t max_chunks(int32_t n_seqs, int64_t total_tokens) {
 size_t prefill_workspace_bytes(const Problem &p, int32_t n_seqs, int64_t total_tokens);
 // state-independent phase: chunk table + per-chunk WY factors into the workspace
 hipError_t launch_prepare(const Problem &p, const PrefillArgs &a, hipStream_t s);
-// sequential phase: reads the workspace written by launch_prepare
+// sequential phase: reads the workspace written by launch_prepare (and runs
+// the gated RMSNorm epilogue when p.z is set)
 hipError_t launch_scan(const Problem &p, const PrefillArgs &a, hipStream_t s);
+
+// Layer fusion passes (gdn_layer.hip).
+// New convolution state of every sequence: the last kConv - 1 inputs of its
+// state followed by its rows.  `cu` null: sequence i is row i (one token
+// each); single_T >= 0: one sequence of rows [0, single_T).  Runs after every
+// reader of the old state (it may be written in place).
+hipError_t launch_conv_state(const Problem &p, const void *qkv, const int32_t *cu, int single_T,
+                             int32_t n_seqs, int64_t total_tokens, const float *conv_in,
+                             float *conv_out, const int32_t *slot_in, const int32_t *slot_out,
+                             hipStream_t s);
+// Gated RMSNorm of the fp32 rows o (T x H_v rows of d_v) into `out`
+// (out_dtype; may be o itself when that is fp32).
+hipError_t launch_gated_norm(const Problem &p, const float *o, void *out, int64_t total_tokens, hipStream_t s);
 
 }  // namespace gdn

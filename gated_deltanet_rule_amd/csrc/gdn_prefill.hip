@@ -53,7 +53,7 @@ namespace {
 constexpr int C = kChunk;
 
 struct ChunkEntry {
-    int32_t seq, t0, len, pad;
+    int32_t seq, t0, len, first;   // first: the sequence's first chunk
 };
 
 // --------------------------------------------------------------------------
@@ -97,16 +97,24 @@ template <int DK, int DV, typename E> struct Geo {
 };
 
 struct WsLayout {
-    size_t entries, cstart, vblocks, kblocks, vblk, kblk, total;
+    size_t entries, cstart, vblocks, kblocks, vblk, kblk, obuf, total;
     int max_chunks;
 };
 
+// With the epilogue and a bf16 output, the scan's fp32 o is staged in the
+// workspace so that the result is rounded once.
+bool stage_o(const Problem &p) { return p.z && p.out_bf16; }
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Operand type of the chunked form: bf16 for bf16 inputs, except with the
+// convolution prologue, whose output keeps fp32 (see prep_kernel).
+bool op_bf16(const Problem &p) { return p.bf16 && !p.conv_w; }
 
 WsLayout ws_layout(const Problem &p, int32_t n_seqs, int64_t T)
 {
     WsLayout L;
-    const bool bf = p.bf16 != 0;
+    const bool bf = op_bf16(p);
     L.max_chunks = (int)max_chunks(n_seqs, T);
     L.entries = 256;
     L.cstart = align256(L.entries + sizeof(ChunkEntry) * (size_t)L.max_chunks);
@@ -114,7 +122,8 @@ WsLayout ws_layout(const Problem &p, int32_t n_seqs, int64_t T)
     L.vblk = (size_t)vblk_kib(p.d_k, p.d_v, bf) * 1024;
     L.kblk = (size_t)kblk_kib(p.d_k, bf) * 1024;
     L.kblocks = L.vblocks + L.vblk * (size_t)L.max_chunks * p.H_v;
-    L.total = L.kblocks + L.kblk * (size_t)L.max_chunks * p.H_k;
+    L.obuf = align256(L.kblocks + L.kblk * (size_t)L.max_chunks * p.H_k);
+    L.total = L.obuf + (stage_o(p) ? sizeof(float) * (size_t)T * p.H_v * p.d_v : 0);
     return L;
 }
 
@@ -164,7 +173,7 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(
             } else {
                 for (int c = 0; c < nc; ++c) {
                     const int idx = start + c;
-                    if (idx < max_ch) ent[idx] = ChunkEntry{i, tb + c * C, min(C, te - tb - c * C), 0};
+                    if (idx < max_ch) ent[idx] = ChunkEntry{i, tb + c * C, min(C, te - tb - c * C), c == 0};
                 }
             }
         }
@@ -190,7 +199,7 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(
         const int tb = min(max(cu[lo], 0), T);
         const int te = min(max(cu[lo + 1], tb), T);
         const int c = j - s_cs[lo];
-        ent[j] = ChunkEntry{lo, tb + c * C, min(C, te - tb - c * C), 0};
+        ent[j] = ChunkEntry{lo, tb + c * C, min(C, te - tb - c * C), c == 0};
     }
 }
 
@@ -309,6 +318,15 @@ struct PrepParams {
     float scale, eps;
     int single_T;      // >= 0: one sequence of this many tokens, no chunk table
     Gates gates;       // raw gate projections, or g and beta as given
+    int64_t rs_qk, rs_v;       // row strides (elements) of q / k and of v
+    // convolution prologue (prep_kernel<..., true>): q, k, v are channel
+    // ranges of the mixed rows; conv_in holds the slot rows (convolution state
+    // first), or any readable buffer when has_state is 0
+    const float *conv_w;
+    const float *conv_in;
+    const int32_t *slot_in;
+    int64_t slot_stride;
+    int has_state;
 };
 
 // LDS of the preparation kernel.  Rows are padded so that the row stride is
@@ -333,9 +351,66 @@ template <int DK, int DV, typename E> struct PrepLds {
 // --------------------------------------------------------------------------
 // 2. per-chunk preparation (state independent)
 // --------------------------------------------------------------------------
-template <int DK, int DV, typename E>
+// silu of a 4-tap causal convolution, per channel: x0 oldest, x3 current.
+__device__ __forceinline__ float conv_silu4(float4 w, float x0, float x1, float x2, float x3)
+{
+    return silu(w.x * x0 + w.y * x1 + w.z * x2 + w.w * x3);
+}
+
+// Four consecutive input elements (the prologue's column vector): 8 bytes of
+// bf16 or 16 bytes of fp32, kept packed until used.
+template <typename In> struct In4;
+template <> struct In4<bf16_t> {
+    typedef uint2 T;
+    __device__ static __forceinline__ float4 f(uint2 u) {
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+    }
+};
+template <> struct In4<float> {
+    typedef float4 T;
+    __device__ static __forceinline__ float4 f(float4 u) { return u; }
+};
+
+// silu(conv) of NR consecutive rows row0.. of four channels, from x[0 .. NR+2]
+// holding rows row0-3 .. row0+NR-1 (fp32); rows before the chunk (negative)
+// are taken from the LDS history hist[m][.] (m = row + 3) at column offset
+// hoff.  Results (fp32 operands) are zero from row `len` on.
+template <int NR>
+__device__ __forceinline__ void conv_rows(const float4 *x, const float4 *w, int row0, int len, const float *hist,
+                                          int hld, int hoff, u32x4 *out)
+{
+#pragma unroll
+    for (int p = 0; p < NR; ++p) {
+        float4 xr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            xr[j] = x[p + j];
+            if (row0 - 3 + p + j < 0) xr[j] = *reinterpret_cast<const float4 *>(hist + (row0 + p + j) * hld + hoff);
+        }
+        const float4 y = make_float4(conv_silu4(w[0], xr[0].x, xr[1].x, xr[2].x, xr[3].x),
+                                     conv_silu4(w[1], xr[0].y, xr[1].y, xr[2].y, xr[3].y),
+                                     conv_silu4(w[2], xr[0].z, xr[1].z, xr[2].z, xr[3].z),
+                                     conv_silu4(w[3], xr[0].w, xr[1].w, xr[2].w, xr[3].w));
+        out[p] = row0 + p < len ? __builtin_bit_cast(u32x4, y) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// CONV: the convolution prologue (build_layer_attn_linear_core on the page
+// "ik_llama.cpp src/llama-delta-net.cpp": ggml_ssm_conv + ggml_silu) is formed
+// while the rows are loaded, from input rows of type In.  A thread then owns
+// KL (VL) consecutive rows of one four-channel column vector; the three rows
+// before a thread's first are read back from LDS (or, for K and Q, loaded
+// too), and the three rows before the chunk (the slot's convolution state
+// for a sequence's first chunk, else the preceding rows) are staged through
+// LDS.  The operands stay fp32 (E = float): after SiLU the keys of
+// neighbouring tokens are correlated, and rounding q, k, v to bf16 would cost
+// the solve and the read-out several percent of the output's rms.
+template <int DK, int DV, typename E, bool CONV, typename In>
 __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepParams pp)
 {
+    static_assert(!CONV || sizeof(E) == 4, "the prologue runs on fp32 operands");
+    using IV = typename In4<In>::T;
     using M = Mfma<E>;
     using SP = Split<E>;
     using G = Geo<DK, DV, E>;
@@ -363,17 +438,21 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
     float *sColh = sBetah + NH * C;                             // [NH][C] beta_c e^{G_c} / |k_c|  (columns of T for W)
 
     const int chunk = blockIdx.x, kh = blockIdx.y;
-    int t0, len;
+    int t0, len, seq, first;
     if (pp.single_T >= 0) {
         // a single sequence covers tokens [0, T): chunk c is [64c, min(64c + 64, T))
         if (chunk * C >= pp.single_T) return;
         t0 = chunk * C;
         len = min(C, pp.single_T - t0);
+        seq = 0;
+        first = chunk == 0;
     } else {
         if (chunk >= pp.hdr[0]) return;
         const ChunkEntry ce = pp.ent[chunk];
         t0 = ce.t0;
         len = ce.len;
+        seq = ce.seq;
+        first = ce.first;
     }
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -381,6 +460,9 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
     const E *qg = static_cast<const E *>(pp.q);
     const E *kg = static_cast<const E *>(pp.k);
     const E *vg = static_cast<const E *>(pp.v);
+    const In *qi = static_cast<const In *>(pp.q);     // the prologue's input rows
+    const In *ki = static_cast<const In *>(pp.k);
+    const In *vi_ = static_cast<const In *>(pp.v);
     const int ratio = pp.H_v / pp.H_k;
 
     // g and beta of up to NH value heads (wave w: head j0 + w, lane: row)
@@ -428,31 +510,107 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
         const float tail = lane == 0 ? expf((float)Gn) : __int_as_float(lane == 1 ? t0 : len);
         buffer_store(tail, raw_buffer(scal + 128, 12), (uint32_t)lane * 4u);
     };
-    // V rows of one value head, loaded one head ahead into registers
+    // prologue: the slot holding this sequence's convolution state (row 0 of
+    // a readable buffer when there is none; its values are then not used)
+    int cslot = 0;
+    bool state_ok = false;
+    if constexpr (CONV) {
+        const int s_in = pp.slot_in[seq];
+        state_ok = pp.has_state && s_in >= 0;
+        cslot = state_ok ? s_in : 0;
+    }
+    const size_t vch0 = 2 * (size_t)pp.H_k * DK;          // first v channel of the mixed rows
+
+    // V rows of one value head, loaded one head ahead into registers (with
+    // the prologue: the thread's VL consecutive rows and its share of the
+    // head's three history rows and of its taps, both staged through LDS;
+    // the three rows before a thread's first are read back from LDS once
+    // every row is there)
     constexpr int VL = (C * VPRV + 255) / 256;
-    u32x4 vpre[VL];
+    constexpr int NHV = CONV ? (3 * DV + 255) / 256 : 1;
+    constexpr int NWV = CONV ? (4 * DV + 255) / 256 : 1;
+    u32x4 vpre[CONV ? 1 : VL];
+    IV vraw[CONV ? VL : 1];
+    float vh[NHV], vw[NWV];
+    const int vrow0 = (tid / VPRV) * VL, vcv = tid % VPRV;
     static_assert(C * VPRV % 256 == 0 && C * VPR % 256 == 0, "whole vectors per thread");
     auto load_v = [&](int hh) {
+        if constexpr (!CONV) {
 #pragma unroll
-        for (int p = 0; p < VL; ++p) {
-            const int vi = tid + 256 * p;
-            const int r = vi / VPRV, cv = vi % VPRV;
-            const u32x4 x = *reinterpret_cast<const u32x4 *>(vg + ((size_t)(t0 + min(r, len - 1)) * pp.H_v + hh) * DV + cv * VEC);
-            vpre[p] = r < len ? x : u32x4{0u, 0u, 0u, 0u};
+            for (int p = 0; p < VL; ++p) {
+                const int vi = tid + 256 * p;
+                const int r = vi / VPRV, cv = vi % VPRV;
+                const u32x4 x = *reinterpret_cast<const u32x4 *>(vg + (size_t)(t0 + min(r, len - 1)) * pp.rs_v +
+                                                                  (size_t)hh * DV + cv * VEC);
+                vpre[p] = r < len ? x : u32x4{0u, 0u, 0u, 0u};
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < VL; ++p) {
+                const int rr = min(vrow0 + p, len - 1);
+                vraw[p] = *reinterpret_cast<const IV *>(vi_ + (size_t)(t0 + rr) * pp.rs_v + (size_t)hh * DV + vcv * VEC);
+            }
+#pragma unroll
+            for (int j = 0; j < NHV; ++j) {
+                const int idx = min(tid + 256 * j, 3 * DV - 1);
+                const int m = idx / DV, c = idx % DV;
+                const float xr = to_f32(vi_[(size_t)max(t0 - 3 + m, 0) * pp.rs_v + (size_t)hh * DV + c]);
+                const float xs = pp.conv_in[(size_t)cslot * pp.slot_stride + (vch0 + (size_t)hh * DV + c) * 3 + m];
+                vh[j] = first ? (state_ok ? xs : 0.f) : xr;
+            }
+#pragma unroll
+            for (int j = 0; j < NWV; ++j)
+                vw[j] = pp.conv_w[(vch0 + (size_t)hh * DV) * 4 + min(tid + 256 * j, 4 * DV - 1)];
         }
     };
+
 
     // 1. K and Q rows of the chunk (row-major, zero past the end) and their
     //    inverse norms; a row's VPR vectors sit in VPR adjacent lanes
     constexpr int KL = C * VPR / 256;     // 16-byte vectors of K (and of Q) per thread
+    constexpr int KR = CONV ? KL + 3 : KL;
+    constexpr int NHK = CONV ? (6 * DK + 255) / 256 : 1;
+    const int krow0 = (tid / VPR) * KL, kcv = tid % VPR;
     u32x4 kx[KL], qx[KL];
+    IV kraw[CONV ? KR : 1], qraw[CONV ? KR : 1];
+    float hk[NHK];
+    float4 wk[CONV ? VEC : 1], wq[CONV ? VEC : 1];
+    if constexpr (!CONV) {
 #pragma unroll
-    for (int p = 0; p < KL; ++p) {
-        const int vi = tid + 256 * p;
-        const int r = vi / VPR, cv = vi % VPR;
-        const size_t off = ((size_t)(t0 + min(r, len - 1)) * pp.H_k + kh) * DK + (size_t)cv * VEC;
-        kx[p] = *reinterpret_cast<const u32x4 *>(kg + off);
-        qx[p] = *reinterpret_cast<const u32x4 *>(qg + off);
+        for (int p = 0; p < KL; ++p) {
+            const int vi = tid + 256 * p;
+            const int r = vi / VPR, cv = vi % VPR;
+            const size_t off = (size_t)(t0 + min(r, len - 1)) * pp.rs_qk + (size_t)kh * DK + (size_t)cv * VEC;
+            kx[p] = *reinterpret_cast<const u32x4 *>(kg + off);
+            qx[p] = *reinterpret_cast<const u32x4 *>(qg + off);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < KR; ++u) {
+            const int rr = min(max(krow0 - 3 + u, 0), len - 1);
+            const size_t off = (size_t)(t0 + rr) * pp.rs_qk + (size_t)kh * DK + (size_t)kcv * VEC;
+            kraw[u] = *reinterpret_cast<const IV *>(ki + off);
+            qraw[u] = *reinterpret_cast<const IV *>(qi + off);
+        }
+        // three history rows of the key head's q and k channels, [m][q | k]
+#pragma unroll
+        for (int j = 0; j < NHK; ++j) {
+            const int idx = min(tid + 256 * j, 6 * DK - 1);
+            const int m = idx / (2 * DK), c2 = idx % (2 * DK);
+            const bool isk = c2 >= DK;
+            const int c = isk ? c2 - DK : c2;
+            const float xr = to_f32((isk ? ki : qi)[(size_t)max(t0 - 3 + m, 0) * pp.rs_qk + (size_t)kh * DK + c]);
+            const size_t ch = (isk ? (size_t)pp.H_k * DK : 0) + (size_t)kh * DK + c;
+            const float xs = pp.conv_in[(size_t)cslot * pp.slot_stride + ch * 3 + m];
+            hk[j] = first ? (state_ok ? xs : 0.f) : xr;
+        }
+        const float4 *wkp = reinterpret_cast<const float4 *>(pp.conv_w + ((size_t)pp.H_k * DK + (size_t)kh * DK + kcv * VEC) * 4);
+        const float4 *wqp = reinterpret_cast<const float4 *>(pp.conv_w + ((size_t)kh * DK + kcv * VEC) * 4);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            wk[e] = wkp[e];
+            wq[e] = wqp[e];
+        }
     }
     // the first value head's g, beta and V: issued after K and Q (the
     // scheduling barrier keeps that order), so that waiting for K and Q does
@@ -460,10 +618,24 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
     __builtin_amdgcn_sched_barrier(0);
     load_gb(0);
     load_v(kh * ratio);
+    if constexpr (CONV) {
+#pragma unroll
+        for (int j = 0; j < NHK; ++j)
+            if (tid + 256 * j < 6 * DK) sA[tid + 256 * j] = hk[j];
+        lds_sync();
+        float4 xk[KR], xq[KR];
+#pragma unroll
+        for (int u = 0; u < KR; ++u) {
+            xk[u] = In4<In>::f(kraw[u]);
+            xq[u] = In4<In>::f(qraw[u]);
+        }
+        conv_rows<KL>(xk, wk, krow0, len, sA, 2 * DK, DK + kcv * VEC, kx);
+        conv_rows<KL>(xq, wq, krow0, len, sA, 2 * DK, kcv * VEC, qx);
+    }
 #pragma unroll
     for (int p = 0; p < KL; ++p) {
-        const int vi = tid + 256 * p;
-        const int r = vi / VPR, cv = vi % VPR;
+        const int r = CONV ? krow0 + p : (tid + 256 * p) / VPR;
+        const int cv = kcv;
         const u32x4 kv = r < len ? kx[p] : u32x4{0u, 0u, 0u, 0u};
         const u32x4 qv = r < len ? qx[p] : u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4 *>(sK + r * LDK + cv * VEC) = kv;
@@ -524,11 +696,41 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
         const float *sRA = sRAh + hs * C, *sBeta = sBetah + hs * C, *sCol = sColh + hs * C;
 
         // 4a. V rows of this head; row scalars of the next NH heads
+        if constexpr (!CONV) {
 #pragma unroll
-        for (int p = 0; p < VL; ++p) {
-            const int vi = tid + 256 * p;
-            if (vi < C * VPRV)
-                *reinterpret_cast<u32x4 *>(sX + (vi / VPRV) * LDX + (vi % VPRV) * VEC) = vpre[p];
+            for (int p = 0; p < VL; ++p) {
+                const int vi = tid + 256 * p;
+                if (vi < C * VPRV)
+                    *reinterpret_cast<u32x4 *>(sX + (vi / VPRV) * LDX + (vi % VPRV) * VEC) = vpre[p];
+            }
+        } else {
+            // raw rows into sX and the head's history rows [m][DV] into sA
+            // (free here); then each thread takes its rows and the three
+            // before them, and after a second barrier writes the prologue's
+            // result over the raw rows
+            float4 xv[VL + 3];
+#pragma unroll
+            for (int p = 0; p < VL; ++p) {
+                xv[p + 3] = In4<In>::f(vraw[p]);
+                *reinterpret_cast<float4 *>(sX + (vrow0 + p) * LDX + vcv * VEC) = xv[p + 3];
+            }
+#pragma unroll
+            for (int j = 0; j < NHV; ++j)
+                if (tid + 256 * j < 3 * DV) sA[tid + 256 * j] = vh[j];
+#pragma unroll
+            for (int j = 0; j < NWV; ++j)
+                if (tid + 256 * j < 4 * DV) sA[3 * DV + tid + 256 * j] = vw[j];
+            lds_sync();
+#pragma unroll
+            for (int u = 0; u < 3; ++u)
+                xv[u] = *reinterpret_cast<const float4 *>(sX + max(vrow0 - 3 + u, 0) * LDX + vcv * VEC);
+            u32x4 res[VL];
+            conv_rows<VL>(xv, reinterpret_cast<const float4 *>(sA + 3 * DV) + vcv * VEC, vrow0, len, sA, DV,
+                          vcv * VEC, res);
+            lds_sync();
+#pragma unroll
+            for (int p = 0; p < VL; ++p)
+                *reinterpret_cast<u32x4 *>(sX + (vrow0 + p) * LDX + vcv * VEC) = res[p];
         }
         load_v(kh * ratio + min(jv + 1, ratio - 1));   // next head (the last reloads itself)
         if (jv > 0 && hs == 0) {
@@ -1006,6 +1208,7 @@ struct WsPtrs {
     ChunkEntry *ent;
     int32_t *cstart;
     char *vblocks, *kblocks;
+    float *obuf;
 };
 
 WsPtrs ws_ptrs(const Problem &p, const PrefillArgs &a)
@@ -1018,6 +1221,7 @@ WsPtrs ws_ptrs(const Problem &p, const PrefillArgs &a)
     w.cstart = reinterpret_cast<int32_t *>(ws + w.L.cstart);
     w.vblocks = ws + w.L.vblocks;
     w.kblocks = ws + w.L.kblocks;
+    w.obuf = reinterpret_cast<float *>(ws + w.L.obuf);
     return w;
 }
 
@@ -1038,12 +1242,31 @@ hipError_t prepare_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
     PrepParams pp{a.q, a.k, a.v, a.g, a.beta, w.hdr, w.ent, w.vblocks, w.kblocks,
                   p.H_k, p.H_v, p.scale, p.eps, single ? (int)a.total_tokens : -1,
                   // without raw gates the parameter loads read g (see gates_of in gdn_decode.hip)
-                  p.ssm_a ? Gates{p.ssm_a, p.ssm_dt, 1} : Gates{a.g, a.g, 0}};
+                  p.ssm_a ? Gates{p.ssm_a, p.ssm_dt, 1} : Gates{a.g, a.g, 0},
+                  p.rs_qk, p.rs_v, p.conv_w,
+                  // without a state pool the history loads read the taps (unused)
+                  a.conv_in ? a.conv_in : p.conv_w, a.slot_in, p.slot_stride, a.conv_in != nullptr};
     constexpr size_t lds = PrepLds<DK, DV, E>::BYTES;
-    e = set_lds(prep_kernel<DK, DV, E>, lds);
-    if (e != hipSuccess) return e;
     const int chunks = single ? (int)((a.total_tokens + C - 1) / C) : w.L.max_chunks;
-    hipLaunchKernelGGL((prep_kernel<DK, DV, E>), dim3(chunks, p.H_k), dim3(256), lds, st, pp);
+    const dim3 grid(chunks, p.H_k);
+    if constexpr (sizeof(E) == 4) {
+        if (p.conv_w) {
+            // the prologue runs on fp32 operands whatever the input rows are
+            if (p.bf16) {
+                e = set_lds(prep_kernel<DK, DV, float, true, bf16_t>, lds);
+                if (e == hipSuccess)
+                    hipLaunchKernelGGL((prep_kernel<DK, DV, float, true, bf16_t>), grid, dim3(256), lds, st, pp);
+            } else {
+                e = set_lds(prep_kernel<DK, DV, float, true, float>, lds);
+                if (e == hipSuccess)
+                    hipLaunchKernelGGL((prep_kernel<DK, DV, float, true, float>), grid, dim3(256), lds, st, pp);
+            }
+            return e != hipSuccess ? e : hipGetLastError();
+        }
+    }
+    e = set_lds(prep_kernel<DK, DV, E, false, E>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((prep_kernel<DK, DV, E, false, E>), grid, dim3(256), lds, st, pp);
     return hipGetLastError();
 }
 
@@ -1052,7 +1275,8 @@ hipError_t scan_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
 {
     const WsPtrs w = ws_ptrs(p, a);
     constexpr int CT = 1;    // column tiles per workgroup
-    ScanParams sp{a.state_in, a.state_out, a.out, a.slot_in, a.slot_out, w.cstart, w.ent,
+    void *o = stage_o(p) ? static_cast<void *>(w.obuf) : a.out;
+    ScanParams sp{a.state_in, a.state_out, o, a.slot_in, a.slot_out, w.cstart, w.ent,
                   w.vblocks, w.kblocks, p.H_k, p.H_v, p.slot_stride,
                   a.n_seqs == 1 ? (int)a.total_tokens : -1};
     // With several sequences, one scan workgroup per CU: two workgroups on
@@ -1065,13 +1289,15 @@ hipError_t scan_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((scan_kernel<DK, DV, CT, E, OT>), dim3(p.H_v, DV / (16 * CT), a.n_seqs),
                        dim3(CT * 256), lds, st, sp);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e == hipSuccess && p.z) e = launch_gated_norm(p, static_cast<const float *>(o), a.out, a.total_tokens, st);
+    return e;
 }
 
 template <int DK, int DV>
 hipError_t prepare_dv(const Problem &p, const PrefillArgs &a, hipStream_t st)
 {
-    return p.bf16 ? prepare_t<DK, DV, bf16_t>(p, a, st) : prepare_t<DK, DV, float>(p, a, st);
+    return op_bf16(p) ? prepare_t<DK, DV, bf16_t>(p, a, st) : prepare_t<DK, DV, float>(p, a, st);
 }
 
 template <int DK>
@@ -1088,9 +1314,11 @@ hipError_t prepare_dk(const Problem &p, const PrefillArgs &a, hipStream_t st)
 template <int DK, int DV>
 hipError_t scan_dv(const Problem &p, const PrefillArgs &a, hipStream_t st)
 {
-    if (p.bf16)
-        return p.out_bf16 ? scan_t<DK, DV, bf16_t, bf16_t>(p, a, st) : scan_t<DK, DV, bf16_t, float>(p, a, st);
-    return p.out_bf16 ? scan_t<DK, DV, float, bf16_t>(p, a, st) : scan_t<DK, DV, float, float>(p, a, st);
+    // with the epilogue the scan writes fp32 o (staged or in place)
+    const bool ob = p.out_bf16 && !p.z;
+    if (op_bf16(p))
+        return ob ? scan_t<DK, DV, bf16_t, bf16_t>(p, a, st) : scan_t<DK, DV, bf16_t, float>(p, a, st);
+    return ob ? scan_t<DK, DV, float, bf16_t>(p, a, st) : scan_t<DK, DV, float, float>(p, a, st);
 }
 
 template <int DK>

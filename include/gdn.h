@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 2
+#define GDN_VERSION 3
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -102,6 +102,41 @@ typedef enum gdn_gate_mode {
     GDN_GATES_RAW = 1
 } gdn_gate_mode;
 
+/*
+ * Layer fusion (optional), the steps next to the operator in
+ * build_layer_attn_linear_core on the page "ik_llama.cpp
+ * src/llama-delta-net.cpp":
+ *
+ * Prologue (d_conv = 4): ggml_ssm_conv + ggml_silu.  The `q` argument of an
+ * entry point then carries the mixed projection rows qkv [T][conv_dim]
+ * (dims->dtype, conv_dim = 2*H_k*d_k + H_v*d_v, channels q | k | v in that
+ * order) and `k`, `v` must be NULL.  Per channel c, with u the channel's d_conv-1
+ * state values (oldest first) followed by the sequence's rows,
+ *     x[t][c] = silu(sum_j conv_w[c][j] * u[t + j]),   silu(y) = y / (1 + e^-y),
+ * and q, k, v are the three channel ranges of x.  The convolution state lives
+ * at the start of every slot row of the state pools: a slot row is
+ *     [conv_dim][d_conv-1] fp32 convolution state (oldest first), then
+ *     [H_v][d_k][d_v] fp32 recurrent state,
+ * so slot_stride (0 = the sum of both) and the state_in / state_out pointers
+ * refer to whole rows.  slot_in < 0 starts both parts at zero; the new
+ * convolution state (the last d_conv-1 inputs of u) is written at slot_out.
+ * The convolution output stays fp32 in every entry point: with bf16 rows,
+ * gdn_chunked_prefill then runs its matrix products on fp32 operands (after
+ * SiLU the keys of neighbouring tokens are correlated, and rounding q, k, v
+ * to bf16 would move the result by several percent of its rms).
+ * The split-phase entry points do not support the prologue.
+ *
+ * Epilogue (z != NULL): llm_build_norm (RMS, weight ssm_norm) followed by
+ * ggml_fused_mul_unary(z, ., SILU): each (token, value head) row o of the
+ * operator's output becomes
+ *     out = o / sqrt(mean(o^2) + eps) * norm_w * silu(z)
+ * with the eps of the L2 norms.  gdn_recurrent_step and gdn_recurrent_multi
+ * apply it before o leaves the chip; the chunked prefill applies it in a
+ * pass after the scan, over fp32 o (in place in an fp32 `out`; with a bf16
+ * `out`, o is staged in the workspace, which then grows by
+ * 4*T*H_v*d_v bytes), so the result is rounded once.
+ */
+
 /* Problem dimensions shared by every entry point. */
 typedef struct gdn_dims {
     int32_t H_k;          /* key heads (q and k)                            */
@@ -123,6 +158,13 @@ typedef struct gdn_dims {
                              (<= 0); read only with GDN_GATES_RAW          */
     const float *ssm_dt;  /* [H_v] device, fp32: per-value-head gate bias;
                              read only with GDN_GATES_RAW                   */
+    int32_t d_conv;       /* 0: no prologue; 4: fused convolution prologue  */
+    const float *conv_w;  /* [conv_dim][d_conv] device fp32, 16-byte
+                             aligned, oldest tap first (with d_conv = 4)   */
+    const void *z;        /* NULL: no epilogue; else the gate [T][H_v][d_v]
+                             (dims->dtype), 16-byte aligned                */
+    const float *norm_w;  /* [d_v] device fp32 RMS-norm weight (with z),
+                             16-byte aligned                                */
 } gdn_dims;
 
 /* Library version (GDN_VERSION). */

@@ -172,3 +172,140 @@ def compare_decode(dc, outs, pool, ref_out, ref_state, heads=None):
     say(f"  {dc.name}: out err/rms = {eo:.3e}, state err/rms = {es:.3e} (tol {tol:g})")
     assert eo <= tol and es <= tol
     return eo, es
+
+
+# ---------------------------------------------------------------------------
+# Layer fusion: convolution prologue (mixed rows + per-slot convolution state
+# at the start of each slot row) and gated RMSNorm epilogue.
+# ---------------------------------------------------------------------------
+
+def layer_pool(case, L):
+    """Slot rows [n_slots, 3*conv_dim + H_v*d_k*d_v]: convolution state, then state."""
+    n = case.pool.shape[0]
+    return np.concatenate([L.conv_pool.reshape(n, -1), case.pool.reshape(n, -1)], axis=1)
+
+
+def split_pool(case, L, rows):
+    """Device slot rows -> (conv states [n, conv_dim, 3], states [n, H_v, d_k, d_v])."""
+    R = rows.cpu().numpy()
+    n = R.shape[0]
+    c = L.conv_pool[0].size
+    return R[:, :c].reshape(L.conv_pool.shape), R[:, c:].reshape(case.pool.shape)
+
+
+def dev_layer(case, L, conv=True, norm=True, device="cuda"):
+    """Device tensors of a layer workload: the case's q/k/v (or the mixed rows),
+    gates, slot rows (or the plain pool), taps, z, norm weight."""
+    import gated_deltanet_rule_amd as gdn
+    d = dev_case(case, device)
+    dt = tdt(case.dtype)
+    f = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(device).to(t)
+    d["conv_w"] = f(L.conv_w)
+    d["qkv"] = f(L.qkv, dt)
+    d["z"] = f(L.z, dt) if norm else None
+    d["norm_w"] = f(L.norm_w) if norm else None
+    if conv:
+        d["pool"] = f(layer_pool(case, L))
+    return d
+
+
+def gpu_layer_prefill(case, L, conv=True, norm=True, raw_gates=False, out_dtype=torch.float32,
+                      inplace=True, chunks=None, d=None):
+    """Run a layer workload through gdn.prefill; `chunks` splits a single
+    sequence into consecutive calls (state rows carried in place)."""
+    import gated_deltanet_rule_amd as gdn
+    d = d or dev_layer(case, L, conv, norm)
+    T = case.total_tokens
+    out = torch.empty((T, case.H_v, case.d_v), dtype=out_dtype, device=d["q"].device)
+    pool_out = d["pool"] if inplace else d["pool"].clone()
+    g, beta, gates = _gate_args(d, raw_gates)
+    cv = (d["conv_w"], case.H_k, case.d_k) if conv else None
+
+    def call(s, e, cu, sl_in):
+        if conv:
+            q, k, v = d["qkv"][s:e], None, None
+        else:
+            q, k, v = d["q"][s:e], d["k"][s:e], d["v"][s:e]
+        z = d["z"][s:e] if norm else None
+        gdn.prefill(q, k, v, g[s:e], beta[s:e], d["pool"], pool_out, out[s:e], cu, sl_in,
+                    d["slot_out"], gates=gates, conv=cv, z=z, norm_w=d["norm_w"])
+
+    if chunks is None:
+        call(0, T, d["cu"], d["slot_in"])
+    else:
+        assert case.n_seqs == 1 and inplace
+        for s in range(0, T, chunks):
+            e = min(T, s + chunks)
+            cu = torch.tensor([0, e - s], dtype=torch.int32, device=d["q"].device)
+            call(s, e, cu, d["slot_in"] if s == 0 else d["slot_out"])
+    torch.cuda.synchronize()
+    return out, pool_out
+
+
+def gpu_layer_multi(case, L, conv=True, norm=True, raw_gates=False, out_dtype=torch.float32,
+                    inplace=True):
+    import gated_deltanet_rule_amd as gdn
+    d = dev_layer(case, L, conv, norm)
+    T = case.total_tokens
+    out = torch.empty((T, case.H_v, case.d_v), dtype=out_dtype, device=d["q"].device)
+    pool_out = d["pool"] if inplace else d["pool"].clone()
+    g, beta, gates = _gate_args(d, raw_gates)
+    q, k, v = (d["qkv"], None, None) if conv else (d["q"], d["k"], d["v"])
+    gdn.decode_multi(q, k, v, g, beta, d["pool"], pool_out, out, d["cu"], d["slot_in"],
+                     d["slot_out"], gates=gates,
+                     conv=(d["conv_w"], case.H_k, case.d_k) if conv else None,
+                     z=d["z"], norm_w=d["norm_w"])
+    torch.cuda.synchronize()
+    return out, pool_out
+
+
+def oracle_layer(case, L, conv=True, norm=True, raw_gates=False, heads=None):
+    """fp64 oracle of the layer workload: (out, states, conv states) per sequence."""
+    from oracle import layer as OL
+    N = case.n_seqs
+    s0 = np.zeros((N, case.H_v, case.d_k, case.d_v))
+    c0 = np.zeros((N,) + L.conv_pool.shape[1:])
+    for i in range(N):
+        if case.slot_in[i] >= 0:
+            s0[i] = case.pool[case.slot_in[i]]
+            c0[i] = L.conv_pool[case.slot_in[i]]
+    g, beta = case.g, case.beta
+    if raw_gates:
+        g, beta = oracle.gates(case.raw_a, case.raw_b, case.ssm_a, case.ssm_dt)
+    z = L.z if norm else None
+    if conv:
+        return OL.run_layer(case.H_k, case.H_v, case.d_k, case.d_v, L.qkv, L.conv_w, c0, g, beta,
+                            case.cu_seqlens, s0, z, L.norm_w, heads=heads)
+    out, sf = oracle.run(case.q, case.k, case.v, g, beta, case.cu_seqlens, s0, heads=heads)
+    if norm:
+        out = OL.gated_rmsnorm(out, z, L.norm_w, 1e-6)
+        if heads is not None:
+            mask = np.zeros(case.H_v, bool)
+            mask[list(heads)] = True
+            out[:, ~mask] = 0.0
+    return out, sf, None
+
+
+def compare_layer(case, L, out, pool_out, ref, conv=True, heads=None, tol=None):
+    """Output and states to the tolerance; convolution states bit-exact (they
+    are copies of inputs)."""
+    ref_out, ref_state, ref_conv = ref
+    tol = tol or TOL[case.dtype]
+    hs = list(range(case.H_v)) if heads is None else list(heads)
+    assert bool(torch.isfinite(out.float()).all()), "non-finite output"
+    o = out[:, hs].float().cpu().numpy().astype(np.float64)
+    eo, _ = rel_err(o, ref_out[:, hs], bf16_out=out.dtype == torch.bfloat16)
+    if conv:
+        cs, st = split_pool(case, L, pool_out)
+    else:
+        cs, st = None, pool_out.cpu().numpy()
+    sl = [int(case.slot_out[i]) for i in range(case.n_seqs)]
+    es, _ = rel_err(st[sl][:, hs].astype(np.float64), ref_state[:, hs])
+    say(f"  {case.name}: out err/rms = {eo:.3e}, state err/rms = {es:.3e} (tol {tol:g})")
+    assert eo <= tol, f"output error {eo:.3e} > {tol}"
+    assert es <= tol, f"state error {es:.3e} > {tol}"
+    if conv:
+        got = cs[sl].astype(np.float64)
+        assert np.array_equal(got, ref_conv), \
+            f"convolution state differs at {np.argwhere(got != ref_conv)[:4].tolist()}"
+    return eo, es

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert gdn.version() == 2
+    assert gdn.version() == 3
     for st in range(5):
         assert gdn.lib.gdn_status_string(st)
     assert gdn.lib.gdn_status_string(99) == b"unknown status"
@@ -67,6 +67,13 @@ def test_workspace_size_grows_with_tokens_and_is_aligned():
     (dict(gate_mode=gdn.GDN_GATES_RAW), 1),                       # no ssm_a / ssm_dt
     (dict(gate_mode=gdn.GDN_GATES_RAW, ssm_a=0x1000), 1),         # ssm_dt missing
     (dict(gate_mode=gdn.GDN_GATES_RAW, ssm_a=0x1002, ssm_dt=0x2000), 1),  # misaligned
+    (dict(d_conv=3, conv_w=0x1000), 2), (dict(d_conv=-4, conv_w=0x1000), 2),
+    (dict(d_conv=4), 1),                                          # no taps
+    (dict(d_conv=4, conv_w=0x1004), 1),                           # misaligned taps
+    (dict(z=0x1000), 1),                                          # no norm weight
+    (dict(z=0x1008, norm_w=0x2000), 1), (dict(z=0x1000, norm_w=0x2004), 1),
+    # with the prologue a slot row also holds 3 * conv_dim convolution state
+    (dict(d_conv=4, conv_w=0x1000, slot_stride=32 * 128 * 128), 1),
 ])
 def test_bad_dims_rejected(kw, status):
     n = ctypes.c_size_t(0)
@@ -84,6 +91,14 @@ def test_raw_gates_accepted_by_sizing():
     m = ctypes.c_size_t(0)
     assert gdn.lib.gdn_prefill_workspace_size(ctypes.byref(_dims()), 1, 64, ctypes.byref(m)) == 0
     assert n.value == m.value
+
+
+def test_conv_rows_grow_the_slot():
+    n = ctypes.c_size_t(0)
+    C = 2 * 16 * 128 + 32 * 128
+    ok = _dims(d_conv=4, conv_w=0x1000, slot_stride=32 * 128 * 128 + 3 * C)
+    assert gdn.lib.gdn_prefill_workspace_size(ctypes.byref(ok), 1, 64, ctypes.byref(n)) == 0
+    assert gdn.conv_state_size(16, 32, 128, 128) == 3 * C
 
 
 def test_null_dims_and_counts():
@@ -181,3 +196,24 @@ def test_multi_decode_validation():
     assert call(sout=FAKE + 1) == 1
     assert gdn.lib.gdn_recurrent_multi(None, *([None] * 11), 1, 4, None) == 1
 
+
+
+def test_prologue_argument_rules():
+    """With d_conv, q carries the mixed rows: k and v must be NULL; the
+    split-phase entry points reject the prologue (it reads the slot state)."""
+    P = ctypes.c_void_p
+    d = _dims(d_conv=4, conv_w=0x1000)
+    assert _call_prefill(d, _prefill_args()) == 1            # k, v given
+    assert b"NULL" in gdn.lib.gdn_last_error()
+    st = gdn.lib.gdn_prefill_prepare(ctypes.byref(d), P(FAKE), None, None, P(FAKE), P(FAKE),
+                                     P(FAKE), 1, 64, P(FAKE), 1 << 40, None)
+    assert st == 2
+    st = gdn.lib.gdn_prefill_scan(ctypes.byref(d), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                                  1, 64, P(FAKE), 1 << 40, None)
+    assert st == 2
+    st = gdn.lib.gdn_recurrent_step(ctypes.byref(d), P(FAKE), P(FAKE), None, P(FAKE), P(FAKE),
+                                    P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 4, None)
+    assert st == 1
+    st = gdn.lib.gdn_recurrent_multi(ctypes.byref(d), None, None, None, P(FAKE), P(FAKE),
+                                     P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 4, 16, None)
+    assert st == 1
