@@ -25,6 +25,9 @@ Alongside (same JSON line):
                 verification), state in place; HBM roofline on state + I/O.
   varlen        8 packed sequences of 17..8192 tokens (12221), one call.
   stream        65536 tokens as 128 calls of 512 with the state carried.
+  layer_prefill the fused layer path (convolution prologue, raw gates, gated
+                RMSNorm epilogue) on the T=4096 prefill, one call.
+  layer_decode  the fused layer path on the decode workload, per step.
   cpu_baseline  the fp64 oracle (test infrastructure, never tuned) on the
                 same prefill workload, on this host's cores.
 All inputs are seeded synthetic data (see gdn_inputs.py).
@@ -57,25 +60,29 @@ C = 64
 # x1.000).  They hold only for the kernel source they were taken on; after any
 # change to its code (comments aside) the bench reports traffic as null until
 # the counters are retaken.
-PREFILL_SRC = os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", "gdn_prefill.hip")
+PREFILL_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
+               for f in ("gdn_prefill.hip", "gdn_mfma.h", "gdn_device.h", "gdn_internal.h")]
 MEASURED_TRAFFIC = {
-    "source_sha256": "0fcc6550fecc97ee8453fe684ab6901812137b784f1eef4b7c05576eec60e5ba",
-    "scan": (100010 * 2.000 + 67584 * 1.000) * 1024,
-    "prepare": (47834 * 2.000 + 165047 * 1.000) * 1024,
+    "source_sha256": "c6034aa41f947ed774fa372bf210f0318a20e067cdd98f8002a6d927f2d36517",
+    "scan": (100005.6 * 2.000 + 67584.0 * 1.000) * 1024,
+    "prepare": (40254.1 * 2.000 + 165147.6 * 1.000) * 1024,
 }
 
 
-def source_digest(path):
-    """SHA-256 of a C/HIP source with comments and blank space removed, so
+def source_digest(paths):
+    """SHA-256 of C/HIP sources with comments and blank space removed, so
     that edits to comments alone do not invalidate measurements."""
     import hashlib
     import re
-    with open(path) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", "", text)
-    text = "\n".join(line.strip() for line in text.splitlines() if line.strip())
-    return hashlib.sha256(text.encode()).hexdigest()
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = "\n".join(line.strip() for line in text.splitlines() if line.strip())
+        h.update(text.encode())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel):
@@ -268,6 +275,98 @@ def bench_decode_multi(gdn, dev, tokens=4, reps=20):
                          "bytes_per_launch": by}}
 
 
+def _layer_dev(case, L, dev):
+    dt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    f = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(t)
+    n = case.pool.shape[0]
+    rows = np.concatenate([L.conv_pool.reshape(n, -1), case.pool.reshape(n, -1)], axis=1)
+    return dict(qkv=f(L.qkv, dt), a=f(case.raw_a), b=f(case.raw_b), ssm_a=f(case.ssm_a),
+                ssm_dt=f(case.ssm_dt), rows=f(rows), conv_w=f(L.conv_w), z=f(L.z, dt),
+                norm_w=f(L.norm_w), cu=f(case.cu_seqlens, torch.int32),
+                slot_in=f(case.slot_in, torch.int32), slot_out=f(case.slot_out, torch.int32))
+
+
+def bench_layer_prefill(gdn, dev, reps=10):
+    """The fused layer path on the T=4096 prefill: mixed q|k|v rows through
+    the convolution prologue, raw gate projections, gated RMSNorm epilogue,
+    bf16 output; one gdn_chunked_prefill call per step."""
+    case = gi.config1()
+    L = gi.make_layer_inputs(case.total_tokens, case.pool.shape[0], case.H_k, case.H_v, case.d_k,
+                             case.d_v, "bf16", 1)
+    d = _layer_dev(case, L, dev)
+    out = torch.empty((case.total_tokens, case.H_v, case.d_v), dtype=torch.bfloat16, device=dev)
+    rows_out = torch.empty_like(d["rows"])
+    stream = torch.cuda.current_stream()
+    cv = (d["conv_w"], case.H_k, case.d_k)
+    dims = gdn._dims_from(d["qkv"], None, out, 0.0, 1e-6, rows_out, (d["ssm_a"], d["ssm_dt"]), cv,
+                          d["z"], d["norm_w"])
+    ws = torch.empty(gdn.workspace_size(dims, 1, case.total_tokens), dtype=torch.uint8, device=dev)
+    call = lambda: gdn.prefill(d["qkv"], None, None, d["a"], d["b"], d["rows"], rows_out, out, d["cu"],
+                               d["slot_in"], d["slot_out"], ws, stream=stream,
+                               gates=(d["ssm_a"], d["ssm_dt"]), conv=cv, z=d["z"], norm_w=d["norm_w"])
+    for _ in range(3):
+        call()
+    t = Timer(stream, reps + 1)
+    torch.cuda.synchronize()
+    t.mark(0)
+    for r in range(reps):
+        call()
+        t.mark(r + 1)
+    torch.cuda.synchronize()
+    ms = statistics.median(t.ms(r, r + 1) for r in range(reps))
+    assert torch.isfinite(out.float()).all()
+    T = case.total_tokens
+    return {"workload": "fused layer prefill: 1 x 4096 tokens, mixed bf16 q|k|v rows -> conv(4) + "
+                        "SiLU, raw gates, gated RMSNorm, bf16 out, Qwen3-Next heads",
+            "ms_per_call": ms, "tokens_s": T / (ms * 1e-3),
+            "operands": "fp32 (the prologue's output is not rounded to bf16)"}
+
+
+def bench_layer_decode(gdn, dev, reps=3):
+    """The fused layer path on the decode workload: 64 sequences x 128
+    steps, one gdn_recurrent_step per step with the prologue (mixed rows,
+    convolution state in the slot rows), raw gates and the epilogue."""
+    dc = gi.config2()
+    S, N = dc.n_steps, dc.n_seqs
+    L = gi.make_layer_inputs(S * N, N, dc.H_k, dc.H_v, dc.d_k, dc.d_v, "bf16", 2)
+    f = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(t)
+    C = L.qkv.shape[1]
+    qkv = f(L.qkv.reshape(S, N, C), torch.bfloat16)
+    z = f(L.z.reshape(S, N, dc.H_v, dc.d_v), torch.bfloat16)
+    rows = f(np.concatenate([L.conv_pool.reshape(N, -1), dc.pool.reshape(N, -1)], axis=1))
+    a, b = f(dc.raw_a), f(dc.raw_b)
+    gates = (f(dc.ssm_a), f(dc.ssm_dt))
+    cv = (f(L.conv_w), dc.H_k, dc.d_k)
+    nw = f(L.norm_w)
+    slots = f(dc.slots, torch.int32)
+    outs = torch.empty((S, N, dc.H_v, dc.d_v), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    per = []
+    for rep in range(reps + 1):
+        t = Timer(stream, 2)
+        torch.cuda.synchronize()
+        t.mark(0)
+        for s in range(S):
+            gdn.decode_step(qkv[s], None, None, a[s], b[s], rows, rows, outs[s], slots, slots,
+                            stream=stream, gates=gates, conv=cv, z=z[s], norm_w=nw)
+        t.mark(1)
+        torch.cuda.synchronize()
+        if rep:
+            per.append(t.ms(0, 1))
+    ms = statistics.median(per)
+    assert torch.isfinite(outs.float()).all()
+    conv_state = N * C * 3 * 4 * 2
+    # state, mixed rows (the q|k|v bytes of the plain step), bf16 out, z, and
+    # the convolution state read and written
+    by = decode_bytes_per_step(dc, out_bytes=2) + N * dc.H_v * dc.d_v * 2 + conv_state
+    gbs = by / (ms / S * 1e-3) / 1e9
+    return {"workload": "fused layer decode: 64 sequences x 128 steps, mixed bf16 rows -> conv(4) "
+                        "+ SiLU, raw gates, gated RMSNorm, bf16 out, state + conv state in slot rows",
+            "ms_per_step": ms / S, "tokens_s": N * S / (ms * 1e-3),
+            "bytes_per_step": by, "achieved_gbs": gbs, "frac": gbs / PEAK_HBM_GBS,
+            "kernels": "decode_kernel + conv_state_kernel"}
+
+
 def bench_varlen(gdn, dev, reps=10):
     case = gi.config3()
     d = to_dev(case, dev)
@@ -333,14 +432,18 @@ def bench_stream(gdn, dev, reps=2):
             "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}
 
 
-def cpu_baseline(case, reps=3):
+def cpu_baseline(case, min_s=10.0, max_reps=40):
+    """The oracle on the whole prefill workload, repeated until about
+    min_s seconds of wall time (at least 3 runs); median per run."""
     import oracle
     threads = oracle.default_threads()
     walls = []
-    for _ in range(reps):
+    t_start = time.perf_counter()
+    while len(walls) < 3 or (time.perf_counter() - t_start < min_s and len(walls) < max_reps):
         t0 = time.perf_counter()
         oracle.run_case(case, threads=threads)
         walls.append(time.perf_counter() - t0)
+    reps = len(walls)
     w = statistics.median(walls)
     return {"value": case.total_tokens / w, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
@@ -356,6 +459,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline prefill + decode only")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="the fused layer prefill and decode only (for kernel traces)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="headline prefill only (for hardware-counter runs)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -372,6 +477,13 @@ def main():
     import gated_deltanet_rule_amd as gdn
     dev = torch.device("cuda:0")
 
+    if args.layer_only:
+        log("fused layer prefill T=4096 ...")
+        lp = bench_layer_prefill(gdn, dev)
+        log("fused layer decode 64x128 ...")
+        ld = bench_layer_decode(gdn, dev)
+        log(f"  {lp['ms_per_call']*1e3:.1f} us/call, {ld['ms_per_step']*1e3:.1f} us/step")
+        return
     if args.copy_mib:
         n = args.copy_mib << 18
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -395,6 +507,12 @@ def main():
     log(f"  {extra['decode_multi']['ms_per_call']*1e3:.1f} us/call, "
         f"{extra['decode_multi']['roofline']['achieved']:.0f} GB/s")
     if not args.quick:
+        log("fused layer prefill T=4096 ...")
+        extra["layer_prefill"] = bench_layer_prefill(gdn, dev)
+        log(f"  {extra['layer_prefill']['ms_per_call']*1e3:.1f} us/call")
+        log("fused layer decode 64x128 ...")
+        extra["layer_decode"] = bench_layer_decode(gdn, dev)
+        log(f"  {extra['layer_decode']['ms_per_step']*1e3:.1f} us/step")
         log("varlen ...")
         extra["varlen"] = bench_varlen(gdn, dev)
         log("stream 65536 ...")

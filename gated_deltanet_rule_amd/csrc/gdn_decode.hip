@@ -113,7 +113,7 @@ __device__ __forceinline__ void gated_norm_row(float o[4], const float zz[4], co
     for (int j = 0; j < 4; ++j) o[j] = o[j] * rn * nw[j] * silu(zz[j]);
 }
 
-template <int DK, int DV, typename E, typename OT>
+template <int DK, int DV, typename E, typename OT, bool FUSED>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(RecParams P)
 {
     constexpr int CG = DV / 4;                  // float4 column groups
@@ -131,8 +131,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(RecParams P)
     const E *q = static_cast<const E *>(P.q);
     const E *k = static_cast<const E *>(P.k);
     const E *v = static_cast<const E *>(P.v);
-    const bool conv = P.conv_w != nullptr;
-    const bool norm = P.z != nullptr;
+    const bool conv = FUSED && P.conv_w != nullptr;
+    const bool norm = FUSED && P.z != nullptr;
 
     __shared__ float sk[DK];
     __shared__ float sq[DK];
@@ -269,8 +269,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(RecParams P)
 // while the current one is processed; k, q and the reduction partials
 // alternate between two LDS buffers, so a token needs two barriers.  With the
 // prologue, each thread keeps the convolution window of its channels in
-// registers from token to token.  FUSED: prologue and/or epilogue present
-// (their registers would otherwise cost the plain kernel occupancy).
+// registers from token to token.  FUSED (here and in decode_kernel):
+// prologue and/or epilogue present; the plain instantiation carries none of
+// their code or registers.
 template <int DK, int DV, typename E, typename OT, bool FUSED>
 __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(RecParams P)
 {
@@ -478,7 +479,12 @@ hipError_t launch_t(const Problem &p, const DecodeArgs &a, hipStream_t st)
 {
     const RecParams P = rec_params(p, a.q, a.k, a.v, a.g, a.beta, a.state_in, a.state_out, a.out,
                                    nullptr, a.slot_in, a.slot_out, a.n_seqs, a.conv_in);
-    hipLaunchKernelGGL((decode_kernel<DK, DV, E, OT>), dim3(a.n_seqs, p.H_v), dim3(kDecodeThreads), 0, st, P);
+    if (p.conv_w || p.z)
+        hipLaunchKernelGGL((decode_kernel<DK, DV, E, OT, true>), dim3(a.n_seqs, p.H_v), dim3(kDecodeThreads), 0,
+                           st, P);
+    else
+        hipLaunchKernelGGL((decode_kernel<DK, DV, E, OT, false>), dim3(a.n_seqs, p.H_v), dim3(kDecodeThreads), 0,
+                           st, P);
     return hipGetLastError();
 }
 
