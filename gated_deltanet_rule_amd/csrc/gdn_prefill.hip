@@ -60,9 +60,10 @@ struct ChunkEntry {
 // workspace geometry
 //
 // per (chunk, value head), in 1 KiB units:
-//   W fragments (4 x NKD) | P hi (4 x NKC) | [P lo (4 x NKC)] | scalars | U0 tiles (4 x NCT)
+//   W fragments (4 x NKD) | [W lo (4 x NKD)] | P hi (4 x NKC) | [P lo (4 x NKC)] | scalars | U0 tiles (4 x NCT)
 // per (chunk, key head):
-//   q fragments (4 x NKD) | k^T fragments (NMT x NKC)
+//   q fragments (4 x NKD) | [q lo (4 x NKD)] | k^T fragments (NMT x NKC) | [k^T lo (NMT x NKC)]
+// (the lo parts exist when q and k are two-term operands, see prep_kernel)
 // A fragment is a 16-row x KB-deep MFMA operand, 64 lanes x 16 bytes.  The
 // scalars are qs[64] (q scale * e^{G_r}), ks[64] (e^{G_n - G_r} / |k_r|), gn,
 // and the chunk's first token and length (int bits).  U0 tiles are stored
@@ -70,30 +71,32 @@ struct ChunkEntry {
 // --------------------------------------------------------------------------
 __host__ __device__ constexpr int kb_of(bool bf16) { return bf16 ? 32 : 16; }
 __host__ __device__ constexpr int ns_of(bool bf16) { return bf16 ? 2 : 1; }
-__host__ __device__ constexpr int vshared_kib(int dk, bool bf16) {
-    return 4 * (dk / kb_of(bf16)) + ns_of(bf16) * 4 * (C / kb_of(bf16)) + 1;
+__host__ __device__ constexpr int vshared_kib(int dk, bool bf16, bool si) {
+    return (si ? 2 : 1) * 4 * (dk / kb_of(bf16)) + ns_of(bf16) * 4 * (C / kb_of(bf16)) + 1;
 }
-__host__ __device__ constexpr int vblk_kib(int dk, int dv, bool bf16) {
-    return vshared_kib(dk, bf16) + 4 * (dv / 16);
+__host__ __device__ constexpr int vblk_kib(int dk, int dv, bool bf16, bool si) {
+    return vshared_kib(dk, bf16, si) + 4 * (dv / 16);
 }
-__host__ __device__ constexpr int kblk_kib(int dk, bool bf16) {
-    return 4 * (dk / kb_of(bf16)) + (dk / 16) * (C / kb_of(bf16));
+__host__ __device__ constexpr int kblk_kib(int dk, bool bf16, bool si) {
+    return (si ? 2 : 1) * (4 * (dk / kb_of(bf16)) + (dk / 16) * (C / kb_of(bf16)));
 }
 
-template <int DK, int DV, typename E> struct Geo {
+// SI: q and k enter the scan as two-term (hi + lo) bf16 operands
+template <int DK, int DV, typename E, bool SI = false> struct Geo {
     using M = Mfma<E>;
     static constexpr bool BF = sizeof(E) == 2;
     static constexpr int KB = M::KB, TPB = M::TPB, NS = Split<E>::N;
     static constexpr int NKD = DK / KB, NKC = C / KB, NMT = DK / 16, NCT = DV / 16;
     static constexpr int NWF = 4 * NKD, NPF = 4 * NKC, NQF = 4 * NKD, NKF = NMT * NKC;
-    static constexpr int F_W = 0, F_PH = NWF, F_PL = NWF + NPF, F_SCAL = NWF + NS * NPF;
+    static constexpr int NQS = SI ? 2 : 1;
+    static constexpr int F_W = 0, F_WL = NWF, F_PH = NQS * NWF, F_PL = F_PH + NPF, F_SCAL = F_PH + NS * NPF;
     static constexpr int SV = F_SCAL + 1;                 // shared part of the value-head block
     static constexpr int F_U0 = SV;
     static constexpr int VBLK = SV + 4 * NCT;
-    static constexpr int F_Q = 0, F_KT = NQF;
-    static constexpr int KBLK = NQF + NKF;
-    static constexpr int A_Q = SV, A_KT = SV + NQF, SA = SV + KBLK;   // scan LDS copy
-    static_assert(VBLK == vblk_kib(DK, DV, BF) && KBLK == kblk_kib(DK, BF), "geometry");
+    static constexpr int F_Q = 0, F_QL = NQF, F_KT = NQS * NQF, F_KTL = F_KT + NKF;
+    static constexpr int KBLK = NQS * (NQF + NKF);
+    static_assert(!SI || BF, "two-term q and k are bf16 operands");
+    static_assert(VBLK == vblk_kib(DK, DV, BF, SI) && KBLK == kblk_kib(DK, BF, SI), "geometry");
 };
 
 struct WsLayout {
@@ -107,9 +110,11 @@ bool stage_o(const Problem &p) { return p.z && p.out_bf16; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Operand type of the chunked form: bf16 for bf16 inputs, except with the
-// convolution prologue, whose output keeps fp32 (see prep_kernel).
-bool op_bf16(const Problem &p) { return p.bf16 && !p.conv_w; }
+// Operand type of the chunked form: that of the inputs.  With the
+// convolution prologue and bf16 rows, q, k, v become two-term bf16 operands
+// (see prep_kernel).
+bool op_bf16(const Problem &p) { return p.bf16 != 0; }
+bool op_split(const Problem &p) { return p.bf16 && p.conv_w; }
 
 WsLayout ws_layout(const Problem &p, int32_t n_seqs, int64_t T)
 {
@@ -119,8 +124,8 @@ WsLayout ws_layout(const Problem &p, int32_t n_seqs, int64_t T)
     L.entries = 256;
     L.cstart = align256(L.entries + sizeof(ChunkEntry) * (size_t)L.max_chunks);
     L.vblocks = align256(L.cstart + sizeof(int32_t) * ((size_t)n_seqs + 1));
-    L.vblk = (size_t)vblk_kib(p.d_k, p.d_v, bf) * 1024;
-    L.kblk = (size_t)kblk_kib(p.d_k, bf) * 1024;
+    L.vblk = (size_t)vblk_kib(p.d_k, p.d_v, bf, op_split(p)) * 1024;
+    L.kblk = (size_t)kblk_kib(p.d_k, bf, op_split(p)) * 1024;
     L.kblocks = L.vblocks + L.vblk * (size_t)L.max_chunks * p.H_v;
     L.obuf = align256(L.kblocks + L.kblk * (size_t)L.max_chunks * p.H_k);
     L.total = L.obuf + (stage_o(p) ? sizeof(float) * (size_t)T * p.H_v * p.d_v : 0);
@@ -332,7 +337,8 @@ struct PrepParams {
 // LDS of the preparation kernel.  Rows are padded so that the row stride is
 // 8 banks (mod 64): the transposed reads (4 rows x 32 bytes per 16 lanes) and
 // the row reads of 16 different rows then hit distinct banks.
-template <int DK, int DV, typename E> struct PrepLds {
+// SI: the lo parts of two-term K and Q / V rows follow.
+template <int DK, int DV, typename E, bool SI = false> struct PrepLds {
     static constexpr int PAD = sizeof(E) == 2 ? 16 : 4;
     static constexpr int LDK = DK + PAD;                  // K rows
     static constexpr int DX = DK > DV ? DK : DV;
@@ -345,7 +351,9 @@ template <int DK, int DV, typename E> struct PrepLds {
     static constexpr size_t OFF_G = OFF_T + (size_t)C * LDA * sizeof(float);
     static constexpr int NH = 4;                          // value heads whose row scalars are held at once
     static constexpr size_t OFF_S = OFF_G + NH * C * sizeof(double);
-    static constexpr size_t BYTES = OFF_S + (2 + 3 * NH) * C * sizeof(float);
+    static constexpr size_t OFF_KL = OFF_S + (2 + 3 * NH) * C * sizeof(float);
+    static constexpr size_t OFF_XL = OFF_KL + (SI ? (size_t)C * LDK * sizeof(E) : 0);
+    static constexpr size_t BYTES = OFF_XL + (SI ? (size_t)C * LDX * sizeof(E) : 0);
 };
 
 // --------------------------------------------------------------------------
@@ -357,64 +365,90 @@ __device__ __forceinline__ float conv_silu4(float4 w, float x0, float x1, float 
     return silu(w.x * x0 + w.y * x1 + w.z * x2 + w.w * x3);
 }
 
-// Four consecutive input elements (the prologue's column vector): 8 bytes of
-// bf16 or 16 bytes of fp32, kept packed until used.
-template <typename In> struct In4;
-template <> struct In4<bf16_t> {
-    typedef uint2 T;
-    __device__ static __forceinline__ float4 f(uint2 u) {
-        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+// The VEC values of a 16-byte vector as fp32, and back (rounded to E).
+template <typename E> __device__ __forceinline__ void unpack16(u32x4 u, float *f);
+template <> __device__ __forceinline__ void unpack16<bf16_t>(u32x4 u, float *f) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = __uint_as_float(u[e] << 16);
+        f[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
     }
-};
-template <> struct In4<float> {
-    typedef float4 T;
-    __device__ static __forceinline__ float4 f(float4 u) { return u; }
-};
+}
+template <> __device__ __forceinline__ void unpack16<float>(u32x4 u, float *f) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(u[e]);
+}
+template <typename E> __device__ __forceinline__ u32x4 pack16(const float *f);
+template <> __device__ __forceinline__ u32x4 pack16<bf16_t>(const float *f) {
+    return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                 pack_bf16x2(f[6], f[7])};
+}
+template <> __device__ __forceinline__ u32x4 pack16<float>(const float *f) {
+    return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+}
 
-// silu(conv) of NR consecutive rows row0.. of four channels, from x[0 .. NR+2]
-// holding rows row0-3 .. row0+NR-1 (fp32); rows before the chunk (negative)
-// are taken from the LDS history hist[m][.] (m = row + 3) at column offset
-// hoff.  Results (fp32 operands) are zero from row `len` on.
-template <int NR>
-__device__ __forceinline__ void conv_rows(const float4 *x, const float4 *w, int row0, int len, const float *hist,
-                                          int hld, int hoff, u32x4 *out)
+// silu(conv) of NR consecutive rows row0.. of one 16-byte column vector (VEC
+// channels), from raw[0 .. NR+2] holding rows row0-3 .. row0+NR-1; rows
+// before the chunk (negative) come from the LDS history hist[m][.] (m = row +
+// 3, fp32) at column offset hoff, the taps from w[e] (channel e).  Results are
+// zero from row `len` on; with a lo array they are stored two-term (hi =
+// rounded to E, lo = the remainder rounded to E), else rounded once.
+template <typename E, int NR>
+__device__ __forceinline__ void conv_rows(const u32x4 *raw, const float4 *w, int row0, int len, const float *hist,
+                                          int hld, int hoff, u32x4 *hi, u32x4 *lo)
 {
+    constexpr int VEC = 16 / (int)sizeof(E);
 #pragma unroll
     for (int p = 0; p < NR; ++p) {
-        float4 xr[4];
+        float x[4][VEC];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            xr[j] = x[p + j];
-            if (row0 - 3 + p + j < 0) xr[j] = *reinterpret_cast<const float4 *>(hist + (row0 + p + j) * hld + hoff);
+            unpack16<E>(raw[p + j], x[j]);
+            if (row0 - 3 + p + j < 0) {
+                const float *hp = hist + (row0 + p + j) * hld + hoff;
+#pragma unroll
+                for (int e = 0; e < VEC; e += 4) {
+                    const float4 h4 = *reinterpret_cast<const float4 *>(hp + e);
+                    x[j][e] = h4.x; x[j][e + 1] = h4.y; x[j][e + 2] = h4.z; x[j][e + 3] = h4.w;
+                }
+            }
         }
-        const float4 y = make_float4(conv_silu4(w[0], xr[0].x, xr[1].x, xr[2].x, xr[3].x),
-                                     conv_silu4(w[1], xr[0].y, xr[1].y, xr[2].y, xr[3].y),
-                                     conv_silu4(w[2], xr[0].z, xr[1].z, xr[2].z, xr[3].z),
-                                     conv_silu4(w[3], xr[0].w, xr[1].w, xr[2].w, xr[3].w));
-        out[p] = row0 + p < len ? __builtin_bit_cast(u32x4, y) : u32x4{0u, 0u, 0u, 0u};
+        float y[VEC], r[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) y[e] = conv_silu4(w[e], x[0][e], x[1][e], x[2][e], x[3][e]);
+        const bool live = row0 + p < len;
+        const u32x4 h = pack16<E>(y);
+        hi[p] = live ? h : u32x4{0u, 0u, 0u, 0u};
+        if (lo) {
+            float hf[VEC];
+            unpack16<E>(h, hf);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) r[e] = y[e] - hf[e];
+            lo[p] = live ? pack16<E>(r) : u32x4{0u, 0u, 0u, 0u};
+        }
     }
 }
 
 // CONV: the convolution prologue (build_layer_attn_linear_core on the page
 // "ik_llama.cpp src/llama-delta-net.cpp": ggml_ssm_conv + ggml_silu) is formed
-// while the rows are loaded, from input rows of type In.  A thread then owns
-// KL (VL) consecutive rows of one four-channel column vector; the three rows
-// before a thread's first are read back from LDS (or, for K and Q, loaded
-// too), and the three rows before the chunk (the slot's convolution state
-// for a sequence's first chunk, else the preceding rows) are staged through
-// LDS.  The operands stay fp32 (E = float): after SiLU the keys of
-// neighbouring tokens are correlated, and rounding q, k, v to bf16 would cost
-// the solve and the read-out several percent of the output's rms.
-template <int DK, int DV, typename E, bool CONV, typename In>
-__global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepParams pp)
+// while the rows are loaded.  A thread then owns KL (VL) consecutive rows of
+// one 16-byte column vector; the three rows before a thread's first are
+// loaded too (K, Q) or read back from LDS (V), and the three rows before the
+// chunk (the slot's convolution state for a sequence's first chunk, else the
+// preceding rows) are staged through LDS with the taps of V.  After SiLU the
+// keys of neighbouring tokens are correlated and a single bf16 rounding of q,
+// k or v moves the result by several percent of its rms, so with bf16 rows
+// the convolution output becomes two-term bf16 operands (SI: hi + lo, about
+// 16 significant bits) in every product that reads q, k or v, and with fp32
+// rows the operands stay fp32.
+template <int DK, int DV, typename E, bool CONV>
+__global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_kernel(PrepParams pp)
 {
-    static_assert(!CONV || sizeof(E) == 4, "the prologue runs on fp32 operands");
-    using IV = typename In4<In>::T;
+    constexpr bool SI = CONV && sizeof(E) == 2;
     using M = Mfma<E>;
     using SP = Split<E>;
-    using G = Geo<DK, DV, E>;
-    using L = PrepLds<DK, DV, E>;
+    using G = Geo<DK, DV, E, SI>;
+    using L = PrepLds<DK, DV, E, SI>;
     using TR = TrLoad<E>;
     using Frag = typename M::Frag;
     constexpr int KB = M::KB, TPB = M::TPB, NS = SP::N;
@@ -429,6 +463,8 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
     E *sX = reinterpret_cast<E *>(smem + L::OFF_X);
     float *sA = reinterpret_cast<float *>(smem + L::OFF_A);
     float *sT = reinterpret_cast<float *>(smem + L::OFF_T);
+    E *sKL = reinterpret_cast<E *>(smem + L::OFF_KL);           // SI: lo parts of K
+    E *sXL = reinterpret_cast<E *>(smem + L::OFF_XL);           //     and of Q / V
     constexpr int NH = L::NH;
     double *sGh = reinterpret_cast<double *>(smem + L::OFF_G);  // [NH][C] G_r = cumsum of g
     float *sRK = reinterpret_cast<float *>(smem + L::OFF_S);    // 1 / |k_r|
@@ -460,9 +496,6 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
     const E *qg = static_cast<const E *>(pp.q);
     const E *kg = static_cast<const E *>(pp.k);
     const E *vg = static_cast<const E *>(pp.v);
-    const In *qi = static_cast<const In *>(pp.q);     // the prologue's input rows
-    const In *ki = static_cast<const In *>(pp.k);
-    const In *vi_ = static_cast<const In *>(pp.v);
     const int ratio = pp.H_v / pp.H_k;
 
     // g and beta of up to NH value heads (wave w: head j0 + w, lane: row)
@@ -529,8 +562,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
     constexpr int VL = (C * VPRV + 255) / 256;
     constexpr int NHV = CONV ? (3 * DV + 255) / 256 : 1;
     constexpr int NWV = CONV ? (4 * DV + 255) / 256 : 1;
-    u32x4 vpre[CONV ? 1 : VL];
-    IV vraw[CONV ? VL : 1];
+    u32x4 vpre[VL];
     float vh[NHV], vw[NWV];
     const int vrow0 = (tid / VPRV) * VL, vcv = tid % VPRV;
     static_assert(C * VPRV % 256 == 0 && C * VPR % 256 == 0, "whole vectors per thread");
@@ -548,13 +580,13 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
 #pragma unroll
             for (int p = 0; p < VL; ++p) {
                 const int rr = min(vrow0 + p, len - 1);
-                vraw[p] = *reinterpret_cast<const IV *>(vi_ + (size_t)(t0 + rr) * pp.rs_v + (size_t)hh * DV + vcv * VEC);
+                vpre[p] = *reinterpret_cast<const u32x4 *>(vg + (size_t)(t0 + rr) * pp.rs_v + (size_t)hh * DV + vcv * VEC);
             }
 #pragma unroll
             for (int j = 0; j < NHV; ++j) {
                 const int idx = min(tid + 256 * j, 3 * DV - 1);
                 const int m = idx / DV, c = idx % DV;
-                const float xr = to_f32(vi_[(size_t)max(t0 - 3 + m, 0) * pp.rs_v + (size_t)hh * DV + c]);
+                const float xr = to_f32(vg[(size_t)max(t0 - 3 + m, 0) * pp.rs_v + (size_t)hh * DV + c]);
                 const float xs = pp.conv_in[(size_t)cslot * pp.slot_stride + (vch0 + (size_t)hh * DV + c) * 3 + m];
                 vh[j] = first ? (state_ok ? xs : 0.f) : xr;
             }
@@ -571,8 +603,8 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
     constexpr int KR = CONV ? KL + 3 : KL;
     constexpr int NHK = CONV ? (6 * DK + 255) / 256 : 1;
     const int krow0 = (tid / VPR) * KL, kcv = tid % VPR;
-    u32x4 kx[KL], qx[KL];
-    IV kraw[CONV ? KR : 1], qraw[CONV ? KR : 1];
+    u32x4 kx[KL], qx[KL], kxl[SI ? KL : 1], qxl[SI ? KL : 1];
+    u32x4 kraw[CONV ? KR : 1], qraw[CONV ? KR : 1];
     float hk[NHK];
     float4 wk[CONV ? VEC : 1], wq[CONV ? VEC : 1];
     if constexpr (!CONV) {
@@ -589,8 +621,8 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
         for (int u = 0; u < KR; ++u) {
             const int rr = min(max(krow0 - 3 + u, 0), len - 1);
             const size_t off = (size_t)(t0 + rr) * pp.rs_qk + (size_t)kh * DK + (size_t)kcv * VEC;
-            kraw[u] = *reinterpret_cast<const IV *>(ki + off);
-            qraw[u] = *reinterpret_cast<const IV *>(qi + off);
+            kraw[u] = *reinterpret_cast<const u32x4 *>(kg + off);
+            qraw[u] = *reinterpret_cast<const u32x4 *>(qg + off);
         }
         // three history rows of the key head's q and k channels, [m][q | k]
 #pragma unroll
@@ -599,7 +631,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
             const int m = idx / (2 * DK), c2 = idx % (2 * DK);
             const bool isk = c2 >= DK;
             const int c = isk ? c2 - DK : c2;
-            const float xr = to_f32((isk ? ki : qi)[(size_t)max(t0 - 3 + m, 0) * pp.rs_qk + (size_t)kh * DK + c]);
+            const float xr = to_f32((isk ? kg : qg)[(size_t)max(t0 - 3 + m, 0) * pp.rs_qk + (size_t)kh * DK + c]);
             const size_t ch = (isk ? (size_t)pp.H_k * DK : 0) + (size_t)kh * DK + c;
             const float xs = pp.conv_in[(size_t)cslot * pp.slot_stride + ch * 3 + m];
             hk[j] = first ? (state_ok ? xs : 0.f) : xr;
@@ -623,14 +655,8 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
         for (int j = 0; j < NHK; ++j)
             if (tid + 256 * j < 6 * DK) sA[tid + 256 * j] = hk[j];
         lds_sync();
-        float4 xk[KR], xq[KR];
-#pragma unroll
-        for (int u = 0; u < KR; ++u) {
-            xk[u] = In4<In>::f(kraw[u]);
-            xq[u] = In4<In>::f(qraw[u]);
-        }
-        conv_rows<KL>(xk, wk, krow0, len, sA, 2 * DK, DK + kcv * VEC, kx);
-        conv_rows<KL>(xq, wq, krow0, len, sA, 2 * DK, kcv * VEC, qx);
+        conv_rows<E, KL>(kraw, wk, krow0, len, sA, 2 * DK, DK + kcv * VEC, kx, SI ? kxl : nullptr);
+        conv_rows<E, KL>(qraw, wq, krow0, len, sA, 2 * DK, kcv * VEC, qx, SI ? qxl : nullptr);
     }
 #pragma unroll
     for (int p = 0; p < KL; ++p) {
@@ -640,7 +666,27 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
         const u32x4 qv = r < len ? qx[p] : u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4 *>(sK + r * LDK + cv * VEC) = kv;
         *reinterpret_cast<u32x4 *>(sX + r * LDX + cv * VEC) = qv;
-        float k2 = sumsq16<E>(kv), q2 = sumsq16<E>(qv);
+        float k2, q2;
+        if constexpr (SI) {
+            // norms of the two-term rows (hi + lo), already zero past the end
+            *reinterpret_cast<u32x4 *>(sKL + r * LDK + cv * VEC) = kxl[p];
+            *reinterpret_cast<u32x4 *>(sXL + r * LDX + cv * VEC) = qxl[p];
+            float a[VEC], b[VEC], c[VEC], d[VEC];
+            unpack16<E>(kv, a);
+            unpack16<E>(kxl[p], b);
+            unpack16<E>(qv, c);
+            unpack16<E>(qxl[p], d);
+            k2 = 0.f;
+            q2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                k2 += (a[e] + b[e]) * (a[e] + b[e]);
+                q2 += (c[e] + d[e]) * (c[e] + d[e]);
+            }
+        } else {
+            k2 = sumsq16<E>(kv);
+            q2 = sumsq16<E>(qv);
+        }
 #pragma unroll
         for (int off = VPR / 2; off >= 1; off >>= 1) {
             k2 += __shfl_xor(k2, off, 64);
@@ -660,10 +706,14 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
         for (int f = w; f < G::NQF; f += 4) {
             const int rt = f / NKD, kb = f % NKD;
             store_frag<E>(kb_blk + G::F_Q * 1024, f, lane, M::load_rm(sX + (16 * rt + n) * LDX, kb * KB, qd));
+            if constexpr (SI)
+                store_frag<E>(kb_blk + G::F_QL * 1024, f, lane, M::load_rm(sXL + (16 * rt + n) * LDX, kb * KB, qd));
         }
         for (int f = w; f < G::NKF; f += 4) {
             const int mt = f / NKC, kc = f % NKC;
             store_frag<E>(kb_blk + G::F_KT * 1024, f, lane, TR::frag(sK, LDK, kc * KB, 16 * mt, lane));
+            if constexpr (SI)
+                store_frag<E>(kb_blk + G::F_KTL * 1024, f, lane, TR::frag(sKL, LDK, kc * KB, 16 * mt, lane));
         }
     }
 
@@ -676,11 +726,20 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
         const int it = w + 4 * s;
         const int pr = it < 10 ? it : it - 10;
         const int rt = low_r(pr), ct = low_c(pr);
-        const E *ra = sK + (16 * (it < 10 ? rt : ct) + n) * LDK;
-        const E *rb = it < 10 ? sK + (16 * ct + n) * LDK : sX + (16 * rt + n) * LDX;
+        const int ka = (16 * (it < 10 ? rt : ct) + n) * LDK;
+        const int kbo = it < 10 ? (16 * ct + n) * LDK : (16 * rt + n) * LDX;
+        const E *ra = sK + ka;
+        const E *rb = (it < 10 ? sK : sX) + kbo;
 #pragma unroll
-        for (int kb = 0; kb < NKD; ++kb)
-            M::mma(acc[s], M::load_rm(ra, kb * KB, qd), M::load_rm(rb, kb * KB, qd));
+        for (int kb = 0; kb < NKD; ++kb) {
+            const Frag fa = M::load_rm(ra, kb * KB, qd), fb = M::load_rm(rb, kb * KB, qd);
+            M::mma(acc[s], fa, fb);
+            if constexpr (SI) {
+                // (a_h + a_l)(b_h + b_l) without the lo x lo term
+                M::mma(acc[s], M::load_rm(sKL + ka, kb * KB, qd), fb);
+                M::mma(acc[s], fa, M::load_rm((it < 10 ? sKL : sXL) + kbo, kb * KB, qd));
+            }
+        }
     }
     lds_sync();   // Q is dead: sX holds V from here on
 
@@ -688,6 +747,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
         const int h = kh * ratio + jv;
         char *blk = pp.vblocks + ((size_t)chunk * pp.H_v + h) * ((size_t)G::VBLK * 1024);
         char *Wf = blk + G::F_W * 1024;
+        char *Wlf = blk + G::F_WL * 1024;
         char *Pf = blk + G::F_PH * 1024;
         char *Plf = blk + G::F_PL * 1024;
         char *U0f = blk + G::F_U0 * 1024;
@@ -708,11 +768,11 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
             // (free here); then each thread takes its rows and the three
             // before them, and after a second barrier writes the prologue's
             // result over the raw rows
-            float4 xv[VL + 3];
+            u32x4 xv[VL + 3];
 #pragma unroll
             for (int p = 0; p < VL; ++p) {
-                xv[p + 3] = In4<In>::f(vraw[p]);
-                *reinterpret_cast<float4 *>(sX + (vrow0 + p) * LDX + vcv * VEC) = xv[p + 3];
+                xv[p + 3] = vpre[p];
+                *reinterpret_cast<u32x4 *>(sX + (vrow0 + p) * LDX + vcv * VEC) = vpre[p];
             }
 #pragma unroll
             for (int j = 0; j < NHV; ++j)
@@ -723,14 +783,16 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
             lds_sync();
 #pragma unroll
             for (int u = 0; u < 3; ++u)
-                xv[u] = *reinterpret_cast<const float4 *>(sX + max(vrow0 - 3 + u, 0) * LDX + vcv * VEC);
-            u32x4 res[VL];
-            conv_rows<VL>(xv, reinterpret_cast<const float4 *>(sA + 3 * DV) + vcv * VEC, vrow0, len, sA, DV,
-                          vcv * VEC, res);
+                xv[u] = *reinterpret_cast<const u32x4 *>(sX + max(vrow0 - 3 + u, 0) * LDX + vcv * VEC);
+            u32x4 res[VL], resl[SI ? VL : 1];
+            conv_rows<E, VL>(xv, reinterpret_cast<const float4 *>(sA + 3 * DV) + vcv * VEC, vrow0, len, sA, DV,
+                             vcv * VEC, res, SI ? resl : nullptr);
             lds_sync();
 #pragma unroll
-            for (int p = 0; p < VL; ++p)
+            for (int p = 0; p < VL; ++p) {
                 *reinterpret_cast<u32x4 *>(sX + (vrow0 + p) * LDX + vcv * VEC) = res[p];
+                if constexpr (SI) *reinterpret_cast<u32x4 *>(sXL + (vrow0 + p) * LDX + vcv * VEC) = resl[p];
+            }
         }
         load_v(kh * ratio + min(jv + 1, ratio - 1));   // next head (the last reloads itself)
         if (jv > 0 && hs == 0) {
@@ -865,8 +927,12 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
                     const Frag a = TR::frag(sK, LDK, kb * KB, 16 * dt, lane);
                     M::mma(a4, a, bh[kb]);
                     if constexpr (NS == 2) M::mma(a4, a, bl[kb]);
+                    if constexpr (SI) M::mma(a4, TR::frag(sKL, LDK, kb * KB, 16 * dt, lane), bh[kb]);
                 }
-                store_quarter<E>(Wf, tt * NKD + dt / TPB, lane, dt % TPB, a4);
+                if constexpr (SI)
+                    store_quarter2<E>(Wf, Wlf, tt * NKD + dt / TPB, lane, dt % TPB, a4);
+                else
+                    store_quarter<E>(Wf, tt * NKD + dt / TPB, lane, dt % TPB, a4);
             }
         }
         {
@@ -885,6 +951,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prep_kernel(PrepP
                     const Frag b = TR::frag(sX, LDX, kb * KB, 16 * ct, lane);
                     M::mma(a4, ah[kb], b);
                     if constexpr (NS == 2) M::mma(a4, al[kb], b);
+                    if constexpr (SI) M::mma(a4, ah[kb], TR::frag(sXL, LDX, kb * KB, 16 * ct, lane));
                 }
                 *(reinterpret_cast<floatx4 *>(U0f) + (size_t)(ct * 4 + rt) * 64 + lane) = a4;
             }
@@ -910,7 +977,7 @@ struct ScanParams {
 };
 
 template <int DK, int DV, int CT, typename E> struct ScanLds {
-    using G = Geo<DK, DV, E>;
+    using G = Geo<DK, DV, E>;      // (the q/k split does not change the exchange)
     // exchange only, per column tile: the state as two-term B fragments per
     // dk block, and the chunk deltas U and ks*U as two-term B fragments per
     // token block (each 1 KiB = 64 lanes x 16 bytes)
@@ -952,12 +1019,12 @@ template <> struct TileOut<float> {
 // registers of the wave that uses it, re-issued for the next chunk right
 // after its last use in this one, so its latency overlaps a chunk of work;
 // LDS carries only the per-chunk exchange (state and delta fragments).
-template <int DK, int DV, int CT, typename E, typename OT>
+template <int DK, int DV, int CT, typename E, typename OT, bool SI>
 __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
 {
     using M = Mfma<E>;
     using SP = Split<E>;
-    using G = Geo<DK, DV, E>;
+    using G = Geo<DK, DV, E, SI>;
     using L = ScanLds<DK, DV, CT, E>;
     using Frag = typename M::Frag;
     constexpr int KB = M::KB, TPB = M::TPB, NS = SP::N;
@@ -1032,11 +1099,17 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
     // operands of the current chunk (loaded for chunk cs before the loop,
     // reloaded for the next chunk right after their last use)
     const int c0 = cs < ce ? cs : 0;
+    // SI: q and k^T also as lo parts (two-term operands)
     Frag Wf[NKD], Qf[NKD], Ph[NKC], Pl[NKC], Kf[NOWN * TPB][NKC];
+    Frag Wlf[SI ? NKD : 1], Qlf[SI ? NKD : 1], Klf[SI ? NOWN * TPB : 1][NKC];
 #pragma unroll
     for (int kb = 0; kb < NKD; ++kb) {
         Wf[kb] = vfrag(c0, G::F_W + rt * NKD + kb);
         Qf[kb] = kfrag(c0, G::F_Q + rt * NKD + kb);
+        if constexpr (SI) {
+            Wlf[kb] = vfrag(c0, G::F_WL + rt * NKD + kb);
+            Qlf[kb] = kfrag(c0, G::F_QL + rt * NKD + kb);
+        }
     }
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
@@ -1049,7 +1122,10 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
         for (int t = 0; t < TPB; ++t) {
             const int mt = min(rt + 4 * o, NKD - 1) * TPB + t;
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) Kf[o * TPB + t][kc] = kfrag(c0, G::F_KT + mt * NKC + kc);
+            for (int kc = 0; kc < NKC; ++kc) {
+                Kf[o * TPB + t][kc] = kfrag(c0, G::F_KT + mt * NKC + kc);
+                if constexpr (SI) Klf[o * TPB + t][kc] = kfrag(c0, G::F_KTL + mt * NKC + kc);
+            }
         }
     floatx4 u0 = __builtin_bit_cast(floatx4, vblk(c0)[u0f * 64 + lane]);
     floatx4 qs4 = scal4(c0, ro), ks4 = scal4(c0, 64 + ro);
@@ -1085,6 +1161,12 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
             M::mma(OQh, Qf[kb], sh);
             if constexpr (NS == 2) M::mma(OQl, Qf[kb], sl);
             Qf[kb] = kfrag(cn, G::F_Q + rt * NKD + kb);
+            if constexpr (SI) {
+                M::mma(WSl, Wlf[kb], sh);
+                Wlf[kb] = vfrag(cn, G::F_WL + rt * NKD + kb);
+                M::mma(OQl, Qlf[kb], sh);
+                Qlf[kb] = kfrag(cn, G::F_QL + rt * NKD + kb);
+            }
         }
         const floatx4 U = u0 - (WSh + WSl);
         const floatx4 Oi = (OQh + OQl) * qs4;
@@ -1098,10 +1180,24 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
             TileOut<E>::put(myKf + (kc * NS) * 64, myKf + (kc * NS + NS - 1) * 64, lane, part, Uk);
         }
         // region order: matrix-core op, load, alternately
+        if constexpr (SI) {
 #pragma unroll
-        for (int q = 0; q < 2 * NKD; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            for (int q = 0; q < NKD; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 2 * NKD; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
         }
         lds_sync();
 
@@ -1157,6 +1253,10 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
                         M::mma(Sa[t], Kf[o * TPB + t][kc], kh_[kc]);
                         if constexpr (NS == 2) M::mma(Sb[t], Kf[o * TPB + t][kc], kl_[kc]);
                         Kf[o * TPB + t][kc] = kfrag(cn, G::F_KT + ((rt + 4 * o) * TPB + t) * NKC + kc);
+                        if constexpr (SI) {
+                            M::mma(Sb[t], Klf[o * TPB + t][kc], kh_[kc]);
+                            Klf[o * TPB + t][kc] = kfrag(cn, G::F_KTL + ((rt + 4 * o) * TPB + t) * NKC + kc);
+                        }
                     }
 #pragma unroll
                 for (int t = 0; t < TPB; ++t) {
@@ -1168,7 +1268,7 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
         gn = scal1(cn, 128);
         // region order: matrix-core op, load, alternately
 #pragma unroll
-        for (int q = 0; q < 12; ++q) {
+        for (int q = 0; q < (SI ? 16 : 12); ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
@@ -1246,31 +1346,24 @@ hipError_t prepare_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
                   p.rs_qk, p.rs_v, p.conv_w,
                   // without a state pool the history loads read the taps (unused)
                   a.conv_in ? a.conv_in : p.conv_w, a.slot_in, p.slot_stride, a.conv_in != nullptr};
-    constexpr size_t lds = PrepLds<DK, DV, E>::BYTES;
     const int chunks = single ? (int)((a.total_tokens + C - 1) / C) : w.L.max_chunks;
     const dim3 grid(chunks, p.H_k);
-    if constexpr (sizeof(E) == 4) {
-        if (p.conv_w) {
-            // the prologue runs on fp32 operands whatever the input rows are
-            if (p.bf16) {
-                e = set_lds(prep_kernel<DK, DV, float, true, bf16_t>, lds);
-                if (e == hipSuccess)
-                    hipLaunchKernelGGL((prep_kernel<DK, DV, float, true, bf16_t>), grid, dim3(256), lds, st, pp);
-            } else {
-                e = set_lds(prep_kernel<DK, DV, float, true, float>, lds);
-                if (e == hipSuccess)
-                    hipLaunchKernelGGL((prep_kernel<DK, DV, float, true, float>), grid, dim3(256), lds, st, pp);
-            }
-            return e != hipSuccess ? e : hipGetLastError();
-        }
+    if (p.conv_w) {
+        // bf16 rows: two-term bf16 operands (SI); fp32 rows: fp32 operands
+        constexpr size_t lds = PrepLds<DK, DV, E, sizeof(E) == 2>::BYTES;
+        e = set_lds(prep_kernel<DK, DV, E, true>, lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((prep_kernel<DK, DV, E, true>), grid, dim3(256), lds, st, pp);
+        return hipGetLastError();
     }
-    e = set_lds(prep_kernel<DK, DV, E, false, E>, lds);
+    constexpr size_t lds = PrepLds<DK, DV, E>::BYTES;
+    e = set_lds(prep_kernel<DK, DV, E, false>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prep_kernel<DK, DV, E, false, E>), grid, dim3(256), lds, st, pp);
+    hipLaunchKernelGGL((prep_kernel<DK, DV, E, false>), grid, dim3(256), lds, st, pp);
     return hipGetLastError();
 }
 
-template <int DK, int DV, typename E, typename OT>
+template <int DK, int DV, typename E, typename OT, bool SI>
 hipError_t scan_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
 {
     const WsPtrs w = ws_ptrs(p, a);
@@ -1285,9 +1378,9 @@ hipError_t scan_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
     // CU holds) keeps them apart.
     constexpr size_t lds_min = ScanLds<DK, DV, CT, E>::BYTES;
     const size_t lds = a.n_seqs > 1 ? std::max<size_t>(lds_min, 96 * 1024) : lds_min;
-    hipError_t e = set_lds(scan_kernel<DK, DV, CT, E, OT>, 96 * 1024);
+    hipError_t e = set_lds(scan_kernel<DK, DV, CT, E, OT, SI>, 96 * 1024);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_kernel<DK, DV, CT, E, OT>), dim3(p.H_v, DV / (16 * CT), a.n_seqs),
+    hipLaunchKernelGGL((scan_kernel<DK, DV, CT, E, OT, SI>), dim3(p.H_v, DV / (16 * CT), a.n_seqs),
                        dim3(CT * 256), lds, st, sp);
     e = hipGetLastError();
     if (e == hipSuccess && p.z) e = launch_gated_norm(p, static_cast<const float *>(o), a.out, a.total_tokens, st);
@@ -1316,9 +1409,11 @@ hipError_t scan_dv(const Problem &p, const PrefillArgs &a, hipStream_t st)
 {
     // with the epilogue the scan writes fp32 o (staged or in place)
     const bool ob = p.out_bf16 && !p.z;
+    if (op_split(p))        // the prologue's two-term operands; z is then set or not
+        return ob ? scan_t<DK, DV, bf16_t, bf16_t, true>(p, a, st) : scan_t<DK, DV, bf16_t, float, true>(p, a, st);
     if (op_bf16(p))
-        return ob ? scan_t<DK, DV, bf16_t, bf16_t>(p, a, st) : scan_t<DK, DV, bf16_t, float>(p, a, st);
-    return ob ? scan_t<DK, DV, float, bf16_t>(p, a, st) : scan_t<DK, DV, float, float>(p, a, st);
+        return ob ? scan_t<DK, DV, bf16_t, bf16_t, false>(p, a, st) : scan_t<DK, DV, bf16_t, float, false>(p, a, st);
+    return ob ? scan_t<DK, DV, float, bf16_t, false>(p, a, st) : scan_t<DK, DV, float, float, false>(p, a, st);
 }
 
 template <int DK>
