@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(RecParams P)
         for (int j = 0; j < 4; ++j) zz[j] = to_f32(zp[j]);
         nw[0] = w4.x; nw[1] = w4.y; nw[2] = w4.z; nw[3] = w4.w;
     }
-    __syncthreads();
+    lds_sync();
 
     // 3. norms (every wave reduces redundantly; no extra barrier)
     float kk = 0.f, qq = 0.f, kq = 0.f;
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(RecParams P)
     }
     red[0][rg][cg] = pk;
     red[1][rg][cg] = pq;
-    __syncthreads();
+    lds_sync();
     float4 tk = make_float4(0.f, 0.f, 0.f, 0.f), tq = tk;
 #pragma unroll 8
     for (int j = 0; j < RG; ++j) {
@@ -360,12 +360,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(RecParams 
         const E *vp = v + (int64_t)t * P.rs_v + (int64_t)h * DV + col;
 #pragma unroll
         for (int j = 0; j < 4; ++j) r.vv[j] = to_f32(vp[j]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) r.zz[j] = 0.f;
-        if (norm) {
-            const E *zp = static_cast<const E *>(P.z) + ((int64_t)t * P.H_v + h) * DV + col;
+        // z (read from v, same layout, when there is no epilogue: an
+        // unconditional load keeps the compiler's count of loads exact)
+        if constexpr (FUSED) {
+            const E *zp = norm ? static_cast<const E *>(P.z) + ((int64_t)t * P.H_v + h) * DV + col
+                               : v + (int64_t)t * P.rs_v + (int64_t)h * DV + col;
 #pragma unroll
             for (int j = 0; j < 4; ++j) r.zz[j] = to_f32(zp[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) r.zz[j] = 0.f;
         }
         return r;
     };
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(RecParams 
         if (tid < DK) sk[b][tid] = kqv;
         else if (tid < 2 * DK) sq[b][tid - DK] = kqv;
         const Tok nxt = fetch(min(t + 1, te - 1));
-        __syncthreads();
+        lds_sync();
 
         // norms (every wave reduces redundantly; no extra barrier)
         float kk = 0.f, qq = 0.f, kq = 0.f;
@@ -414,7 +418,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(RecParams 
         }
         red[b][0][rg][cg] = pk;
         red[b][1][rg][cg] = pq;
-        __syncthreads();
+        lds_sync();
         float4 tk = make_float4(0.f, 0.f, 0.f, 0.f), tq = tk;
 #pragma unroll 8
         for (int j = 0; j < RG; ++j) {
@@ -435,10 +439,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(RecParams 
         float o[4] = {dq * tq.x + kqh * d.x, dq * tq.y + kqh * d.y, dq * tq.z + kqh * d.z,
                       dq * tq.w + kqh * d.w};
         if (norm) gated_norm_row<CG, DV>(o, cur.zz, nw, P.eps);
-        if (rg == 0) {
-            OT *op = static_cast<OT *>(P.out) + ((int64_t)t * P.H_v + h) * DV + col;
+        {
+            // row group 0 writes the row; the other lanes' offsets fall past
+            // the buffer's end and are dropped.  No branch: a store inside one
+            // would make the next wait for the prefetched token wait for it
+            // too (on gfx9 stores and loads share the counter).
+            const __amdgpu_buffer_rsrc_t ob =
+                raw_buffer(static_cast<OT *>(P.out) + ((int64_t)t * P.H_v + h) * DV, (uint32_t)(DV * sizeof(OT)));
+            const uint32_t off = rg == 0 ? (uint32_t)(col * sizeof(OT)) : 0x80000000u;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) op[j] = from_f32<OT>(o[j]);
+            for (int j = 0; j < 4; ++j) buffer_store(from_f32<OT>(o[j]), ob, off + (uint32_t)(j * sizeof(OT)));
         }
         // rank-1 update of the decayed state, in registers
 #pragma unroll
