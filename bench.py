@@ -63,9 +63,19 @@ C = 64
 PREFILL_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
                for f in ("gdn_prefill.hip", "gdn_mfma.h", "gdn_device.h", "gdn_internal.h")]
 MEASURED_TRAFFIC = {
-    "source_sha256": "c6034aa41f947ed774fa372bf210f0318a20e067cdd98f8002a6d927f2d36517",
-    "scan": (100005.6 * 2.000 + 67584.0 * 1.000) * 1024,
-    "prepare": (40254.1 * 2.000 + 165147.6 * 1.000) * 1024,
+    "source_sha256": "3fe3feed94019230c502e78888dbc87f1e0e3e5dff5642a48ba33e351affa9b6",
+    "scan": (99998.2 * 2.000 + 67584.0 * 1.000) * 1024,
+    "prepare": (40298.4 * 2.000 + 165134.1 * 1.000) * 1024,
+}
+
+
+# The same for the decode kernel on the 64 x 128 decode workload
+# (profiles/decode64x128_hbm_traffic.md), per launch.
+DECODE_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
+              for f in ("gdn_decode.hip", "gdn_device.h", "gdn_internal.h")]
+MEASURED_DECODE_TRAFFIC = {
+    "source_sha256": "16f662346a299f3c6e246ed3ede85c482f7feb19a8f54e71ab8b14df9fb6610b",
+    "decode": (66140.1 * 2.000 + 132096.0 * 1.000) * 1024,
 }
 
 
@@ -86,6 +96,9 @@ def source_digest(paths):
 
 
 def measured_traffic(kernel):
+    if kernel == "decode":
+        ok = source_digest(DECODE_SRC) == MEASURED_DECODE_TRAFFIC["source_sha256"]
+        return MEASURED_DECODE_TRAFFIC["decode"] if ok else None
     ok = source_digest(PREFILL_SRC) == MEASURED_TRAFFIC["source_sha256"]
     return MEASURED_TRAFFIC.get(kernel) if ok else None
 
@@ -237,7 +250,8 @@ def bench_decode(gdn, dev, reps=3):
             "value": ip["tokens_s"], "unit": "tokens/s",
             "ms_per_step": ip["mean_launch_ms"],
             "roofline": {"bound": "hbm", "achieved": ip["achieved_gbs"], "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": ip["frac"], "traffic": None,
+                         "unit": "GB/s", "frac": ip["frac"], "traffic": measured_traffic("decode"),
+                         "traffic_unit": "bytes per launch",
                          "kernel": "decode_kernel", "bytes_per_launch": ip["bytes_per_launch"],
                          "mean_launch_ms": ip["mean_launch_ms"]},
             "ping_pong": res["ping_pong"], "in_place": ip}
@@ -459,6 +473,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline prefill + decode only")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="the decode workload only (for hardware-counter runs)")
     ap.add_argument("--layer-only", action="store_true",
                     help="the fused layer prefill and decode only (for kernel traces)")
     ap.add_argument("--prefill-only", action="store_true",
@@ -493,6 +509,11 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration: 3 copies of {args.copy_mib} MiB")
         del src, dst
+    if args.decode_only:
+        log("decode 64x128 ...")
+        dec = bench_decode(gdn, dev, reps=1)
+        log(f"  {dec['ms_per_step']*1e3:.2f} us/step, {dec['roofline']['achieved']:.0f} GB/s")
+        return
     log("prefill T=4096 ...")
     case, pf = bench_prefill(gdn, dev, args.steps, args.warmup)
     log(f"  {pf['ms_step']:.4f} ms/step, {pf['tokens_s']:.4g} tok/s")
