@@ -333,7 +333,8 @@ def bench_layer_prefill(gdn, dev, reps=10):
     return {"workload": "fused layer prefill: 1 x 4096 tokens, mixed bf16 q|k|v rows -> conv(4) + "
                         "SiLU, raw gates, gated RMSNorm, bf16 out, Qwen3-Next heads",
             "ms_per_call": ms, "tokens_s": T / (ms * 1e-3),
-            "operands": "fp32 (the prologue's output is not rounded to bf16)"}
+            "operands": "two-term bf16 (hi + lo) q, k, v and W: the prologue's output is not rounded "
+                        "to bf16 once"}
 
 
 def bench_layer_decode(gdn, dev, reps=3):

@@ -120,10 +120,13 @@ typedef enum gdn_gate_mode {
  * so slot_stride (0 = the sum of both) and the state_in / state_out pointers
  * refer to whole rows.  slot_in < 0 starts both parts at zero; the new
  * convolution state (the last d_conv-1 inputs of u) is written at slot_out.
- * The convolution output stays fp32 in every entry point: with bf16 rows,
- * gdn_chunked_prefill then runs its matrix products on fp32 operands (after
- * SiLU the keys of neighbouring tokens are correlated, and rounding q, k, v
- * to bf16 would move the result by several percent of its rms).
+ * The convolution output is never rounded once to bf16 (after SiLU the keys
+ * of neighbouring tokens are correlated, and a single bf16 rounding of q, k,
+ * v moves the result by several percent of its rms): the recurrent entry
+ * points use it in fp32, and with bf16 rows gdn_chunked_prefill feeds it to
+ * the matrix cores as two-term bf16 operands (hi + lo, about 16 significant
+ * bits; fp32 rows keep fp32 operands).  The prefill workspace grows
+ * accordingly (gdn_prefill_workspace_size accounts for it).
  * The split-phase entry points do not support the prologue.
  *
  * Epilogue (z != NULL): llm_build_norm (RMS, weight ssm_norm) followed by
