@@ -43,6 +43,8 @@
 // of raw (bf16) operands, so the inputs are used as MFMA operands exactly as
 // stored.  A final partial chunk is zero-padded; padded rows carry beta = 0,
 // g = 0 and zero norms, which makes them the identity on the state.
+#include <atomic>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
@@ -109,6 +111,20 @@ struct WsLayout {
 bool stage_o(const Problem &p) { return p.z && p.out_bf16; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Compute units of the current device (cached per device).
+int cu_count()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 // Operand type of the chunked form: that of the inputs.  With the
 // convolution prologue and bf16 rows, q, k, v become two-term bf16 operands
@@ -332,6 +348,10 @@ struct PrepParams {
     const int32_t *slot_in;
     int64_t slot_stride;
     int has_state;
+    // 1: one workgroup per (chunk, value head) instead of per (chunk, key
+    // head), for grids too small to fill the GPU (K K^T is then formed once
+    // per value head)
+    int head_split;
 };
 
 // LDS of the preparation kernel.  Rows are padded so that the row stride is
@@ -473,7 +493,13 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     float *sBetah = sRAh + NH * C;                              // [NH][C] beta_c          (columns of T for U0)
     float *sColh = sBetah + NH * C;                             // [NH][C] beta_c e^{G_c} / |k_c|  (columns of T for W)
 
-    const int chunk = blockIdx.x, kh = blockIdx.y;
+    const int chunk = blockIdx.x;
+    const int ratio = pp.H_v / pp.H_k;
+    const int kh = pp.head_split ? blockIdx.y / ratio : blockIdx.y;
+    // value heads of this workgroup: [jbeg, jend) of the key head's ratio;
+    // row scalars are computed for NH heads at a time from jbase on
+    const int jbeg = pp.head_split ? blockIdx.y % ratio : 0;
+    const int jend = pp.head_split ? jbeg + 1 : ratio;
     int t0, len, seq, first;
     if (pp.single_T >= 0) {
         // a single sequence covers tokens [0, T): chunk c is [64c, min(64c + 64, T))
@@ -496,7 +522,6 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     const E *qg = static_cast<const E *>(pp.q);
     const E *kg = static_cast<const E *>(pp.k);
     const E *vg = static_cast<const E *>(pp.v);
-    const int ratio = pp.H_v / pp.H_k;
 
     // g and beta of up to NH value heads (wave w: head j0 + w, lane: row)
     // Loads here are unconditional (clamped row / head, zero selected
@@ -648,8 +673,9 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     // scheduling barrier keeps that order), so that waiting for K and Q does
     // not wait for these too
     __builtin_amdgcn_sched_barrier(0);
-    load_gb(0);
-    load_v(kh * ratio);
+    const int jbase = jbeg - jbeg % NH;
+    load_gb(jbase);
+    load_v(kh * ratio + jbeg);
     if constexpr (CONV) {
 #pragma unroll
         for (int j = 0; j < NHK; ++j)
@@ -698,7 +724,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
         }
     }
     lds_sync();
-    head_scalars(0);
+    head_scalars(jbase);
 
     // 2. raw q and k^T of this key head as operand fragments for the scan
     {
@@ -743,7 +769,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     }
     lds_sync();   // Q is dead: sX holds V from here on
 
-    for (int jv = 0; jv < ratio; ++jv) {
+    for (int jv = jbeg; jv < jend; ++jv) {
         const int h = kh * ratio + jv;
         char *blk = pp.vblocks + ((size_t)chunk * pp.H_v + h) * ((size_t)G::VBLK * 1024);
         char *Wf = blk + G::F_W * 1024;
@@ -794,8 +820,8 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
                 if constexpr (SI) *reinterpret_cast<u32x4 *>(sXL + (vrow0 + p) * LDX + vcv * VEC) = resl[p];
             }
         }
-        load_v(kh * ratio + min(jv + 1, ratio - 1));   // next head (the last reloads itself)
-        if (jv > 0 && hs == 0) {
+        load_v(kh * ratio + min(jv + 1, jend - 1));    // next head (the last reloads itself)
+        if (jv > jbase && hs == 0) {
             load_gb(jv);
             head_scalars(jv);
         }
@@ -1345,9 +1371,15 @@ hipError_t prepare_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
                   p.ssm_a ? Gates{p.ssm_a, p.ssm_dt, 1} : Gates{a.g, a.g, 0},
                   p.rs_qk, p.rs_v, p.conv_w,
                   // without a state pool the history loads read the taps (unused)
-                  a.conv_in ? a.conv_in : p.conv_w, a.slot_in, p.slot_stride, a.conv_in != nullptr};
+                  a.conv_in ? a.conv_in : p.conv_w, a.slot_in, p.slot_stride, a.conv_in != nullptr, 0};
     const int chunks = single ? (int)((a.total_tokens + C - 1) / C) : w.L.max_chunks;
-    const dim3 grid(chunks, p.H_k);
+    // A grid that leaves most workgroup slots empty (e.g. one 512-token
+    // ubatch: 8 chunks x 16 key heads) is bound by one workgroup's latency;
+    // splitting it by value head halves that chain for a little more work.
+    const int per_cu = (sizeof(E) == 2 && !p.conv_w) ? 2 : 1;
+    const int ratio = p.H_v / p.H_k;
+    if (ratio > 1 && (int64_t)chunks * p.H_v <= (int64_t)per_cu * cu_count()) pp.head_split = 1;
+    const dim3 grid(chunks, pp.head_split ? p.H_v : p.H_k);
     if (p.conv_w) {
         // bf16 rows: two-term bf16 operands (SI); fp32 rows: fp32 operands
         constexpr size_t lds = PrepLds<DK, DV, E, sizeof(E) == 2>::BYTES;
