@@ -1039,14 +1039,20 @@ template <> struct TileOut<float> {
 };
 
 // Scan over a sequence's chunks for one value head and CT column tiles of 16
-// state columns.  Wave (ctl, rt): token rows 16*rt.. of column tile ctl in
-// phase A and for the output; owner of dk blocks kb = rt (mod 4) of the state.
-// Every operand of a chunk is loaded from the workspace straight into the
-// registers of the wave that uses it, re-issued for the next chunk right
-// after its last use in this one, so its latency overlaps a chunk of work;
-// LDS carries only the per-chunk exchange (state and delta fragments).
+// state columns, with two sets of four waves per column tile:
+//   state waves (role 0), wave rt: U = U0 - W S for token rows 16*rt.. in
+//     phase A (published with ks*U for the update); in phase B the update of
+//     the owned dk blocks kb = rt (mod 4) of the state, S = gn S + K^T (ks U).
+//   output waves (role 1), wave rt: the inter-chunk read-out Q S for token
+//     rows 16*rt.. in phase A, then O = qs (Q S) + P U and its store.
+// Each set's chain per chunk is half of a single wave's, and every SIMD holds
+// one wave of each set.  Every operand of a chunk is loaded from the
+// workspace straight into the registers of the wave that uses it, re-issued
+// for the next chunk right after its last use in this one, so its latency
+// overlaps a chunk of work; LDS carries only the per-chunk exchange (state
+// and delta fragments).
 template <int DK, int DV, int CT, typename E, typename OT, bool SI>
-__global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
+__global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
 {
     using M = Mfma<E>;
     using SP = Split<E>;
@@ -1068,39 +1074,16 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
     const int h = blockIdx.x, cg = blockIdx.y, i = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int ctl = wv >> 2, rt = wv & 3;
+    const int ctl = wv >> 3, role = (wv >> 2) & 1, rt = wv & 3;
     const int n = lane & 15, qd = lane >> 4;
     const int kh = h / (sp.H_v / sp.H_k);
     const int ct = cg * CT + ctl;
     const int col0 = 16 * ct;
-    OT *og = static_cast<OT *>(sp.out);
 
     auto xfrag = [&](const u32x4 *base, int f) -> Frag { return __builtin_bit_cast(Frag, base[f * 64 + lane]); };
     u32x4 *mySf = sSf + ctl * (NKD * NS * 64);
     u32x4 *myUf = sUf + ctl * (NKC * NS * 64);
     u32x4 *myKf = sKf + ctl * (NKC * NS * 64);
-
-    // state: registers of the owning wave, published as two-term B fragments
-    floatx4 Sreg[NOWN][TPB];
-    {
-        const int sin = sp.state_in ? sp.slot_in[i] : -1;
-        const float *base = sin >= 0 ? sp.state_in + (int64_t)sin * sp.slot_stride + (int64_t)h * DK * DV + col0 + n
-                                     : nullptr;
-#pragma unroll
-        for (int o = 0; o < NOWN; ++o) {
-            const int kb = rt + 4 * o;
-#pragma unroll
-            for (int t = 0; t < TPB; ++t) {
-                floatx4 v = {0.f, 0.f, 0.f, 0.f};
-                if (base && kb < NKD) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) v[j] = base[(int64_t)(16 * (kb * TPB + t) + 4 * qd + j) * DV];
-                }
-                Sreg[o][t] = v;
-                if (kb < NKD) TileOut<E>::put(mySf + (kb * NS) * 64, mySf + (kb * NS + NS - 1) * 64, lane, t, v);
-            }
-        }
-    }
 
     const bool single = sp.single_T >= 0;
     const int cs = single ? 0 : sp.cstart[i];
@@ -1119,200 +1102,239 @@ __global__ __launch_bounds__(CT * 256) void scan_kernel(ScanParams sp)
     auto scal1 = [&](int c, int off) -> float {
         return reinterpret_cast<const float *>(vblk(c) + G::F_SCAL * 64)[off];
     };
-    const int u0f = G::F_U0 + ct * 4 + rt;         // accumulator tile (ct, rt) of U0
     const int ro = 16 * rt + 4 * qd;               // first of this lane's 4 token rows
-
-    // operands of the current chunk (loaded for chunk cs before the loop,
-    // reloaded for the next chunk right after their last use)
+    // operands of the first chunk (a sequence without chunks reads chunk 0
+    // and runs no iteration)
     const int c0 = cs < ce ? cs : 0;
-    // SI: q and k^T also as lo parts (two-term operands)
-    Frag Wf[NKD], Qf[NKD], Ph[NKC], Pl[NKC], Kf[NOWN * TPB][NKC];
-    Frag Wlf[SI ? NKD : 1], Qlf[SI ? NKD : 1], Klf[SI ? NOWN * TPB : 1][NKC];
+
+    if (role == 0) {
+        // state: registers of the owning wave, published as two-term B fragments
+        floatx4 Sreg[NOWN][TPB];
+        {
+            const int sin = sp.state_in ? sp.slot_in[i] : -1;
+            const float *base = sin >= 0 ? sp.state_in + (int64_t)sin * sp.slot_stride + (int64_t)h * DK * DV + col0 + n
+                                         : nullptr;
 #pragma unroll
-    for (int kb = 0; kb < NKD; ++kb) {
-        Wf[kb] = vfrag(c0, G::F_W + rt * NKD + kb);
-        Qf[kb] = kfrag(c0, G::F_Q + rt * NKD + kb);
-        if constexpr (SI) {
-            Wlf[kb] = vfrag(c0, G::F_WL + rt * NKD + kb);
-            Qlf[kb] = kfrag(c0, G::F_QL + rt * NKD + kb);
-        }
-    }
+            for (int o = 0; o < NOWN; ++o) {
+                const int kb = rt + 4 * o;
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-        Ph[kc] = vfrag(c0, G::F_PH + rt * NKC + kc);
-        if constexpr (NS == 2) Pl[kc] = vfrag(c0, G::F_PL + rt * NKC + kc);
-    }
+                for (int t = 0; t < TPB; ++t) {
+                    floatx4 v = {0.f, 0.f, 0.f, 0.f};
+                    if (base && kb < NKD) {
 #pragma unroll
-    for (int o = 0; o < NOWN; ++o)
-#pragma unroll
-        for (int t = 0; t < TPB; ++t) {
-            const int mt = min(rt + 4 * o, NKD - 1) * TPB + t;
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-                Kf[o * TPB + t][kc] = kfrag(c0, G::F_KT + mt * NKC + kc);
-                if constexpr (SI) Klf[o * TPB + t][kc] = kfrag(c0, G::F_KTL + mt * NKC + kc);
+                        for (int j = 0; j < 4; ++j) v[j] = base[(int64_t)(16 * (kb * TPB + t) + 4 * qd + j) * DV];
+                    }
+                    Sreg[o][t] = v;
+                    if (kb < NKD) TileOut<E>::put(mySf + (kb * NS) * 64, mySf + (kb * NS + NS - 1) * 64, lane, t, v);
+                }
             }
         }
-    floatx4 u0 = __builtin_bit_cast(floatx4, vblk(c0)[u0f * 64 + lane]);
-    floatx4 qs4 = scal4(c0, ro), ks4 = scal4(c0, 64 + ro);
-    float gn = scal1(c0, 128);
-    // the sequence's token range; its chunks are consecutive 64-token pieces
-    const int tbeg = single || cs >= ce ? 0 : sp.ent[cs].t0;
-    const int tend = single ? sp.single_T : cs < ce ? sp.ent[ce - 1].t0 + sp.ent[ce - 1].len : 0;
-    // Let the first chunk's operands land before the loop: the loop's waits
-    // then only have to account for the loads issued inside it.
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
-    lds_sync();
-
-    const uint32_t row_bytes = (uint32_t)(sp.H_v * DV * sizeof(OT));
-    // The per-CU vector memory path, not the matrix cores, bounds a chunk:
-    // every wave moves ~16 KiB of operands per chunk.  The loads for the next
-    // chunk are therefore spread between this chunk's matrix-core ops
-    // (scheduling groups below) rather than issued in bursts, which would
-    // stall the issuing waves.  W and q are reloaded right after their last
-    // use in phase A, P after phase B and k^T after the state update: each
-    // a whole chunk before it is needed again.
-    for (int c = cs; c < ce; ++c) {
-        const int cn = min(c + 1, ce - 1);         // next chunk (the last one reloads itself)
-
-        // phase A: U = U0 - W S and the inter-chunk read-out Q S, state from LDS
-        floatx4 WSh = {0.f, 0.f, 0.f, 0.f}, WSl = WSh, OQh = WSh, OQl = WSh;
+        const int u0f = G::F_U0 + ct * 4 + rt;     // accumulator tile (ct, rt) of U0
+        Frag Wf[NKD], Wlf[SI ? NKD : 1], Kf[NOWN * TPB][NKC], Klf[SI ? NOWN * TPB : 1][NKC];
 #pragma unroll
         for (int kb = 0; kb < NKD; ++kb) {
-            const Frag sh = xfrag(mySf, kb * NS);
-            const Frag sl = xfrag(mySf, kb * NS + NS - 1);
-            M::mma(WSh, Wf[kb], sh);
-            if constexpr (NS == 2) M::mma(WSl, Wf[kb], sl);
-            Wf[kb] = vfrag(cn, G::F_W + rt * NKD + kb);
-            M::mma(OQh, Qf[kb], sh);
-            if constexpr (NS == 2) M::mma(OQl, Qf[kb], sl);
-            Qf[kb] = kfrag(cn, G::F_Q + rt * NKD + kb);
-            if constexpr (SI) {
-                M::mma(WSl, Wlf[kb], sh);
-                Wlf[kb] = vfrag(cn, G::F_WL + rt * NKD + kb);
-                M::mma(OQl, Qlf[kb], sh);
-                Qlf[kb] = kfrag(cn, G::F_QL + rt * NKD + kb);
+            Wf[kb] = vfrag(c0, G::F_W + rt * NKD + kb);
+            if constexpr (SI) Wlf[kb] = vfrag(c0, G::F_WL + rt * NKD + kb);
+        }
+#pragma unroll
+        for (int o = 0; o < NOWN; ++o)
+#pragma unroll
+            for (int t = 0; t < TPB; ++t) {
+                const int mt = min(rt + 4 * o, NKD - 1) * TPB + t;
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) {
+                    Kf[o * TPB + t][kc] = kfrag(c0, G::F_KT + mt * NKC + kc);
+                    if constexpr (SI) Klf[o * TPB + t][kc] = kfrag(c0, G::F_KTL + mt * NKC + kc);
+                }
             }
-        }
-        const floatx4 U = u0 - (WSh + WSl);
-        const floatx4 Oi = (OQh + OQl) * qs4;
-        const floatx4 Uk = U * ks4;
-        u0 = __builtin_bit_cast(floatx4, vblk(cn)[u0f * 64 + lane]);
-        qs4 = scal4(cn, ro);
-        ks4 = scal4(cn, 64 + ro);
-        {
-            const int kc = rt / TPB, part = rt % TPB;
-            TileOut<E>::put(myUf + (kc * NS) * 64, myUf + (kc * NS + NS - 1) * 64, lane, part, U);
-            TileOut<E>::put(myKf + (kc * NS) * 64, myKf + (kc * NS + NS - 1) * 64, lane, part, Uk);
-        }
-        // region order: matrix-core op, load, alternately
-        if constexpr (SI) {
+        floatx4 u0 = __builtin_bit_cast(floatx4, vblk(c0)[u0f * 64 + lane]);
+        floatx4 ks4 = scal4(c0, 64 + ro);
+        float gn = scal1(c0, 128);
+        // Let the first chunk's operands land before the loop: the loop's
+        // waits then only have to account for the loads issued inside it.
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+        lds_sync();
+
+        for (int c = cs; c < ce; ++c) {
+            const int cn = min(c + 1, ce - 1);     // next chunk (the last one reloads itself)
+
+            // phase A: U = U0 - W S, state from LDS
+            floatx4 WSh = {0.f, 0.f, 0.f, 0.f}, WSl = WSh;
+#pragma unroll
+            for (int kb = 0; kb < NKD; ++kb) {
+                const Frag sh = xfrag(mySf, kb * NS);
+                M::mma(WSh, Wf[kb], sh);
+                if constexpr (NS == 2) M::mma(WSl, Wf[kb], xfrag(mySf, kb * NS + 1));
+                Wf[kb] = vfrag(cn, G::F_W + rt * NKD + kb);
+                if constexpr (SI) {
+                    M::mma(WSl, Wlf[kb], sh);
+                    Wlf[kb] = vfrag(cn, G::F_WL + rt * NKD + kb);
+                }
+            }
+            const floatx4 U = u0 - (WSh + WSl);
+            const floatx4 Uk = U * ks4;
+            u0 = __builtin_bit_cast(floatx4, vblk(cn)[u0f * 64 + lane]);
+            ks4 = scal4(cn, 64 + ro);
+            {
+                const int kc = rt / TPB, part = rt % TPB;
+                TileOut<E>::put(myUf + (kc * NS) * 64, myUf + (kc * NS + NS - 1) * 64, lane, part, U);
+                TileOut<E>::put(myKf + (kc * NS) * 64, myKf + (kc * NS + NS - 1) * 64, lane, part, Uk);
+            }
+            // region order: matrix-core op, load, alternately
 #pragma unroll
             for (int q = 0; q < NKD; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if constexpr (SI) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+            }
+            lds_sync();
+
+            // phase B: the owned blocks of the state
+            if (rt < NKD) {
+                Frag kh_[NKC], kl_[NKC];
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) {
+                    kh_[kc] = xfrag(myKf, kc * NS);
+                    kl_[kc] = xfrag(myKf, kc * NS + NS - 1);
+                }
+#pragma unroll
+                for (int o = 0; o < NOWN; ++o) {
+                    const int kb = rt + 4 * o;
+                    if (kb >= NKD) continue;
+                    floatx4 Sa[TPB], Sb[TPB];
+#pragma unroll
+                    for (int t = 0; t < TPB; ++t) {
+                        Sa[t] = Sreg[o][t] * gn;
+                        Sb[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    }
+#pragma unroll
+                    for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                        for (int t = 0; t < TPB; ++t) {
+                            M::mma(Sa[t], Kf[o * TPB + t][kc], kh_[kc]);
+                            if constexpr (NS == 2) M::mma(Sb[t], Kf[o * TPB + t][kc], kl_[kc]);
+                            Kf[o * TPB + t][kc] = kfrag(cn, G::F_KT + ((rt + 4 * o) * TPB + t) * NKC + kc);
+                            if constexpr (SI) {
+                                M::mma(Sb[t], Klf[o * TPB + t][kc], kh_[kc]);
+                                Klf[o * TPB + t][kc] = kfrag(cn, G::F_KTL + ((rt + 4 * o) * TPB + t) * NKC + kc);
+                            }
+                        }
+#pragma unroll
+                    for (int t = 0; t < TPB; ++t) {
+                        Sreg[o][t] = Sa[t] + Sb[t];
+                        TileOut<E>::put(mySf + (kb * NS) * 64, mySf + (kb * NS + NS - 1) * 64, lane, t, Sreg[o][t]);
+                    }
+                }
+            }
+            gn = scal1(cn, 128);
+            // region order: matrix-core op, load, alternately
+#pragma unroll
+            for (int q = 0; q < NOWN * TPB * NKC; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if constexpr (SI) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
             }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 2 * NKD; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            }
-        }
-        lds_sync();
-
-        // phase B: intra-chunk output P U, then the owned blocks of the state
-        floatx4 Oa = Oi, Ob = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-            if (kc * KB > 16 * rt + 15) continue;
-            const Frag uh = xfrag(myUf, kc * NS);
-            M::mma(Oa, Ph[kc], uh);
-            if constexpr (NS == 2) {
-                M::mma(Ob, Ph[kc], xfrag(myUf, kc * NS + 1));
-                M::mma(Ob, Pl[kc], uh);
-            }
-        }
-        {
-            // rows >= len of a partial chunk fall outside the buffer and are dropped
-            const int t0 = tbeg + C * (c - cs), len = min(C, tend - t0);
-            const __amdgpu_buffer_rsrc_t ob =
-                raw_buffer(og + ((size_t)t0 * sp.H_v + h) * DV + col0, (uint32_t)len * row_bytes);
-            const floatx4 O = Oa + Ob;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                buffer_store(from_f32<OT>(O[j]), ob, (uint32_t)(ro + j) * row_bytes + n * (uint32_t)sizeof(OT));
-        }
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-            Ph[kc] = vfrag(cn, G::F_PH + rt * NKC + kc);
-            if constexpr (NS == 2) Pl[kc] = vfrag(cn, G::F_PL + rt * NKC + kc);
+            lds_sync();
         }
 
-        if (rt < NKD) {
-            Frag kh_[NKC], kl_[NKC];
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-                kh_[kc] = xfrag(myKf, kc * NS);
-                kl_[kc] = xfrag(myKf, kc * NS + NS - 1);
-            }
+        const int sout = sp.slot_out[i];
+        if (sout >= 0) {
+            float *base = sp.state_out + (int64_t)sout * sp.slot_stride + (int64_t)h * DK * DV + col0 + n;
 #pragma unroll
             for (int o = 0; o < NOWN; ++o) {
                 const int kb = rt + 4 * o;
                 if (kb >= NKD) continue;
-                floatx4 Sa[TPB], Sb[TPB];
 #pragma unroll
-                for (int t = 0; t < TPB; ++t) {
-                    Sa[t] = Sreg[o][t] * gn;
-                    Sb[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-                }
+                for (int t = 0; t < TPB; ++t)
 #pragma unroll
-                for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-                    for (int t = 0; t < TPB; ++t) {
-                        M::mma(Sa[t], Kf[o * TPB + t][kc], kh_[kc]);
-                        if constexpr (NS == 2) M::mma(Sb[t], Kf[o * TPB + t][kc], kl_[kc]);
-                        Kf[o * TPB + t][kc] = kfrag(cn, G::F_KT + ((rt + 4 * o) * TPB + t) * NKC + kc);
-                        if constexpr (SI) {
-                            M::mma(Sb[t], Klf[o * TPB + t][kc], kh_[kc]);
-                            Klf[o * TPB + t][kc] = kfrag(cn, G::F_KTL + ((rt + 4 * o) * TPB + t) * NKC + kc);
-                        }
-                    }
-#pragma unroll
-                for (int t = 0; t < TPB; ++t) {
-                    Sreg[o][t] = Sa[t] + Sb[t];
-                    TileOut<E>::put(mySf + (kb * NS) * 64, mySf + (kb * NS + NS - 1) * 64, lane, t, Sreg[o][t]);
-                }
+                    for (int j = 0; j < 4; ++j)
+                        base[(int64_t)(16 * (kb * TPB + t) + 4 * qd + j) * DV] = Sreg[o][t][j];
             }
         }
-        gn = scal1(cn, 128);
-        // region order: matrix-core op, load, alternately
+    } else {
+        OT *og = static_cast<OT *>(sp.out);
+        Frag Qf[NKD], Qlf[SI ? NKD : 1], Ph[NKC], Pl[NKC];
 #pragma unroll
-        for (int q = 0; q < (SI ? 16 : 12); ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        for (int kb = 0; kb < NKD; ++kb) {
+            Qf[kb] = kfrag(c0, G::F_Q + rt * NKD + kb);
+            if constexpr (SI) Qlf[kb] = kfrag(c0, G::F_QL + rt * NKD + kb);
         }
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            Ph[kc] = vfrag(c0, G::F_PH + rt * NKC + kc);
+            if constexpr (NS == 2) Pl[kc] = vfrag(c0, G::F_PL + rt * NKC + kc);
+        }
+        floatx4 qs4 = scal4(c0, ro);
+        // the sequence's token range; its chunks are consecutive 64-token pieces
+        const int tbeg = single || cs >= ce ? 0 : sp.ent[cs].t0;
+        const int tend = single ? sp.single_T : cs < ce ? sp.ent[ce - 1].t0 + sp.ent[ce - 1].len : 0;
+        const uint32_t row_bytes = (uint32_t)(sp.H_v * DV * sizeof(OT));
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
         lds_sync();
-    }
 
-    const int sout = sp.slot_out[i];
-    if (sout >= 0) {
-        float *base = sp.state_out + (int64_t)sout * sp.slot_stride + (int64_t)h * DK * DV + col0 + n;
+        for (int c = cs; c < ce; ++c) {
+            const int cn = min(c + 1, ce - 1);
+
+            // phase A: the inter-chunk read-out Q S, state from LDS
+            floatx4 OQh = {0.f, 0.f, 0.f, 0.f}, OQl = OQh;
 #pragma unroll
-        for (int o = 0; o < NOWN; ++o) {
-            const int kb = rt + 4 * o;
-            if (kb >= NKD) continue;
+            for (int kb = 0; kb < NKD; ++kb) {
+                const Frag sh = xfrag(mySf, kb * NS);
+                M::mma(OQh, Qf[kb], sh);
+                if constexpr (NS == 2) M::mma(OQl, Qf[kb], xfrag(mySf, kb * NS + 1));
+                Qf[kb] = kfrag(cn, G::F_Q + rt * NKD + kb);
+                if constexpr (SI) {
+                    M::mma(OQl, Qlf[kb], sh);
+                    Qlf[kb] = kfrag(cn, G::F_QL + rt * NKD + kb);
+                }
+            }
+            const floatx4 Oi = (OQh + OQl) * qs4;
+            qs4 = scal4(cn, ro);
 #pragma unroll
-            for (int t = 0; t < TPB; ++t)
+            for (int q = 0; q < NKD; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if constexpr (SI) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+            }
+            lds_sync();
+
+            // phase B: intra-chunk output P U
+            floatx4 Oa = Oi, Ob = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+                if (kc * KB > 16 * rt + 15) continue;
+                const Frag uh = xfrag(myUf, kc * NS);
+                M::mma(Oa, Ph[kc], uh);
+                if constexpr (NS == 2) {
+                    M::mma(Ob, Ph[kc], xfrag(myUf, kc * NS + 1));
+                    M::mma(Ob, Pl[kc], uh);
+                }
+            }
+            {
+                // rows >= len of a partial chunk fall outside the buffer and are dropped
+                const int t0 = tbeg + C * (c - cs), len = min(C, tend - t0);
+                const __amdgpu_buffer_rsrc_t ob =
+                    raw_buffer(og + ((size_t)t0 * sp.H_v + h) * DV + col0, (uint32_t)len * row_bytes);
+                const floatx4 O = Oa + Ob;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    base[(int64_t)(16 * (kb * TPB + t) + 4 * qd + j) * DV] = Sreg[o][t][j];
+                    buffer_store(from_f32<OT>(O[j]), ob, (uint32_t)(ro + j) * row_bytes + n * (uint32_t)sizeof(OT));
+            }
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+                Ph[kc] = vfrag(cn, G::F_PH + rt * NKC + kc);
+                if constexpr (NS == 2) Pl[kc] = vfrag(cn, G::F_PL + rt * NKC + kc);
+            }
+            lds_sync();
         }
     }
 }
@@ -1413,7 +1435,7 @@ hipError_t scan_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
     hipError_t e = set_lds(scan_kernel<DK, DV, CT, E, OT, SI>, 96 * 1024);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((scan_kernel<DK, DV, CT, E, OT, SI>), dim3(p.H_v, DV / (16 * CT), a.n_seqs),
-                       dim3(CT * 256), lds, st, sp);
+                       dim3(CT * 512), lds, st, sp);
     e = hipGetLastError();
     if (e == hipSuccess && p.z) e = launch_gated_norm(p, static_cast<const float *>(o), a.out, a.total_tokens, st);
     return e;
