@@ -1,6 +1,7 @@
 // gdn_api.cpp -- the libgdn C ABI: argument validation, workspace sizing and
 // dispatch to the kernel launchers.  No allocation, no synchronisation and no
 // host reads of device memory happen here.
+#include <algorithm>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -233,7 +234,7 @@ gdn_status gdn_prefill_prepare(const gdn_dims *dims, const void *q, const void *
     if (st != GDN_OK) return st;
     gdn::PrefillArgs a{q, k, v, g, beta, nullptr, nullptr, nullptr, cu_seqlens, nullptr,
                        nullptr, n_seqs, total_tokens, workspace, nullptr, nullptr};
-    return hip_status(gdn::launch_prepare(p, a, static_cast<hipStream_t>(stream)), "prepare");
+    return hip_status(gdn::launch_prepare(p, a, gdn::Segment{}, static_cast<hipStream_t>(stream)), "prepare");
 }
 
 gdn_status gdn_prefill_scan(const gdn_dims *dims, const float *state_in, float *state_out,
@@ -254,7 +255,7 @@ gdn_status gdn_prefill_scan(const gdn_dims *dims, const float *state_in, float *
     gdn::PrefillArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, state_in, state_out, out, nullptr, slot_in,
                        slot_out, n_seqs, total_tokens, const_cast<void *>(workspace), nullptr, nullptr};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return hip_status(gdn::launch_scan(p, a, s), "scan");
+    return hip_status(gdn::launch_scan(p, a, gdn::Segment{}, s), "scan");
 }
 
 gdn_status gdn_chunked_prefill(const gdn_dims *dims, const void *q, const void *k,
@@ -280,8 +281,19 @@ gdn_status gdn_chunked_prefill(const gdn_dims *dims, const void *q, const void *
                        cu_seqlens, slot_in, slot_out, n_seqs, total_tokens, workspace,
                        state_in, state_out};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    st = hip_status(gdn::launch_prepare(p, a, s), "prepare");
-    if (st == GDN_OK) st = hip_status(gdn::launch_scan(p, a, s), "scan");
+    // consecutive chunk ranges within the cache budget
+    const int chunks = gdn::prefill_chunk_count(p, n_seqs, total_tokens);
+    const int per = gdn::segment_chunks(p, chunks);
+    const int n_seg = std::max(1, (chunks + per - 1) / per);
+    for (int k = 0; k < n_seg && st == GDN_OK; ++k) {
+        gdn::Segment sg;
+        sg.lo = k * per;
+        sg.hi = k + 1 == n_seg ? 0x7fffffff : (k + 1) * per;
+        sg.first = k == 0;
+        sg.last = k + 1 == n_seg;
+        st = hip_status(gdn::launch_prepare(p, a, sg, s), "prepare");
+        if (st == GDN_OK) st = hip_status(gdn::launch_scan(p, a, sg, s), "scan");
+    }
     // the convolution state is replaced only after the preparation has read it
     if (st == GDN_OK && p.conv_w)
         st = hip_status(gdn::launch_conv_state(p, qkv, cu_seqlens, n_seqs == 1 ? (int)total_tokens : -1,

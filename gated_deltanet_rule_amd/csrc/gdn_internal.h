@@ -91,11 +91,32 @@ inline int64_t max_chunks(int32_t n_seqs, int64_t total_tokens) {
 }
 
 size_t prefill_workspace_bytes(const Problem &p, int32_t n_seqs, int64_t total_tokens);
+
+// A range of chunks run as one preparation + scan pair.  A long prefill is
+// run as several consecutive ranges so that the WY factors one range writes
+// are still in the 256 MB last-level cache (the MALL) when its scan reads
+// them: once they outgrow it, the scan's time per chunk rises by half.
+// Sequences crossing a range boundary carry their state through the
+// workspace.
+struct Segment {
+    int lo = 0, hi = 0x7fffffff;   // chunks [lo, hi) of the batch
+    bool first = true;             // the first range: builds the chunk table
+    bool last = true;              // the last range: runs the epilogue
+};
+// A batch whose factors fit kOneRangeBytes runs as one range (a second
+// launch pair costs more than the cache misses it saves); a longer one runs
+// in ranges of at most kSegmentBytes of factors, which leaves room in the
+// cache for the range's inputs and outputs.
+constexpr size_t kOneRangeBytes = 168u << 20;
+constexpr size_t kSegmentBytes = 96u << 20;
+// chunks of a batch (an upper bound when n_seqs > 1) and chunks per range
+int prefill_chunk_count(const Problem &p, int32_t n_seqs, int64_t total_tokens);
+int segment_chunks(const Problem &p, int chunks);
 // state-independent phase: chunk table + per-chunk WY factors into the workspace
-hipError_t launch_prepare(const Problem &p, const PrefillArgs &a, hipStream_t s);
+hipError_t launch_prepare(const Problem &p, const PrefillArgs &a, const Segment &sg, hipStream_t s);
 // sequential phase: reads the workspace written by launch_prepare (and runs
 // the gated RMSNorm epilogue when p.z is set)
-hipError_t launch_scan(const Problem &p, const PrefillArgs &a, hipStream_t s);
+hipError_t launch_scan(const Problem &p, const PrefillArgs &a, const Segment &sg, hipStream_t s);
 
 // Layer fusion passes (gdn_layer.hip).
 // New convolution state of every sequence: the last kConv - 1 inputs of its

@@ -102,7 +102,7 @@ template <int DK, int DV, typename E, bool SI = false> struct Geo {
 };
 
 struct WsLayout {
-    size_t entries, cstart, vblocks, kblocks, vblk, kblk, obuf, total;
+    size_t entries, cstart, vblocks, kblocks, vblk, kblk, obuf, carry, total;
     int max_chunks;
 };
 
@@ -144,7 +144,8 @@ WsLayout ws_layout(const Problem &p, int32_t n_seqs, int64_t T)
     L.kblk = (size_t)kblk_kib(p.d_k, bf, op_split(p)) * 1024;
     L.kblocks = L.vblocks + L.vblk * (size_t)L.max_chunks * p.H_v;
     L.obuf = align256(L.kblocks + L.kblk * (size_t)L.max_chunks * p.H_k);
-    L.total = L.obuf + (stage_o(p) ? sizeof(float) * (size_t)T * p.H_v * p.d_v : 0);
+    L.carry = align256(L.obuf + (stage_o(p) ? sizeof(float) * (size_t)T * p.H_v * p.d_v : 0));
+    L.total = L.carry + sizeof(float) * (size_t)n_seqs * p.H_v * p.d_k * p.d_v;
     return L;
 }
 
@@ -352,6 +353,7 @@ struct PrepParams {
     // head), for grids too small to fill the GPU (K K^T is then formed once
     // per value head)
     int head_split;
+    int chunk_base;    // blockIdx.x = 0 is this chunk of the batch
 };
 
 // LDS of the preparation kernel.  Rows are padded so that the row stride is
@@ -493,7 +495,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     float *sBetah = sRAh + NH * C;                              // [NH][C] beta_c          (columns of T for U0)
     float *sColh = sBetah + NH * C;                             // [NH][C] beta_c e^{G_c} / |k_c|  (columns of T for W)
 
-    const int chunk = blockIdx.x;
+    const int chunk = blockIdx.x + pp.chunk_base;
     const int ratio = pp.H_v / pp.H_k;
     const int kh = pp.head_split ? blockIdx.y / ratio : blockIdx.y;
     // value heads of this workgroup: [jbeg, jend) of the key head's ratio;
@@ -1000,6 +1002,11 @@ struct ScanParams {
     int H_k, H_v;
     int64_t slot_stride;
     int single_T;      // >= 0: one sequence of this many tokens, no chunk table
+    // chunks [seg_lo, seg_hi) of the batch; a sequence that began in an
+    // earlier range takes its state from carry, one that goes on past this
+    // range leaves it there ([sequence][H_v][DK][DV] fp32)
+    int seg_lo, seg_hi;
+    float *carry;
 };
 
 template <int DK, int DV, int CT, typename E> struct ScanLds {
@@ -1086,8 +1093,17 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
     u32x4 *myKf = sKf + ctl * (NKC * NS * 64);
 
     const bool single = sp.single_T >= 0;
-    const int cs = single ? 0 : sp.cstart[i];
-    const int ce = single ? (sp.single_T + C - 1) / C : sp.cstart[i + 1];
+    const int cs_seq = single ? 0 : sp.cstart[i];
+    const int ce_seq = single ? (sp.single_T + C - 1) / C : sp.cstart[i + 1];
+    // this launch's part of the sequence; an empty sequence (state copied
+    // through) belongs to the first range
+    const bool empty = cs_seq >= ce_seq;
+    const int cs = empty ? cs_seq : max(cs_seq, sp.seg_lo);
+    const int ce = empty ? cs_seq : min(ce_seq, sp.seg_hi);
+    if (empty ? sp.seg_lo != 0 : cs >= ce) return;      // uniform over the workgroup
+    const bool carried_in = !empty && cs_seq < sp.seg_lo;
+    const bool carried_out = !empty && ce_seq > sp.seg_hi;
+    float *carry = sp.carry + ((int64_t)i * sp.H_v + h) * DK * DV + col0 + n;
     const size_t vstride = (size_t)G::VBLK * 1024, kstride = (size_t)G::KBLK * 1024;
     const char *vbase = sp.vblocks + (size_t)h * vstride;
     const char *kbase = sp.kblocks + (size_t)kh * kstride;
@@ -1112,8 +1128,9 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
         floatx4 Sreg[NOWN][TPB];
         {
             const int sin = sp.state_in ? sp.slot_in[i] : -1;
-            const float *base = sin >= 0 ? sp.state_in + (int64_t)sin * sp.slot_stride + (int64_t)h * DK * DV + col0 + n
-                                         : nullptr;
+            const float *base = carried_in ? carry
+                              : sin >= 0   ? sp.state_in + (int64_t)sin * sp.slot_stride + (int64_t)h * DK * DV + col0 + n
+                                           : nullptr;
 #pragma unroll
             for (int o = 0; o < NOWN; ++o) {
                 const int kb = rt + 4 * o;
@@ -1244,8 +1261,8 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
         }
 
         const int sout = sp.slot_out[i];
-        if (sout >= 0) {
-            float *base = sp.state_out + (int64_t)sout * sp.slot_stride + (int64_t)h * DK * DV + col0 + n;
+        if (carried_out || sout >= 0) {
+            float *base = carried_out ? carry : sp.state_out + (int64_t)sout * sp.slot_stride + (int64_t)h * DK * DV + col0 + n;
 #pragma unroll
             for (int o = 0; o < NOWN; ++o) {
                 const int kb = rt + 4 * o;
@@ -1272,7 +1289,7 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
         }
         floatx4 qs4 = scal4(c0, ro);
         // the sequence's token range; its chunks are consecutive 64-token pieces
-        const int tbeg = single || cs >= ce ? 0 : sp.ent[cs].t0;
+        const int tbeg = single ? C * cs : cs >= ce ? 0 : sp.ent[cs].t0;
         const int tend = single ? sp.single_T : cs < ce ? sp.ent[ce - 1].t0 + sp.ent[ce - 1].len : 0;
         const uint32_t row_bytes = (uint32_t)(sp.H_v * DV * sizeof(OT));
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
@@ -1356,7 +1373,7 @@ struct WsPtrs {
     ChunkEntry *ent;
     int32_t *cstart;
     char *vblocks, *kblocks;
-    float *obuf;
+    float *obuf, *carry;
 };
 
 WsPtrs ws_ptrs(const Problem &p, const PrefillArgs &a)
@@ -1370,18 +1387,19 @@ WsPtrs ws_ptrs(const Problem &p, const PrefillArgs &a)
     w.vblocks = ws + w.L.vblocks;
     w.kblocks = ws + w.L.kblocks;
     w.obuf = reinterpret_cast<float *>(ws + w.L.obuf);
+    w.carry = reinterpret_cast<float *>(ws + w.L.carry);
     return w;
 }
 
 template <int DK, int DV, typename E>
-hipError_t prepare_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
+hipError_t prepare_t(const Problem &p, const PrefillArgs &a, const Segment &sg, hipStream_t st)
 {
     const WsPtrs w = ws_ptrs(p, a);
     // one sequence: cu_seqlens is [0, total_tokens] by contract, and both
     // kernels derive the chunks arithmetically (no chunk-table launch)
     const bool single = a.n_seqs == 1;
     hipError_t e = hipSuccess;
-    if (!single) {
+    if (!single && sg.first) {
         hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.n_seqs,
                            (int)a.total_tokens, w.L.max_chunks, w.hdr, w.ent, w.cstart);
         e = hipGetLastError();
@@ -1393,8 +1411,10 @@ hipError_t prepare_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
                   p.ssm_a ? Gates{p.ssm_a, p.ssm_dt, 1} : Gates{a.g, a.g, 0},
                   p.rs_qk, p.rs_v, p.conv_w,
                   // without a state pool the history loads read the taps (unused)
-                  a.conv_in ? a.conv_in : p.conv_w, a.slot_in, p.slot_stride, a.conv_in != nullptr, 0};
-    const int chunks = single ? (int)((a.total_tokens + C - 1) / C) : w.L.max_chunks;
+                  a.conv_in ? a.conv_in : p.conv_w, a.slot_in, p.slot_stride, a.conv_in != nullptr, 0, sg.lo};
+    const int all = single ? (int)((a.total_tokens + C - 1) / C) : w.L.max_chunks;
+    const int chunks = std::min(all, sg.hi) - sg.lo;
+    if (chunks <= 0) return hipSuccess;
     // A grid that leaves most workgroup slots empty (e.g. one 512-token
     // ubatch: 8 chunks x 16 key heads) is bound by one workgroup's latency;
     // splitting it by value head halves that chain for a little more work.
@@ -1418,14 +1438,14 @@ hipError_t prepare_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
 }
 
 template <int DK, int DV, typename E, typename OT, bool SI>
-hipError_t scan_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
+hipError_t scan_t(const Problem &p, const PrefillArgs &a, const Segment &sg, hipStream_t st)
 {
     const WsPtrs w = ws_ptrs(p, a);
     constexpr int CT = 1;    // column tiles per workgroup
     void *o = stage_o(p) ? static_cast<void *>(w.obuf) : a.out;
     ScanParams sp{a.state_in, a.state_out, o, a.slot_in, a.slot_out, w.cstart, w.ent,
                   w.vblocks, w.kblocks, p.H_k, p.H_v, p.slot_stride,
-                  a.n_seqs == 1 ? (int)a.total_tokens : -1};
+                  a.n_seqs == 1 ? (int)a.total_tokens : -1, sg.lo, sg.hi, w.carry};
     // With several sequences, one scan workgroup per CU: two workgroups on
     // one CU each run about 3x slower per chunk (they contend for its vector
     // memory path and VALU), so the reservation below (more LDS than half a
@@ -1437,46 +1457,47 @@ hipError_t scan_t(const Problem &p, const PrefillArgs &a, hipStream_t st)
     hipLaunchKernelGGL((scan_kernel<DK, DV, CT, E, OT, SI>), dim3(p.H_v, DV / (16 * CT), a.n_seqs),
                        dim3(CT * 512), lds, st, sp);
     e = hipGetLastError();
-    if (e == hipSuccess && p.z) e = launch_gated_norm(p, static_cast<const float *>(o), a.out, a.total_tokens, st);
+    if (e == hipSuccess && p.z && sg.last)
+        e = launch_gated_norm(p, static_cast<const float *>(o), a.out, a.total_tokens, st);
     return e;
 }
 
 template <int DK, int DV>
-hipError_t prepare_dv(const Problem &p, const PrefillArgs &a, hipStream_t st)
+hipError_t prepare_dv(const Problem &p, const PrefillArgs &a, const Segment &sg, hipStream_t st)
 {
-    return op_bf16(p) ? prepare_t<DK, DV, bf16_t>(p, a, st) : prepare_t<DK, DV, float>(p, a, st);
+    return op_bf16(p) ? prepare_t<DK, DV, bf16_t>(p, a, sg, st) : prepare_t<DK, DV, float>(p, a, sg, st);
 }
 
 template <int DK>
-hipError_t prepare_dk(const Problem &p, const PrefillArgs &a, hipStream_t st)
+hipError_t prepare_dk(const Problem &p, const PrefillArgs &a, const Segment &sg, hipStream_t st)
 {
     switch (p.d_v) {
-    case 32: return prepare_dv<DK, 32>(p, a, st);
-    case 64: return prepare_dv<DK, 64>(p, a, st);
-    case 128: return prepare_dv<DK, 128>(p, a, st);
+    case 32: return prepare_dv<DK, 32>(p, a, sg, st);
+    case 64: return prepare_dv<DK, 64>(p, a, sg, st);
+    case 128: return prepare_dv<DK, 128>(p, a, sg, st);
     }
     return hipErrorInvalidValue;
 }
 
 template <int DK, int DV>
-hipError_t scan_dv(const Problem &p, const PrefillArgs &a, hipStream_t st)
+hipError_t scan_dv(const Problem &p, const PrefillArgs &a, const Segment &sg, hipStream_t st)
 {
     // with the epilogue the scan writes fp32 o (staged or in place)
     const bool ob = p.out_bf16 && !p.z;
     if (op_split(p))        // the prologue's two-term operands; z is then set or not
-        return ob ? scan_t<DK, DV, bf16_t, bf16_t, true>(p, a, st) : scan_t<DK, DV, bf16_t, float, true>(p, a, st);
+        return ob ? scan_t<DK, DV, bf16_t, bf16_t, true>(p, a, sg, st) : scan_t<DK, DV, bf16_t, float, true>(p, a, sg, st);
     if (op_bf16(p))
-        return ob ? scan_t<DK, DV, bf16_t, bf16_t, false>(p, a, st) : scan_t<DK, DV, bf16_t, float, false>(p, a, st);
-    return ob ? scan_t<DK, DV, float, bf16_t, false>(p, a, st) : scan_t<DK, DV, float, float, false>(p, a, st);
+        return ob ? scan_t<DK, DV, bf16_t, bf16_t, false>(p, a, sg, st) : scan_t<DK, DV, bf16_t, float, false>(p, a, sg, st);
+    return ob ? scan_t<DK, DV, float, bf16_t, false>(p, a, sg, st) : scan_t<DK, DV, float, float, false>(p, a, sg, st);
 }
 
 template <int DK>
-hipError_t scan_dk(const Problem &p, const PrefillArgs &a, hipStream_t st)
+hipError_t scan_dk(const Problem &p, const PrefillArgs &a, const Segment &sg, hipStream_t st)
 {
     switch (p.d_v) {
-    case 32: return scan_dv<DK, 32>(p, a, st);
-    case 64: return scan_dv<DK, 64>(p, a, st);
-    case 128: return scan_dv<DK, 128>(p, a, st);
+    case 32: return scan_dv<DK, 32>(p, a, sg, st);
+    case 64: return scan_dv<DK, 64>(p, a, sg, st);
+    case 128: return scan_dv<DK, 128>(p, a, sg, st);
     }
     return hipErrorInvalidValue;
 }
@@ -1488,22 +1509,41 @@ size_t prefill_workspace_bytes(const Problem &p, int32_t n_seqs, int64_t total_t
     return ws_layout(p, n_seqs, total_tokens).total;
 }
 
-hipError_t launch_prepare(const Problem &p, const PrefillArgs &a, hipStream_t st)
+int prefill_chunk_count(const Problem &p, int32_t n_seqs, int64_t total_tokens)
+{
+    return n_seqs == 1 ? (int)((total_tokens + C - 1) / C) : (int)max_chunks(n_seqs, total_tokens);
+}
+
+int segment_chunks(const Problem &p, int chunks)
+{
+    const bool bf = op_bf16(p), si = op_split(p);
+    const size_t per = (size_t)p.H_v * vblk_kib(p.d_k, p.d_v, bf, si) * 1024 +
+                       (size_t)p.H_k * kblk_kib(p.d_k, bf, si) * 1024;
+    if ((size_t)chunks * per <= kOneRangeBytes) return std::max(chunks, 1);
+    const int fit = (int)std::max<size_t>(1, std::min<size_t>(kSegmentBytes / per, 0x7fffffff));
+    // whole rounds of the preparation grid (chunks x key heads over its
+    // workgroup slots), so that no range ends on a nearly empty round
+    const int slots = (bf && !p.conv_w ? 2 : 1) * cu_count();
+    const int round = std::max(1, slots / p.H_k);
+    return fit >= round ? fit / round * round : fit;
+}
+
+hipError_t launch_prepare(const Problem &p, const PrefillArgs &a, const Segment &sg, hipStream_t st)
 {
     switch (p.d_k) {
-    case 32: return prepare_dk<32>(p, a, st);
-    case 64: return prepare_dk<64>(p, a, st);
-    case 128: return prepare_dk<128>(p, a, st);
+    case 32: return prepare_dk<32>(p, a, sg, st);
+    case 64: return prepare_dk<64>(p, a, sg, st);
+    case 128: return prepare_dk<128>(p, a, sg, st);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_scan(const Problem &p, const PrefillArgs &a, hipStream_t st)
+hipError_t launch_scan(const Problem &p, const PrefillArgs &a, const Segment &sg, hipStream_t st)
 {
     switch (p.d_k) {
-    case 32: return scan_dk<32>(p, a, st);
-    case 64: return scan_dk<64>(p, a, st);
-    case 128: return scan_dk<128>(p, a, st);
+    case 32: return scan_dk<32>(p, a, sg, st);
+    case 64: return scan_dk<64>(p, a, sg, st);
+    case 128: return scan_dk<128>(p, a, sg, st);
     }
     return hipErrorInvalidValue;
 }

@@ -185,7 +185,11 @@ const char *gdn_last_error(void);
  * The workspace holds the chunk table and the per-chunk WY factors
  * (build_delta_net_chunking: k_cumdecay, the beta-weighted values and the
  * decayed q.k attention, plus q and k in matrix-core operand order) between
- * the two phases.
+ * the two phases, and one d_k x d_v fp32 state per (sequence, value head):
+ * gdn_chunked_prefill runs a batch whose factors outgrow the GPU's 256 MB
+ * last-level cache as consecutive ranges of chunks (preparation, then scan,
+ * per range; results are bitwise those of one range), and a sequence that
+ * crosses a range boundary keeps its state there in between.
  */
 gdn_status gdn_prefill_workspace_size(const gdn_dims *dims, int32_t n_seqs,
                                       int64_t total_tokens, size_t *bytes);

@@ -160,3 +160,46 @@ def test_prefill_then_decode_equals_longer_prefill():
     compare_prefill(case, out, pool, ref_o, ref_s)
     e, _ = rel_err(out.cpu().numpy(), out_full.cpu().numpy())
     assert e <= TOL["bf16"]
+
+
+def _split_phase(case, d):
+    """prepare + scan as two calls: always one chunk range over the batch."""
+    import gated_deltanet_rule_amd as gdn
+    out = torch.empty(d["v"].shape, dtype=torch.float32, device="cuda")
+    pool = d["pool"].clone()
+    plan = gdn.PrefillPlan(d["q"], d["v"], out, case.n_seqs, state=pool)
+    plan.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"])
+    plan.scan(d["pool"], pool, out, d["slot_in"], d["slot_out"])
+    torch.cuda.synchronize()
+    return out, pool
+
+
+def test_long_prefill_runs_in_cache_sized_ranges():
+    """A long single sequence (129 chunks, weak decay so the state carried
+    from range to range matters) runs as several chunk ranges inside one
+    call: parity on sampled heads, and bitwise equal to the split-phase
+    calls, which run the whole batch as one range."""
+    case = gi.make_case("ranges_T8229", [8229], dtype="bf16", seed=91, decay="weak",
+                        **gi.QWEN3_NEXT_HEADS)
+    d = dev_case(case)
+    out, pool = gpu_prefill(case, d=d, inplace=False)
+    o1, p1 = _split_phase(case, d)
+    assert torch.equal(out, o1) and torch.equal(pool, p1)
+    ref_o, ref_s = oracle_case(case, heads=[0, 5, 16, 31])
+    compare_prefill(case, out, pool, ref_o, ref_s, heads=[0, 5, 16, 31])
+
+
+def test_varlen_sequences_across_range_boundaries():
+    """Sequences that start and end inside ranges, span several ranges, are
+    empty or a single token, with the zero-state slot and scattered slots."""
+    lengths = [1900, 0, 1, 2100, 64 * 33, 7, 3000, 65]
+    case = gi.make_case("ranges_varlen", lengths, dtype="bf16", seed=92, decay="weak",
+                        n_slots=20, scatter_slots=True, **gi.QWEN3_NEXT_HEADS)
+    case.slot_in[3] = -1
+    d = dev_case(case)
+    out, pool = gpu_prefill(case, d=d, inplace=False)
+    o1, p1 = _split_phase(case, d)
+    assert torch.equal(out, o1) and torch.equal(pool, p1)
+    heads = [0, 9, 22, 31]
+    ref_o, ref_s = oracle_case(case, heads=heads)
+    compare_prefill(case, out, pool, ref_o, ref_s, heads=heads)
