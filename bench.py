@@ -244,6 +244,22 @@ def bench_decode(gdn, dev, reps=3):
                      "bytes_per_launch": by, "achieved_gbs": gbs,
                      "frac": gbs / PEAK_HBM_GBS}
     assert torch.isfinite(outs).all()
+    # context for the HBM fraction: a plain device copy (PyTorch's own copy
+    # kernel) of the pool, i.e. the same bytes read once and written once
+    copy_ms = []
+    for rep in range(21):
+        t = Timer(stream, 2)
+        t.mark(0)
+        pool2.copy_(pool)
+        t.mark(1)
+        torch.cuda.synchronize()
+        if rep:
+            copy_ms.append(t.ms(0, 1))
+    cms = statistics.median(copy_ms)
+    cby = 2 * pool.numel() * pool.element_size()
+    res["copy_reference"] = {"what": "torch copy_ of the 128 MiB pool into a second pool",
+                             "bytes": cby, "ms": cms, "achieved_gbs": cby / (cms * 1e-3) / 1e9,
+                             "frac": cby / (cms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     ip = res["in_place"]
     return {"workload": "decode: 64 sequences x 128 steps, H_k=16 H_v=32 d=128, bf16 in, "
                         "fp32 out, fp32 state slots (128 MiB pool)",
@@ -254,7 +270,7 @@ def bench_decode(gdn, dev, reps=3):
                          "traffic_unit": "bytes per launch",
                          "kernel": "decode_kernel", "bytes_per_launch": ip["bytes_per_launch"],
                          "mean_launch_ms": ip["mean_launch_ms"]},
-            "ping_pong": res["ping_pong"], "in_place": ip}
+            "ping_pong": res["ping_pong"], "in_place": ip, "copy_reference": res["copy_reference"]}
 
 
 def bench_decode_multi(gdn, dev, tokens=4, reps=20):
@@ -513,7 +529,8 @@ def main():
     if args.decode_only:
         log("decode 64x128 ...")
         dec = bench_decode(gdn, dev, reps=1)
-        log(f"  {dec['ms_per_step']*1e3:.2f} us/step, {dec['roofline']['achieved']:.0f} GB/s")
+        log(f"  {dec['ms_per_step']*1e3:.2f} us/step, {dec['roofline']['achieved']:.0f} GB/s "
+            f"(device copy of the pool: {dec['copy_reference']['achieved_gbs']:.0f} GB/s)")
         return
     log("prefill T=4096 ...")
     case, pf = bench_prefill(gdn, dev, args.steps, args.warmup)
@@ -522,7 +539,8 @@ def main():
         return
     log("decode 64x128 ...")
     dec = bench_decode(gdn, dev)
-    log(f"  {dec['ms_per_step']*1e3:.2f} us/step, {dec['roofline']['achieved']:.0f} GB/s")
+    log(f"  {dec['ms_per_step']*1e3:.2f} us/step, {dec['roofline']['achieved']:.0f} GB/s "
+        f"(device copy of the pool: {dec['copy_reference']['achieved_gbs']:.0f} GB/s)")
     extra = {}
     log("multi-token decode 64x4 ...")
     extra["decode_multi"] = bench_decode_multi(gdn, dev)
