@@ -24,7 +24,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_layer.hip", "gdn_prefill.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_check.hip", "gdn_decode.hip", "gdn_layer.hip", "gdn_prefill.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/gdn.h"
@@ -114,6 +115,32 @@ float *ssm_part(const gdn::Problem &p, float *s) { return s ? s + p.conv_state :
 gdn_status hip_status(hipError_t e, const char *what)
 {
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    return GDN_OK;
+}
+
+// GDN_CHECK=1: validate the device-side preconditions before any kernel of
+// the call is launched (synchronises `s`; debugging aid, not for timing).
+bool check_mode()
+{
+    const char *e = getenv("GDN_CHECK");
+    return e && e[0] == '1' && e[1] == 0;
+}
+
+gdn_status device_check(const int32_t *cu, int32_t n, int64_t T, const int32_t *slot_in,
+                        const int32_t *slot_out, hipStream_t s)
+{
+    if (!check_mode()) return GDN_OK;
+    int v = 0;
+    gdn_status st = hip_status(gdn::run_check(cu, n, T, slot_in, slot_out, s, &v), "GDN_CHECK validation");
+    if (st != GDN_OK) return st;
+    if (v & gdn::kCheckCuStart) return fail(GDN_ERR_INVALID_ARG, "GDN_CHECK: cu_seqlens[0] is not 0");
+    if (v & gdn::kCheckCuEnd)
+        return fail(GDN_ERR_INVALID_ARG, "GDN_CHECK: cu_seqlens[n_seqs] differs from total_tokens (%lld)",
+                    (long long)T);
+    if (v & gdn::kCheckCuOrder) return fail(GDN_ERR_INVALID_ARG, "GDN_CHECK: cu_seqlens is not non-decreasing");
+    if (v & gdn::kCheckSlotDup) return fail(GDN_ERR_INVALID_ARG, "GDN_CHECK: two sequences write the same slot");
+    if (v & gdn::kCheckSlotAlias)
+        return fail(GDN_ERR_INVALID_ARG, "GDN_CHECK: a sequence writes a slot that another sequence reads");
     return GDN_OK;
 }
 
@@ -232,6 +259,8 @@ gdn_status gdn_prefill_prepare(const gdn_dims *dims, const void *q, const void *
     if (st == GDN_OK) st = check_prepare_inputs(q, k, v, g, beta, cu_seqlens);
     if (st == GDN_OK) st = check_workspace(p, n_seqs, total_tokens, workspace, workspace_bytes);
     if (st != GDN_OK) return st;
+    st = device_check(cu_seqlens, n_seqs, total_tokens, nullptr, nullptr, static_cast<hipStream_t>(stream));
+    if (st != GDN_OK) return st;
     gdn::PrefillArgs a{q, k, v, g, beta, nullptr, nullptr, nullptr, cu_seqlens, nullptr,
                        nullptr, n_seqs, total_tokens, workspace, nullptr, nullptr};
     return hip_status(gdn::launch_prepare(p, a, gdn::Segment{}, static_cast<hipStream_t>(stream)), "prepare");
@@ -255,6 +284,8 @@ gdn_status gdn_prefill_scan(const gdn_dims *dims, const float *state_in, float *
     gdn::PrefillArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, state_in, state_out, out, nullptr, slot_in,
                        slot_out, n_seqs, total_tokens, const_cast<void *>(workspace), nullptr, nullptr};
     hipStream_t s = static_cast<hipStream_t>(stream);
+    st = device_check(nullptr, n_seqs, n_seqs, slot_in, slot_out, s);
+    if (st != GDN_OK) return st;
     return hip_status(gdn::launch_scan(p, a, gdn::Segment{}, s), "scan");
 }
 
@@ -281,6 +312,8 @@ gdn_status gdn_chunked_prefill(const gdn_dims *dims, const void *q, const void *
                        cu_seqlens, slot_in, slot_out, n_seqs, total_tokens, workspace,
                        state_in, state_out};
     hipStream_t s = static_cast<hipStream_t>(stream);
+    st = device_check(cu_seqlens, n_seqs, total_tokens, slot_in, slot_out, s);
+    if (st != GDN_OK) return st;
     // consecutive chunk ranges within the cache budget
     const int chunks = gdn::prefill_chunk_count(p, n_seqs, total_tokens);
     const int per = gdn::segment_chunks(p, chunks);
@@ -322,6 +355,8 @@ gdn_status gdn_recurrent_step(const gdn_dims *dims, const void *q, const void *k
     gdn::DecodeArgs a{q, k, v, g, beta, ssm_part(p, state_in), ssm_part(p, state_out), out,
                       slot_in, slot_out, n_seqs, state_in, state_out};
     hipStream_t s = static_cast<hipStream_t>(stream);
+    st = device_check(nullptr, n_seqs, n_seqs, slot_in, slot_out, s);
+    if (st != GDN_OK) return st;
     st = hip_status(gdn::launch_decode(p, a, s), "decode");
     if (st == GDN_OK && p.conv_w)
         st = hip_status(gdn::launch_conv_state(p, qkv, nullptr, -1, n_seqs, n_seqs, state_in, state_out,
@@ -350,6 +385,8 @@ gdn_status gdn_recurrent_multi(const gdn_dims *dims, const void *q, const void *
     gdn::DecodeMultiArgs a{q, k, v, g, beta, ssm_part(p, state_in), ssm_part(p, state_out), out,
                            cu_seqlens, slot_in, slot_out, n_seqs, total_tokens, state_in, state_out};
     hipStream_t s = static_cast<hipStream_t>(stream);
+    st = device_check(cu_seqlens, n_seqs, total_tokens, slot_in, slot_out, s);
+    if (st != GDN_OK) return st;
     st = hip_status(gdn::launch_decode_multi(p, a, s), "multi-token decode");
     if (st == GDN_OK && p.conv_w)
         st = hip_status(gdn::launch_conv_state(p, qkv, cu_seqlens, -1, n_seqs, total_tokens, state_in,

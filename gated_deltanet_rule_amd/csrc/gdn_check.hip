@@ -1,0 +1,69 @@
+// gdn_check.hip -- validation of the device-side preconditions of a call
+// (GDN_CHECK=1 only).  The calls never read device data on the host; their
+// kernels clamp what they index with, so bad sequence bounds or slot lists
+// give wrong results rather than faults.  In check mode the library runs this
+// kernel first, reads its verdict back (synchronising the stream) and
+// rejects the call before any other kernel is launched.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kCheckMaxPairs = 16384;
+
+// One workgroup.  cu: null for one token per sequence (decode); slot_out
+// null: no slot lists (slot_in may be null on its own).  The verdict
+// (check_* bits) is gathered in LDS and written by thread 0 at the end, so
+// the result buffer needs no clearing.
+__global__ __launch_bounds__(1024) void check_kernel(const int32_t *__restrict__ cu, int32_t n, int64_t T,
+                                                     const int32_t *__restrict__ slot_in,
+                                                     const int32_t *__restrict__ slot_out, int *result)
+{
+    __shared__ int verdict;
+    if (threadIdx.x == 0) verdict = 0;
+    __syncthreads();
+    int bad = 0;
+    if (cu) {
+        if (threadIdx.x == 0) {
+            if (cu[0] != 0) bad |= kCheckCuStart;
+            if ((int64_t)cu[n] != T) bad |= kCheckCuEnd;
+        }
+        for (int i = threadIdx.x; i < n; i += blockDim.x)
+            if (cu[i + 1] < cu[i]) bad |= kCheckCuOrder;
+    }
+    // out slots pairwise distinct; no sequence writes a slot another reads
+    // (all pairs: batches above kCheckMaxPairs sequences skip this part; a
+    // call without slot lists, the preparation half, has none to check)
+    const int64_t pairs = slot_out && n <= kCheckMaxPairs ? (int64_t)n * n : 0;
+    for (int64_t x = threadIdx.x; x < pairs; x += blockDim.x) {
+        const int i = (int)(x / n), j = (int)(x % n);
+        if (i == j) continue;
+        const int oi = slot_out[i];
+        if (oi < 0) continue;
+        if (oi == slot_out[j]) bad |= kCheckSlotDup;
+        if (slot_in && oi == slot_in[j]) bad |= kCheckSlotAlias;
+    }
+    if (bad) atomicOr(&verdict, bad);
+    __syncthreads();
+    if (threadIdx.x == 0) *result = verdict;
+}
+
+__device__ int g_check_result;
+
+}  // namespace
+
+hipError_t run_check(const int32_t *cu, int32_t n, int64_t T, const int32_t *slot_in, const int32_t *slot_out,
+                     hipStream_t s, int *verdict)
+{
+    int *res = nullptr;
+    hipError_t e = hipGetSymbolAddress(reinterpret_cast<void **>(&res), HIP_SYMBOL(g_check_result));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(check_kernel, dim3(1), dim3(1024), 0, s, cu, n, T, slot_in, slot_out, res);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipMemcpyAsync(verdict, res, sizeof(int), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e;
+}
+
+}  // namespace gdn
