@@ -731,13 +731,17 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     // 2. raw q and k^T of this key head as operand fragments for the scan
     {
         char *kb_blk = pp.kblocks + ((size_t)chunk * pp.H_k + kh) * ((size_t)G::KBLK * 1024);
-        for (int f = w; f < G::NQF; f += 4) {
+#pragma unroll
+        for (int ff = 0; ff < G::NQF / 4; ++ff) {
+            const int f = w + 4 * ff;
             const int rt = f / NKD, kb = f % NKD;
             store_frag<E>(kb_blk + G::F_Q * 1024, f, lane, M::load_rm(sX + (16 * rt + n) * LDX, kb * KB, qd));
             if constexpr (SI)
                 store_frag<E>(kb_blk + G::F_QL * 1024, f, lane, M::load_rm(sXL + (16 * rt + n) * LDX, kb * KB, qd));
         }
-        for (int f = w; f < G::NKF; f += 4) {
+#pragma unroll
+        for (int ff = 0; ff < G::NKF / 4; ++ff) {
+            const int f = w + 4 * ff;
             const int mt = f / NKC, kc = f % NKC;
             store_frag<E>(kb_blk + G::F_KT * 1024, f, lane, TR::frag(sK, LDK, kc * KB, 16 * mt, lane));
             if constexpr (SI)
