@@ -2,7 +2,7 @@
 // (GDN_CHECK=1 only).  The calls never read device data on the host; their
 // kernels clamp what they index with, so bad sequence bounds or slot lists
 // give wrong results rather than faults.  In check mode the library runs this
-// kernel first, reads its verdict back (synchronising the stream) and
+// kernel first, reads its flags back (synchronising the stream) and
 // rejects the call before any other kernel is launched.
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -13,15 +13,15 @@ namespace {
 constexpr int kCheckMaxPairs = 16384;
 
 // One workgroup.  cu: null for one token per sequence (decode); slot_out
-// null: no slot lists (slot_in may be null on its own).  The verdict
+// null: no slot lists (slot_in may be null on its own).  The flags
 // (check_* bits) is gathered in LDS and written by thread 0 at the end, so
 // the result buffer needs no clearing.
 __global__ __launch_bounds__(1024) void check_kernel(const int32_t *__restrict__ cu, int32_t n, int64_t T,
                                                      const int32_t *__restrict__ slot_in,
                                                      const int32_t *__restrict__ slot_out, int *result)
 {
-    __shared__ int verdict;
-    if (threadIdx.x == 0) verdict = 0;
+    __shared__ int flags;
+    if (threadIdx.x == 0) flags = 0;
     __syncthreads();
     int bad = 0;
     if (cu) {
@@ -44,9 +44,9 @@ __global__ __launch_bounds__(1024) void check_kernel(const int32_t *__restrict__
         if (oi == slot_out[j]) bad |= kCheckSlotDup;
         if (slot_in && oi == slot_in[j]) bad |= kCheckSlotAlias;
     }
-    if (bad) atomicOr(&verdict, bad);
+    if (bad) atomicOr(&flags, bad);
     __syncthreads();
-    if (threadIdx.x == 0) *result = verdict;
+    if (threadIdx.x == 0) *result = flags;
 }
 
 __device__ int g_check_result;
@@ -54,14 +54,14 @@ __device__ int g_check_result;
 }  // namespace
 
 hipError_t run_check(const int32_t *cu, int32_t n, int64_t T, const int32_t *slot_in, const int32_t *slot_out,
-                     hipStream_t s, int *verdict)
+                     hipStream_t s, int *flags)
 {
     int *res = nullptr;
     hipError_t e = hipGetSymbolAddress(reinterpret_cast<void **>(&res), HIP_SYMBOL(g_check_result));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(check_kernel, dim3(1), dim3(1024), 0, s, cu, n, T, slot_in, slot_out, res);
     e = hipGetLastError();
-    if (e == hipSuccess) e = hipMemcpyAsync(verdict, res, sizeof(int), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(flags, res, sizeof(int), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     return e;
 }

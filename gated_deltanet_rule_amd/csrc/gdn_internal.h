@@ -120,14 +120,14 @@ hipError_t launch_scan(const Problem &p, const PrefillArgs &a, const Segment &sg
 
 // Check mode (GDN_CHECK=1, gdn_check.hip): validates cu_seqlens (null: one
 // token per sequence) and the slot lists of a call on the device, then
-// synchronises the stream and returns the verdict, a set of these bits.
+// synchronises the stream and returns its findings, a set of these bits.
 constexpr int kCheckCuStart = 1;     // cu_seqlens[0] != 0
 constexpr int kCheckCuEnd = 2;       // cu_seqlens[n_seqs] != total_tokens
 constexpr int kCheckCuOrder = 4;     // cu_seqlens decreases somewhere
 constexpr int kCheckSlotDup = 8;     // two sequences write the same slot
 constexpr int kCheckSlotAlias = 16;  // a sequence writes a slot another one reads
 hipError_t run_check(const int32_t *cu, int32_t n, int64_t T, const int32_t *slot_in, const int32_t *slot_out,
-                     hipStream_t s, int *verdict);
+                     hipStream_t s, int *flags);
 
 // Layer fusion passes (gdn_layer.hip).
 // New convolution state of every sequence: the last kConv - 1 inputs of its

@@ -58,13 +58,17 @@
  *     returned, with a message from gdn_last_error().  Device-resident
  *     preconditions (cu_seqlens starting at 0, non-decreasing and ending at
  *     total_tokens; slot indices in range; distinct output slots; no output
- *     slot read by another sequence) are the caller's duty: the kernels
- *     clamp the indices they use, so violations give wrong results, not
- *     faults.  With the environment variable GDN_CHECK=1 every call first
+ *     slot read by another sequence) are the caller's duty.  The kernels
+ *     clamp sequence bounds into [0, total_tokens], so bad cu_seqlens give
+ *     wrong results, not out-of-range accesses; a slot index outside the
+ *     pool addresses memory outside it.  With the environment variable
+ *     GDN_CHECK=1 every call first
  *     validates them on the device (one small kernel), waits for the
- *     verdict (a stream synchronisation: a debugging aid, not for timed or
+ *     result (a stream synchronisation: a debugging aid, not for timed or
  *     captured code) and returns GDN_ERR_INVALID_ARG, enqueueing nothing
- *     else, if one fails.  Slot indices are checked for distinctness and
+ *     else, if one fails (checked calls made at the same time on one device
+ *     share the word the result is read from: make them one at a time).
+ *     Slot indices are checked for distinctness and
  *     aliasing only (the pool size is not an argument), and only for up to
  *     16384 sequences per call.  The library never aborts or throws.
  *   - Thread safety: calls may be made from several host threads; the error
