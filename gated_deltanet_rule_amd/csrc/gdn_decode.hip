@@ -272,6 +272,25 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(RecParams P)
 // registers from token to token.  FUSED (here and in decode_kernel):
 // prologue and/or epilogue present; the plain instantiation carries none of
 // their code or registers.
+// Sum over the row groups of one wave: lanes that hold the same column group
+// (lane mod CG) and different row groups.
+template <int CG>
+__device__ __forceinline__ float rg_wave_sum(float x)
+{
+    if constexpr (CG <= 8) x += __shfl_xor(x, 8, 64);
+    if constexpr (CG <= 16) x += __shfl_xor(x, 16, 64);
+    // lanes l and l ^ 32 (v_permlane32_swap with both operands x: the low
+    // half of the first result and the high half of the second hold x, the
+    // other halves x of the partner lane).  The results pass through an
+    // empty asm: with identical operands the compiler otherwise takes the
+    // two results for one and adds the first to itself.
+    const unsigned a = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+    unsigned lo = r[0], hi = r[1];
+    asm volatile("" : "+v"(lo), "+v"(hi));
+    return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+}
+
 template <int DK, int DV, typename E, typename OT, bool FUSED>
 __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(RecParams P)
 {
@@ -296,7 +315,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(RecParams 
 
     __shared__ float sk[2][DK];
     __shared__ float sq[2][DK];
-    __shared__ float4 red[2][2][RG][CG];
+    constexpr int NW = kDecodeThreads / 64;
+    __shared__ float4 red[2][2][NW][CG];
 
     // tokens of this sequence (clamped so that bad cu_seqlens stay in range)
     const int tb = min(max(P.cu[i], 0), P.T);
@@ -416,12 +436,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(RecParams 
             pk.x += s[r].x * a; pk.y += s[r].y * a; pk.z += s[r].z * a; pk.w += s[r].w * a;
             pq.x += s[r].x * c; pq.y += s[r].y * c; pq.z += s[r].z * c; pq.w += s[r].w * c;
         }
-        red[b][0][rg][cg] = pk;
-        red[b][1][rg][cg] = pq;
+        // the wave's row groups first (lane exchanges), then the waves (LDS)
+        pk.x = rg_wave_sum<CG>(pk.x); pk.y = rg_wave_sum<CG>(pk.y); pk.z = rg_wave_sum<CG>(pk.z); pk.w = rg_wave_sum<CG>(pk.w);
+        pq.x = rg_wave_sum<CG>(pq.x); pq.y = rg_wave_sum<CG>(pq.y); pq.z = rg_wave_sum<CG>(pq.z); pq.w = rg_wave_sum<CG>(pq.w);
+        if (lane < CG) {
+            red[b][0][tid >> 6][cg] = pk;
+            red[b][1][tid >> 6][cg] = pq;
+        }
         lds_sync();
         float4 tk = make_float4(0.f, 0.f, 0.f, 0.f), tq = tk;
-#pragma unroll 8
-        for (int j = 0; j < RG; ++j) {
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
             const float4 a = red[b][0][j][cg], c = red[b][1][j][cg];
             tk.x += a.x; tk.y += a.y; tk.z += a.z; tk.w += a.w;
             tq.x += c.x; tq.y += c.y; tq.z += c.z; tq.w += c.w;
