@@ -63,9 +63,9 @@ C = 64
 PREFILL_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
                for f in ("gdn_prefill.hip", "gdn_mfma.h", "gdn_device.h", "gdn_internal.h")]
 MEASURED_TRAFFIC = {
-    "source_sha256": "292cc6da3faa41d01eda6bc8a3e5391c971aeecdfcd723cc50c50a69c20d7c8f",
+    "source_sha256": "ffd8e2e9f5560379d901567a25c1783756346e756255a51b058c40688543b192",
     "scan": (100010.6 * 2.000 + 67584.0 * 1.000) * 1024,
-    "prepare": (40305.6 * 2.000 + 165145.9 * 1.000) * 1024,
+    "prepare": (40810.2 * 2.000 + 165163.0 * 1.000) * 1024,
 }
 
 
@@ -74,8 +74,8 @@ MEASURED_TRAFFIC = {
 DECODE_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
               for f in ("gdn_decode.hip", "gdn_device.h", "gdn_internal.h")]
 MEASURED_DECODE_TRAFFIC = {
-    "source_sha256": "16f662346a299f3c6e246ed3ede85c482f7feb19a8f54e71ab8b14df9fb6610b",
-    "decode": (66140.1 * 2.000 + 132096.0 * 1.000) * 1024,
+    "source_sha256": "15794d35050744c968397d72a52aedc429cf45fbd78c9cc84caec091a0c030ef",
+    "decode": (66141.1 * 2.000 + 132096.0 * 1.000) * 1024,
 }
 
 
