@@ -203,3 +203,23 @@ def test_varlen_sequences_across_range_boundaries():
     heads = [0, 9, 22, 31]
     ref_o, ref_s = oracle_case(case, heads=heads)
     compare_prefill(case, out, pool, ref_o, ref_s, heads=heads)
+
+
+@pytest.mark.parametrize("n_seqs", [1500, 5000])
+def test_many_sequences(n_seqs):
+    """Thousands of short ragged sequences in one call (empty ones included):
+    the chunk table's loop over 1024-sequence blocks, and above 4096
+    sequences its direct write of the descriptors."""
+    rng = np.random.default_rng(n_seqs)
+    lengths = [int(x) for x in rng.choice([0, 1, 2, 3, 17, 64, 65, 130], size=n_seqs)]
+    case = gi.make_case(f"many_{n_seqs}", lengths, 1, 2, 32, 32, "bf16", seed=n_seqs + 1,
+                        decay="weak", n_slots=n_seqs, scatter_slots=True)
+    _check(case)
+
+
+def test_single_call_65536_tokens():
+    """The long-context workload as one call: 1024 chunks in 32 chunk ranges
+    (sampled heads)."""
+    case = gi.make_case("one_call_65536", [65536], dtype="bf16", seed=93, decay="weak",
+                        **gi.QWEN3_NEXT_HEADS)
+    _check(case, heads=[0, 13, 31])
