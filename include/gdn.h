@@ -73,6 +73,9 @@
  *     16384 sequences per call.  The library never aborts or throws.
  *   - Thread safety: calls may be made from several host threads; the error
  *     message is thread-local.
+ *   - Graph capture: a call enqueues kernels only (no allocation, memset or
+ *     synchronisation), so it may be captured into a HIP graph and replayed
+ *     (with GDN_CHECK=1 a call synchronises and cannot be captured).
  */
 #ifndef GDN_H
 #define GDN_H
