@@ -456,11 +456,43 @@ def bench_stream(gdn, dev, reps=2):
         torch.cuda.synchronize()
         times.append(t.ms(0, 1))
     ms = statistics.median(times)
+    eager_out, eager_pool = out.clone(), pool.clone()
+    # the same 256 launches captured once into a HIP graph and replayed: the
+    # host's launch gaps between the short kernels drop out
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        pool.copy_(d["pool"])
+        run()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gstream = torch.cuda.current_stream()
+        for s0 in range(0, T, U):
+            sl_in = d["slot_in"] if s0 == 0 else d["slot_out"]
+            plan.prepare(d["q"][s0:s0 + U], d["k"][s0:s0 + U], d["v"][s0:s0 + U], d["g"][s0:s0 + U],
+                         d["beta"][s0:s0 + U], cu, stream=gstream)
+            plan.scan(pool, pool, out[s0:s0 + U], sl_in, d["slot_out"], stream=gstream)
+    gtimes = []
+    for _ in range(reps + 1):
+        pool.copy_(d["pool"])
+        t = Timer(stream, 2)
+        torch.cuda.synchronize()
+        t.mark(0)
+        graph.replay()
+        t.mark(1)
+        torch.cuda.synchronize()
+        gtimes.append(t.ms(0, 1))
+    assert torch.equal(out, eager_out) and torch.equal(pool, eager_pool), "graph replay differs from eager"
+    gms = statistics.median(gtimes[1:])
     fp, fs = prefill_flops_per_token_head(case.H_k, case.H_v, case.d_k, case.d_v)
     tf = (fp + fs) * T * case.H_v / (ms * 1e-3) / 1e12
     return {"workload": "stream: 65536 tokens as 128 calls of 512, state carried in place",
             "ms_total": ms, "us_per_call": ms * 1e3 / (T // U), "tokens_s": T / (ms * 1e-3),
-            "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}
+            "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS,
+            "hip_graph": {"ms_total": gms, "us_per_call": gms * 1e3 / (T // U),
+                          "tokens_s": T / (gms * 1e-3)}}
 
 
 def cpu_baseline(case, min_s=10.0, max_reps=40):
@@ -557,6 +589,8 @@ def main():
         extra["varlen"] = bench_varlen(gdn, dev)
         log("stream 65536 ...")
         extra["stream"] = bench_stream(gdn, dev)
+        log(f"  {extra['stream']['us_per_call']:.1f} us/call, "
+            f"{extra['stream']['hip_graph']['us_per_call']:.1f} us/call replayed from a HIP graph")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
