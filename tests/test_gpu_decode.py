@@ -83,3 +83,10 @@ def test_decode_deterministic():
     o1, p1 = run_decode(dc)
     o2, p2 = run_decode(dc)
     assert torch.equal(o1, o2) and torch.equal(p1, p2)
+
+
+def test_decode_f32_inputs_bf16_output():
+    dc = gi.make_decode("dec_f32_bf16out", 6, 7, 2, 4, 64, 128, "f32", seed=95, decay="weak")
+    outs, pool = run_decode(dc, out_dtype=torch.bfloat16)
+    ref_o, ref_s = oracle_decode(dc)
+    compare_decode(dc, outs, pool, ref_o, ref_s)

@@ -90,3 +90,9 @@ def test_agrees_with_chunked_prefill_and_single_step():
     torch.cuda.synchronize()
     assert torch.allclose(o1, o2, rtol=1e-5, atol=1e-6)
     assert torch.allclose(s1, s2, rtol=1e-5, atol=1e-6)
+
+
+def test_f32_inputs_bf16_output():
+    case = gi.make_case("multi_f32_bf16out", [0, 1, 3, 7, 16], 2, 4, 128, 32, "f32", seed=96,
+                        decay="weak", n_slots=6, scatter_slots=True)
+    _check(case, out_dtype=torch.bfloat16)

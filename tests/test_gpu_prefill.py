@@ -223,3 +223,11 @@ def test_single_call_65536_tokens():
     case = gi.make_case("one_call_65536", [65536], dtype="bf16", seed=93, decay="weak",
                         **gi.QWEN3_NEXT_HEADS)
     _check(case, heads=[0, 13, 31])
+
+
+def test_f32_inputs_bf16_output():
+    """fp32 inputs (fp32 matrix-core operands) with a bf16 output: the output
+    is rounded once from fp32, held to 1e-4 rms + 2^-8 |ref|."""
+    case = gi.make_case("f32_in_bf16_out", [1, 63, 64, 65, 200, 0], 2, 4, 64, 32, "f32", seed=94,
+                        decay="weak", n_slots=8, scatter_slots=True)
+    _check(case, out_dtype=torch.bfloat16)
