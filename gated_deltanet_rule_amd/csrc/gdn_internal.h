@@ -106,9 +106,12 @@ struct Segment {
 // A batch whose factors fit kOneRangeBytes runs as one range (a second
 // launch pair costs more than the cache misses it saves); a longer one runs
 // in ranges of at most kSegmentBytes of factors, which leaves room in the
-// cache for the range's inputs and outputs.
-constexpr size_t kOneRangeBytes = 168u << 20;
-constexpr size_t kSegmentBytes = 96u << 20;
+// cache for the range's outputs.  Measured at Qwen3-Next heads: 5120 tokens
+// (206 MiB of factors) 165 us as one range against 186 us as two; the fused
+// layer's 4096 tokens (226 MiB) 350 us as one range against 330 us as two;
+// 8192 tokens 281 us in ranges of 32 chunks against 324 us in ranges of 64.
+constexpr size_t kOneRangeBytes = 212u << 20;
+constexpr size_t kSegmentBytes = 128u << 20;
 // chunks of a batch (an upper bound when n_seqs > 1) and chunks per range
 int prefill_chunk_count(const Problem &p, int32_t n_seqs, int64_t total_tokens);
 int segment_chunks(const Problem &p, int chunks);
