@@ -7,12 +7,14 @@ Headline (`value`): chunked-prefill throughput in tokens/s on the single-layer
 Qwen3-Next-shaped prefill (1 sequence, T=4096, H_k=16, H_v=32, d_k=d_v=128,
 bf16 q/k/v, fp32 g/beta/state, fp32 output, chunk 64).  One step = one
 gdn_prefill_prepare + gdn_prefill_scan over that batch (every prefill row of
-the path), inputs resident in HBM.  W untimed warm-up steps, then exactly K
-timed steps between two device synchronisations.
+the path), inputs resident in HBM.  The step first runs untimed for 100 ms so that the
+GPU's clocks settle, then W untimed warm-up steps, then exactly K timed steps
+between two device synchronisations.
 
 Alongside (same JSON line):
   roofline      the prefill's dominant kernel, from HIP events recorded on the
-                stream the kernels run on: algorithmic flops per launch
+                stream the kernels run on around K launches of that kernel
+                back to back (after the timed steps): algorithmic flops per launch
                 (per token per value head: 8*C*d + 6*d^2 for the whole
                 prefill, split 4*C*d_k/r + 2*C*d_k for the preparation and
                 4*C*d_v + 6*d_k*d_v for the scan) / mean launch time, against
@@ -63,9 +65,9 @@ C = 64
 PREFILL_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
                for f in ("gdn_prefill.hip", "gdn_mfma.h", "gdn_device.h", "gdn_internal.h")]
 MEASURED_TRAFFIC = {
-    "source_sha256": "ffd8e2e9f5560379d901567a25c1783756346e756255a51b058c40688543b192",
-    "scan": (100010.6 * 2.000 + 67584.0 * 1.000) * 1024,
-    "prepare": (40810.2 * 2.000 + 165163.0 * 1.000) * 1024,
+    "source_sha256": "a6731d42146171b2ffe914a7cb5a57221df65547acb6068d7870c8c9e05b519c",
+    "scan": (100010.5 * 2.000 + 67584.0 * 1.000) * 1024,
+    "prepare": (42074.6 * 2.000 + 165200.9 * 1.000) * 1024,
 }
 
 
@@ -74,8 +76,8 @@ MEASURED_TRAFFIC = {
 DECODE_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
               for f in ("gdn_decode.hip", "gdn_device.h", "gdn_internal.h")]
 MEASURED_DECODE_TRAFFIC = {
-    "source_sha256": "15794d35050744c968397d72a52aedc429cf45fbd78c9cc84caec091a0c030ef",
-    "decode": (66141.1 * 2.000 + 132096.0 * 1.000) * 1024,
+    "source_sha256": "b96e62c70cef20d420675d453dd3db6258e45ad119c4f483a89f597f28c12a0e",
+    "decode": (66131.4 * 2.000 + 132096.0 * 1.000) * 1024,
 }
 
 
@@ -122,6 +124,22 @@ def to_dev(case, dev):
                 slot_in=f(case.slot_in, torch.int32), slot_out=f(case.slot_out, torch.int32))
 
 
+# Before each measurement the workload runs back to back for this long,
+# untimed: the GPU's clocks take about 10 ms of sustained work to settle and
+# drop again within a fraction of a second of idling (the T=4096 prefill step:
+# 128 us over the first 20 steps, 112 us once settled).
+SETTLE_MS = 100.0
+
+
+def settle(call, ms=SETTLE_MS):
+    """Run `call` back to back for at least `ms` of wall time (untimed)."""
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            call()
+        torch.cuda.synchronize()
+
+
 class Timer:
     """HIP events on the stream the kernels are launched on."""
 
@@ -144,13 +162,14 @@ def bench_prefill(gdn, dev, steps, warmup):
     plan = gdn.PrefillPlan(d["q"], d["v"], out, case.n_seqs, state=state_out)
     stream = torch.cuda.current_stream()
 
-    def step(t=None):
-        if t: t.mark(0)
-        plan.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], stream=stream)
-        if t: t.mark(1)
-        plan.scan(d["pool"], state_out, out, d["slot_in"], d["slot_out"], stream=stream)
-        if t: t.mark(2)
+    prep = lambda: plan.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], stream=stream)
+    scan = lambda: plan.scan(d["pool"], state_out, out, d["slot_in"], d["slot_out"], stream=stream)
 
+    def step():
+        prep()
+        scan()
+
+    settle(step)
     for _ in range(warmup):
         step()
     # the step rate: steps issued back to back, nothing else on the stream
@@ -161,14 +180,22 @@ def bench_prefill(gdn, dev, steps, warmup):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
-    # per-kernel launch durations, from HIP events around each launch on the
-    # launch stream (a separate pass: the event records add gaps of their own)
-    timers = [Timer(stream, 3) for _ in range(steps)]
-    for i in range(steps):
-        step(timers[i])
+    # per-kernel launch durations: each kernel launched K times back to back
+    # between two HIP events on the launch stream (an event recorded between
+    # two launches would add the dispatch gap after it to every interval).
+    # The scans re-read the factors of the last preparation, as in a step,
+    # and both kernels give the same results on every repeat.
+    t = Timer(stream, 3)
+    t.mark(0)
+    for _ in range(steps):
+        prep()
+    t.mark(1)
+    for _ in range(steps):
+        scan()
+    t.mark(2)
     torch.cuda.synchronize()
-    prep_ms = statistics.mean(t.ms(0, 1) for t in timers)
-    scan_ms = statistics.mean(t.ms(1, 2) for t in timers)
+    prep_ms = t.ms(0, 1) / steps
+    scan_ms = t.ms(1, 2) / steps
     assert torch.isfinite(out).all() and torch.isfinite(state_out).all()
     T, H_v = case.total_tokens, case.H_v
     fp, fs = prefill_flops_per_token_head(case.H_k, case.H_v, case.d_k, case.d_v)
@@ -215,11 +242,12 @@ def bench_decode(gdn, dev, reps=3):
     stream = torch.cuda.current_stream()
     S = dc.n_steps
     res = {}
+    settle(lambda: gdn.decode_step(q[0], k[0], v[0], g[0], b[0], pool2, pool2, outs[0], slots, slots,
+                                   stream=stream))
     for mode in ("in_place", "ping_pong"):
         per_rep = []
-        kern_ms = []
         for rep in range(reps + 1):
-            t = Timer(stream, S + 1)
+            t = Timer(stream, 2)
             torch.cuda.synchronize()
             t.mark(0)
             for s in range(S):
@@ -229,14 +257,14 @@ def bench_decode(gdn, dev, reps=3):
                     src, dst = (pool, pool2) if s % 2 == 0 else (pool2, pool)
                 gdn.decode_step(q[s], k[s], v[s], g[s], b[s], src, dst, outs[s], slots, slots,
                                 stream=stream)
-                t.mark(s + 1)
+            t.mark(1)
             torch.cuda.synchronize()
             if rep == 0:
                 continue  # warm-up pass
-            per_rep.append(t.ms(0, S))
-            kern_ms.extend(t.ms(s, s + 1) for s in range(S))
+            per_rep.append(t.ms(0, 1))
+        # the 128 launches run back to back between one pair of events
         ms_128 = statistics.median(per_rep)
-        launch_ms = statistics.mean(kern_ms)
+        launch_ms = ms_128 / S
         by = decode_bytes_per_step(dc)
         gbs = by / (launch_ms * 1e-3) / 1e9
         res[mode] = {"ms_per_128_steps": ms_128, "mean_launch_ms": launch_ms,
@@ -273,7 +301,7 @@ def bench_decode(gdn, dev, reps=3):
             "ping_pong": res["ping_pong"], "in_place": ip, "copy_reference": res["copy_reference"]}
 
 
-def bench_decode_multi(gdn, dev, tokens=4, reps=20):
+def bench_decode_multi(gdn, dev, tokens=4, reps=200):
     """gdn_recurrent_multi: 64 sequences x `tokens` tokens (speculative
     verification), state pool in place; HBM roofline on state + I/O bytes."""
     case = gi.make_case(f"spec64x{tokens}", [tokens] * 64, dtype="bf16", seed=40 + tokens,
@@ -284,16 +312,15 @@ def bench_decode_multi(gdn, dev, tokens=4, reps=20):
     call = lambda: gdn.decode_multi(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"],
                                     d["pool"], out, d["cu"], d["slot_in"], d["slot_out"],
                                     stream=stream)
-    for _ in range(3):
-        call()
-    t = Timer(stream, reps + 1)
+    settle(call)
+    t = Timer(stream, 2)
     torch.cuda.synchronize()
     t.mark(0)
     for r in range(reps):
         call()
-        t.mark(r + 1)
+    t.mark(1)
     torch.cuda.synchronize()
-    ms = statistics.median(t.ms(r, r + 1) for r in range(reps))
+    ms = t.ms(0, 1) / reps
     N, H_k, H_v, dk, dv, T = 64, case.H_k, case.H_v, case.d_k, case.d_v, case.total_tokens
     by = N * H_v * dk * dv * 4 * 2 + T * (2 * H_k * dk * 2 + H_v * dv * 2 + H_v * dv * 4 + H_v * 8)
     gbs = by / (ms * 1e-3) / 1e9
@@ -316,7 +343,7 @@ def _layer_dev(case, L, dev):
                 slot_in=f(case.slot_in, torch.int32), slot_out=f(case.slot_out, torch.int32))
 
 
-def bench_layer_prefill(gdn, dev, reps=10):
+def bench_layer_prefill(gdn, dev, reps=50):
     """The fused layer path on the T=4096 prefill: mixed q|k|v rows through
     the convolution prologue, raw gate projections, gated RMSNorm epilogue,
     bf16 output; one gdn_chunked_prefill call per step."""
@@ -334,16 +361,15 @@ def bench_layer_prefill(gdn, dev, reps=10):
     call = lambda: gdn.prefill(d["qkv"], None, None, d["a"], d["b"], d["rows"], rows_out, out, d["cu"],
                                d["slot_in"], d["slot_out"], ws, stream=stream,
                                gates=(d["ssm_a"], d["ssm_dt"]), conv=cv, z=d["z"], norm_w=d["norm_w"])
-    for _ in range(3):
-        call()
-    t = Timer(stream, reps + 1)
+    settle(call)
+    t = Timer(stream, 2)
     torch.cuda.synchronize()
     t.mark(0)
     for r in range(reps):
         call()
-        t.mark(r + 1)
+    t.mark(1)
     torch.cuda.synchronize()
-    ms = statistics.median(t.ms(r, r + 1) for r in range(reps))
+    ms = t.ms(0, 1) / reps
     assert torch.isfinite(out.float()).all()
     T = case.total_tokens
     return {"workload": "fused layer prefill: 1 x 4096 tokens, mixed bf16 q|k|v rows -> conv(4) + "
@@ -372,6 +398,10 @@ def bench_layer_decode(gdn, dev, reps=3):
     slots = f(dc.slots, torch.int32)
     outs = torch.empty((S, N, dc.H_v, dc.d_v), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
+    rows2 = rows.clone()
+    settle(lambda: gdn.decode_step(qkv[0], None, None, a[0], b[0], rows2, rows2, outs[0], slots, slots,
+                                   stream=stream, gates=gates, conv=cv, z=z[0], norm_w=nw))
+    del rows2
     per = []
     for rep in range(reps + 1):
         t = Timer(stream, 2)
@@ -406,9 +436,8 @@ def bench_varlen(gdn, dev, reps=10):
     plan = gdn.PrefillPlan(d["q"], d["v"], out, case.n_seqs, state=pool_out)
     stream = torch.cuda.current_stream()
     t = Timer(stream, 2 * reps + 1)
-    for i in range(2):
-        plan.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], stream=stream)
-        plan.scan(d["pool"], pool_out, out, d["slot_in"], d["slot_out"], stream=stream)
+    settle(lambda: (plan.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], stream=stream),
+                    plan.scan(d["pool"], pool_out, out, d["slot_in"], d["slot_out"], stream=stream)))
     torch.cuda.synchronize()
     t.mark(0)
     for i in range(reps):
@@ -444,7 +473,7 @@ def bench_stream(gdn, dev, reps=2):
                          d["beta"][s:s + U], cu, stream=stream)
             plan.scan(pool, pool, out[s:s + U], sl_in, d["slot_out"], stream=stream)
 
-    run()
+    settle(run)
     times = []
     for _ in range(reps):
         pool.copy_(d["pool"])
@@ -518,8 +547,8 @@ def cpu_baseline(case, min_s=10.0, max_reps=40):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline prefill + decode only")
     ap.add_argument("--decode-only", action="store_true",
