@@ -65,9 +65,9 @@ C = 64
 PREFILL_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
                for f in ("gdn_prefill.hip", "gdn_mfma.h", "gdn_device.h", "gdn_internal.h")]
 MEASURED_TRAFFIC = {
-    "source_sha256": "a6731d42146171b2ffe914a7cb5a57221df65547acb6068d7870c8c9e05b519c",
-    "scan": (100010.5 * 2.000 + 67584.0 * 1.000) * 1024,
-    "prepare": (42074.6 * 2.000 + 165200.9 * 1.000) * 1024,
+    "source_sha256": "5834e183b784e5259d606743b4d2320729464cd1a9abf2aa80ec3293876355a4",
+    "scan": (100011.0 * 2.000 + 67584.0 * 1.000) * 1024,
+    "prepare": (42061.5 * 2.000 + 165243.1 * 1.000) * 1024,
 }
 
 
@@ -76,8 +76,8 @@ MEASURED_TRAFFIC = {
 DECODE_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
               for f in ("gdn_decode.hip", "gdn_device.h", "gdn_internal.h")]
 MEASURED_DECODE_TRAFFIC = {
-    "source_sha256": "b96e62c70cef20d420675d453dd3db6258e45ad119c4f483a89f597f28c12a0e",
-    "decode": (66131.4 * 2.000 + 132096.0 * 1.000) * 1024,
+    "source_sha256": "f7f700a68bbe65cce79a3a28fd4843d6be432500af20dfbd0561a351af650383",
+    "decode": (66131.8 * 2.000 + 132096.0 * 1.000) * 1024,
 }
 
 
@@ -428,32 +428,42 @@ def bench_layer_decode(gdn, dev, reps=3):
             "kernels": "decode_kernel + conv_state_kernel"}
 
 
-def bench_varlen(gdn, dev, reps=10):
+def bench_varlen(gdn, dev, reps=20):
+    """The varlen batch as one gdn_chunked_prefill call (it runs as chunk
+    ranges of about 64 chunks), and as the two split-phase calls (one range
+    over the whole batch) for comparison."""
     case = gi.config3()
     d = to_dev(case, dev)
     out = torch.empty(d["v"].shape, dtype=torch.float32, device=dev)
     pool_out = d["pool"].clone()
-    plan = gdn.PrefillPlan(d["q"], d["v"], out, case.n_seqs, state=pool_out)
     stream = torch.cuda.current_stream()
-    t = Timer(stream, 2 * reps + 1)
-    settle(lambda: (plan.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], stream=stream),
-                    plan.scan(d["pool"], pool_out, out, d["slot_in"], d["slot_out"], stream=stream)))
-    torch.cuda.synchronize()
-    t.mark(0)
-    for i in range(reps):
-        plan.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], stream=stream)
-        t.mark(2 * i + 1)
-        plan.scan(d["pool"], pool_out, out, d["slot_in"], d["slot_out"], stream=stream)
-        t.mark(2 * i + 2)
-    torch.cuda.synchronize()
-    total = t.ms(0, 2 * reps) / reps
-    scan = statistics.mean(t.ms(2 * i + 1, 2 * i + 2) for i in range(reps))
+    dims = gdn._dims_from(d["q"], d["v"], out, 0.0, 1e-6, pool_out)
+    ws = torch.empty(gdn.workspace_size(dims, case.n_seqs, case.total_tokens), dtype=torch.uint8,
+                     device=dev)
+    call = lambda: gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], pool_out, out,
+                               d["cu"], d["slot_in"], d["slot_out"], ws, stream=stream)
+    plan = gdn.PrefillPlan(d["q"], d["v"], out, case.n_seqs, state=pool_out, workspace=ws)
+    split = lambda: (plan.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], stream=stream),
+                     plan.scan(d["pool"], pool_out, out, d["slot_in"], d["slot_out"], stream=stream))
+    res = {}
+    for name, fn in (("call", call), ("split", split)):
+        settle(fn)
+        t = Timer(stream, 2)
+        torch.cuda.synchronize()
+        t.mark(0)
+        for _ in range(reps):
+            fn()
+        t.mark(1)
+        torch.cuda.synchronize()
+        res[name] = t.ms(0, 1) / reps
+    total = res["call"]
     T = case.total_tokens
     fp, fs = prefill_flops_per_token_head(case.H_k, case.H_v, case.d_k, case.d_v)
     tf = (fp + fs) * T * case.H_v / (total * 1e-3) / 1e12
     return {"workload": "varlen: 8 sequences {17,64,65,300,512,1023,2048,8192} = 12221 tokens, "
-                        "scattered slots", "ms_per_call": total, "scan_ms": scan,
-            "tokens_s": T / (total * 1e-3), "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}
+                        "scattered slots", "ms_per_call": total,
+            "split_phase_ms": res["split"], "tokens_s": T / (total * 1e-3), "tflops": tf,
+            "mfma_frac": tf / PEAK_BF16_TFLOPS}
 
 
 def bench_stream(gdn, dev, reps=2):
@@ -616,6 +626,8 @@ def main():
         log(f"  {extra['layer_decode']['ms_per_step']*1e3:.1f} us/step")
         log("varlen ...")
         extra["varlen"] = bench_varlen(gdn, dev)
+        log(f"  {extra['varlen']['ms_per_call']*1e3:.0f} us/call "
+            f"({extra['varlen']['split_phase_ms']*1e3:.0f} us as split-phase calls)")
         log("stream 65536 ...")
         extra["stream"] = bench_stream(gdn, dev)
         log(f"  {extra['stream']['us_per_call']:.1f} us/call, "

@@ -106,12 +106,15 @@ struct Segment {
 // A batch whose factors fit kOneRangeBytes runs as one range (a second
 // launch pair costs more than the cache misses it saves); a longer one runs
 // in ranges of at most kSegmentBytes of factors, which leaves room in the
-// cache for the range's outputs.  Measured at Qwen3-Next heads: 5120 tokens
-// (206 MiB of factors) 165 us as one range against 186 us as two; the fused
-// layer's 4096 tokens (226 MiB) 350 us as one range against 330 us as two;
-// 8192 tokens 281 us in ranges of 32 chunks against 324 us in ranges of 64.
+// cache for the range's outputs.  Every range writes its factors to the same
+// workspace slots (chunk c of the range at slot c - lo), so a range rewrites
+// lines the cache already holds.  Measured at Qwen3-Next heads: 5120 tokens
+// (206 MiB of factors) 163 us as one range against 186 us as two; 8192
+// tokens 231 us in ranges of 64 chunks (165 MiB), 263 us in ranges of 32 and
+// 289 us in ranges of 96; the fused layer's 4096 tokens (226 MiB) 294-300 us
+// as two ranges against 345 us as one.
 constexpr size_t kOneRangeBytes = 212u << 20;
-constexpr size_t kSegmentBytes = 128u << 20;
+constexpr size_t kSegmentBytes = 168u << 20;
 // chunks of a batch (an upper bound when n_seqs > 1) and chunks per range
 int prefill_chunk_count(const Problem &p, int32_t n_seqs, int64_t total_tokens);
 int segment_chunks(const Problem &p, int chunks);

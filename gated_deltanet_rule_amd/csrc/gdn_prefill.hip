@@ -367,7 +367,7 @@ struct PrepParams {
     // head), for grids too small to fill the GPU (K K^T is then formed once
     // per value head)
     int head_split;
-    int chunk_base;    // blockIdx.x = 0 is this chunk of the batch
+    int chunk_base;    // blockIdx.x = 0 is this chunk of the batch; its factors go to slot 0
 };
 
 // LDS of the preparation kernel.  Rows are padded so that the row stride is
@@ -510,6 +510,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     float *sColh = sBetah + NH * C;                             // [NH][C] beta_c e^{G_c} / |k_c|  (columns of T for W)
 
     const int chunk = blockIdx.x + pp.chunk_base;
+    const int slot = blockIdx.x;     // its factors' place in the workspace (relative to the range)
     const int ratio = pp.H_v / pp.H_k;
     const int kh = pp.head_split ? blockIdx.y / ratio : blockIdx.y;
     // value heads of this workgroup: [jbeg, jend) of the key head's ratio;
@@ -561,7 +562,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     auto head_scalars = [&](int j0) {
         const int jw = min(j0 + w, ratio - 1);
         const int hh = kh * ratio + jw, hs = jw % NH;
-        float *scal = reinterpret_cast<float *>(pp.vblocks + ((size_t)chunk * pp.H_v + hh) * ((size_t)G::VBLK * 1024) +
+        float *scal = reinterpret_cast<float *>(pp.vblocks + ((size_t)slot * pp.H_v + hh) * ((size_t)G::VBLK * 1024) +
                                                 G::F_SCAL * 1024);
         const int r = lane;
         double Gc = gq;
@@ -743,7 +744,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
 
     // 2. raw q and k^T of this key head as operand fragments for the scan
     {
-        char *kb_blk = pp.kblocks + ((size_t)chunk * pp.H_k + kh) * ((size_t)G::KBLK * 1024);
+        char *kb_blk = pp.kblocks + ((size_t)slot * pp.H_k + kh) * ((size_t)G::KBLK * 1024);
 #pragma unroll
         for (int ff = 0; ff < G::NQF / 4; ++ff) {
             const int f = w + 4 * ff;
@@ -790,7 +791,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
 
     for (int jv = jbeg; jv < jend; ++jv) {
         const int h = kh * ratio + jv;
-        char *blk = pp.vblocks + ((size_t)chunk * pp.H_v + h) * ((size_t)G::VBLK * 1024);
+        char *blk = pp.vblocks + ((size_t)slot * pp.H_v + h) * ((size_t)G::VBLK * 1024);
         char *Wf = blk + G::F_W * 1024;
         char *Wlf = blk + G::F_WL * 1024;
         char *Pf = blk + G::F_PH * 1024;
@@ -1125,8 +1126,11 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
     const char *vbase = sp.vblocks + (size_t)h * vstride;
     const char *kbase = sp.kblocks + (size_t)kh * kstride;
     const size_t vstep = (size_t)sp.H_v * vstride, kstep = (size_t)sp.H_k * kstride;
-    auto vblk = [&](int c) { return reinterpret_cast<const u32x4 *>(vbase + (size_t)c * vstep); };
-    auto kblk = [&](int c) { return reinterpret_cast<const u32x4 *>(kbase + (size_t)c * kstep); };
+    // chunk c of this range has its factors in slot c - seg_lo (c >= seg_lo
+    // for every chunk read: an empty sequence reads chunk 0 and only in the
+    // range that starts at 0)
+    auto vblk = [&](int c) { return reinterpret_cast<const u32x4 *>(vbase + (size_t)(c - sp.seg_lo) * vstep); };
+    auto kblk = [&](int c) { return reinterpret_cast<const u32x4 *>(kbase + (size_t)(c - sp.seg_lo) * kstep); };
     auto vfrag = [&](int c, int f) -> Frag { return __builtin_bit_cast(Frag, vblk(c)[f * 64 + lane]); };
     auto kfrag = [&](int c, int f) -> Frag { return __builtin_bit_cast(Frag, kblk(c)[f * 64 + lane]); };
     auto scal4 = [&](int c, int off) -> floatx4 {

@@ -204,7 +204,9 @@ const char *gdn_last_error(void);
  * gdn_chunked_prefill runs a batch whose factors outgrow the GPU's 256 MB
  * last-level cache as consecutive ranges of chunks (preparation, then scan,
  * per range; results are bitwise those of one range), and a sequence that
- * crosses a range boundary keeps its state there in between.
+ * crosses a range boundary keeps its state there in between.  The size
+ * covers the factors of every chunk, as the split-phase calls need; the
+ * ranges of gdn_chunked_prefill reuse the slots of the first range.
  */
 gdn_status gdn_prefill_workspace_size(const gdn_dims *dims, int32_t n_seqs,
                                       int64_t total_tokens, size_t *bytes);

@@ -190,9 +190,11 @@ def test_long_prefill_runs_in_cache_sized_ranges():
 
 
 def test_varlen_sequences_across_range_boundaries():
-    """Sequences that start and end inside ranges, span several ranges, are
-    empty or a single token, with the zero-state slot and scattered slots."""
-    lengths = [1900, 0, 1, 2100, 64 * 33, 7, 3000, 65]
+    """Sequences that start and end inside ranges, end and start on a range
+    boundary, span three ranges (9000 tokens), are empty or a single token,
+    with the zero-state slot and scattered slots (ranges of 64 chunks at
+    these heads)."""
+    lengths = [1900, 0, 1, 2100, 64 * 33, 7, 9000, 3000, 65]
     case = gi.make_case("ranges_varlen", lengths, dtype="bf16", seed=92, decay="weak",
                         n_slots=20, scatter_slots=True, **gi.QWEN3_NEXT_HEADS)
     case.slot_in[3] = -1
@@ -218,7 +220,7 @@ def test_many_sequences(n_seqs):
 
 
 def test_single_call_65536_tokens():
-    """The long-context workload as one call: 1024 chunks in 32 chunk ranges
+    """The long-context workload as one call: 1024 chunks in 16 chunk ranges
     (sampled heads)."""
     case = gi.make_case("one_call_65536", [65536], dtype="bf16", seed=93, decay="weak",
                         **gi.QWEN3_NEXT_HEADS)
