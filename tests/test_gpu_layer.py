@@ -43,6 +43,16 @@ def test_prefill_conv_norm_tiny_f32():
     _prefill(case, _layer(case, 80))
 
 
+def test_prefill_layer_varlen_in_ranges_bf16():
+    """A fused-layer batch whose two-term factors (3.5 MiB per chunk) run as
+    three chunk ranges, with sequences that cross range boundaries: the
+    convolution history of a range's first chunk comes from the preceding
+    rows, of a sequence's first chunk from its slot (sampled heads)."""
+    case = gi.make_case("layer_ranges", [3000, 1500, 1, 700], dtype="bf16", seed=89,
+                        decay="weak", n_slots=6, scatter_slots=True, **gi.QWEN3_NEXT_HEADS)
+    _prefill(case, _layer(case, 89), raw_gates=True, heads=[0, 17, 31])
+
+
 def test_prefill_conv_ragged_short_sequences_f32():
     case = gi.make_case("layer_ragged", [1, 2, 3, 63, 64, 65, 130], 2, 4, 64, 32, "f32", seed=81,
                         decay="weak", n_slots=12, scatter_slots=True)

@@ -189,6 +189,21 @@ def test_long_prefill_runs_in_cache_sized_ranges():
     compare_prefill(case, out, pool, ref_o, ref_s, heads=[0, 5, 16, 31])
 
 
+def test_long_prefill_f32_runs_in_ranges():
+    """fp32 inputs (fp32 operands, larger factors: 3.5 MiB per chunk at these
+    heads) over 71 chunks, which run as ranges of 32 chunks: parity on
+    sampled heads and bitwise equal to the split-phase calls (one range)."""
+    case = gi.make_case("ranges_f32_T4500", [4500], dtype="f32", seed=94, decay="weak",
+                        **gi.QWEN3_NEXT_HEADS)
+    d = dev_case(case)
+    out, pool = gpu_prefill(case, d=d, inplace=False)
+    o1, p1 = _split_phase(case, d)
+    assert torch.equal(out, o1) and torch.equal(pool, p1)
+    heads = [0, 7, 31]
+    ref_o, ref_s = oracle_case(case, heads=heads)
+    compare_prefill(case, out, pool, ref_o, ref_s, heads=heads)
+
+
 def test_varlen_sequences_across_range_boundaries():
     """Sequences that start and end inside ranges, end and start on a range
     boundary, span three ranges (9000 tokens), are empty or a single token,
