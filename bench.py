@@ -65,9 +65,9 @@ C = 64
 PREFILL_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
                for f in ("gdn_prefill.hip", "gdn_mfma.h", "gdn_device.h", "gdn_internal.h")]
 MEASURED_TRAFFIC = {
-    "source_sha256": "5834e183b784e5259d606743b4d2320729464cd1a9abf2aa80ec3293876355a4",
-    "scan": (100011.0 * 2.000 + 67584.0 * 1.000) * 1024,
-    "prepare": (42061.5 * 2.000 + 165243.1 * 1.000) * 1024,
+    "source_sha256": "09a83639c57aa7f512f2ae754896d3f4c9abc684599e0fd04b56ae7320c22b91",
+    "scan": (83627.0 * 2.000 + 67584.0 * 1.000) * 1024,
+    "prepare": (42062.1 * 2.000 + 165242.7 * 1.000) * 1024,
 }
 
 

