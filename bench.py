@@ -65,9 +65,9 @@ C = 64
 PREFILL_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
                for f in ("gdn_prefill.hip", "gdn_mfma.h", "gdn_device.h", "gdn_internal.h")]
 MEASURED_TRAFFIC = {
-    "source_sha256": "09a83639c57aa7f512f2ae754896d3f4c9abc684599e0fd04b56ae7320c22b91",
-    "scan": (83627.0 * 2.000 + 67584.0 * 1.000) * 1024,
-    "prepare": (42062.1 * 2.000 + 165242.7 * 1.000) * 1024,
+    "source_sha256": "e91434300a174b3793ed5be8c416aa9734cd8debb1d61f077ba4e880bbf569ac",
+    "scan": (83627.1 * 2.000 + 67584.0 * 1.000) * 1024,
+    "prepare": (42052.8 * 2.000 + 165256.2 * 1.000) * 1024,
 }
 
 
@@ -76,8 +76,8 @@ MEASURED_TRAFFIC = {
 DECODE_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
               for f in ("gdn_decode.hip", "gdn_device.h", "gdn_internal.h")]
 MEASURED_DECODE_TRAFFIC = {
-    "source_sha256": "f7f700a68bbe65cce79a3a28fd4843d6be432500af20dfbd0561a351af650383",
-    "decode": (66131.8 * 2.000 + 132096.0 * 1.000) * 1024,
+    "source_sha256": "e71f79e6a0b3fecc673623ab9129ca0d9688412c59901a1f415494bfed6a27fa",
+    "decode": (66131.5 * 2.000 + 132096.0 * 1.000) * 1024,
 }
 
 

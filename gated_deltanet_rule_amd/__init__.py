@@ -62,6 +62,8 @@ def _load() -> ctypes.CDLL:
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_prefill_workspace_size.argtypes = [D, I32, I64, ctypes.POINTER(SZ)]
     lib.gdn_prefill_workspace_size.restype = ctypes.c_int
+    lib.gdn_chunked_prefill_workspace_size.argtypes = [D, I32, I64, ctypes.POINTER(SZ)]
+    lib.gdn_chunked_prefill_workspace_size.restype = ctypes.c_int
     lib.gdn_chunked_prefill.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, I32, I64, P, SZ, P]
     lib.gdn_chunked_prefill.restype = ctypes.c_int
     lib.gdn_recurrent_step.argtypes = [D, P, P, P, P, P, P, P, P, P, P, I32, P]
@@ -78,7 +80,8 @@ def _load() -> ctypes.CDLL:
 lib = _load()
 
 EXPORTED = ["gdn_version", "gdn_status_string", "gdn_last_error",
-            "gdn_prefill_workspace_size", "gdn_chunked_prefill", "gdn_prefill_prepare",
+            "gdn_prefill_workspace_size", "gdn_chunked_prefill_workspace_size",
+            "gdn_chunked_prefill", "gdn_prefill_prepare",
             "gdn_prefill_scan", "gdn_recurrent_step", "gdn_recurrent_multi"]
 
 
@@ -198,8 +201,17 @@ def _need(t, name, dtype=None, dev=None):
 
 
 def workspace_size(dims: Dims, n_seqs: int, total_tokens: int) -> int:
+    """gdn_prefill_workspace_size: the split-phase calls' workspace (enough for prefill too)."""
     n = ctypes.c_size_t(0)
     _check(lib.gdn_prefill_workspace_size(ctypes.byref(dims), n_seqs, total_tokens, ctypes.byref(n)))
+    return n.value
+
+
+def chunked_workspace_size(dims: Dims, n_seqs: int, total_tokens: int) -> int:
+    """gdn_chunked_prefill_workspace_size: the workspace of prefill()."""
+    n = ctypes.c_size_t(0)
+    _check(lib.gdn_chunked_prefill_workspace_size(ctypes.byref(dims), n_seqs, total_tokens,
+                                                  ctypes.byref(n)))
     return n.value
 
 
@@ -222,8 +234,8 @@ def prefill(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in, slo
     dims = _dims_from(q, v, out, scale, eps, state_out, gates, conv, z, norm_w)
     n_seqs = slot_out.shape[0]
     T = q.shape[0]
-    need = workspace_size(dims, n_seqs, T)
     if workspace is None:
+        need = chunked_workspace_size(dims, n_seqs, T)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _check(lib.gdn_chunked_prefill(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                    _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),

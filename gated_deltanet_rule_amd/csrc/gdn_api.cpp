@@ -171,9 +171,9 @@ gdn_status check_counts(int32_t n_seqs, int64_t total_tokens)
 }
 
 gdn_status check_workspace(const gdn::Problem &p, int32_t n_seqs, int64_t total_tokens,
-                           const void *workspace, size_t workspace_bytes)
+                           const void *workspace, size_t workspace_bytes, int slots = 0)
 {
-    const size_t need = gdn::prefill_workspace_bytes(p, n_seqs, total_tokens);
+    const size_t need = gdn::prefill_workspace_bytes(p, n_seqs, total_tokens, slots);
     if (!workspace || workspace_bytes < need)
         return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need,
                     workspace_bytes, workspace);
@@ -245,6 +245,21 @@ gdn_status gdn_prefill_workspace_size(const gdn_dims *dims, int32_t n_seqs,
     return GDN_OK;
 }
 
+gdn_status gdn_chunked_prefill_workspace_size(const gdn_dims *dims, int32_t n_seqs,
+                                              int64_t total_tokens, size_t *bytes)
+{
+    g_last_error[0] = 0;
+    gdn::Problem p;
+    gdn_status st = resolve(dims, &p);
+    if (st != GDN_OK) return st;
+    if (!bytes) return fail(GDN_ERR_INVALID_ARG, "bytes is NULL");
+    st = check_counts(n_seqs, total_tokens);
+    if (st != GDN_OK) return st;
+    const int per = gdn::segment_chunks(p, gdn::prefill_chunk_count(p, n_seqs, total_tokens));
+    *bytes = gdn::prefill_workspace_bytes(p, n_seqs, total_tokens, per);
+    return GDN_OK;
+}
+
 gdn_status gdn_prefill_prepare(const gdn_dims *dims, const void *q, const void *k,
                                const void *v, const float *g, const float *beta,
                                const int32_t *cu_seqlens, int32_t n_seqs, int64_t total_tokens,
@@ -305,19 +320,21 @@ gdn_status gdn_chunked_prefill(const gdn_dims *dims, const void *q, const void *
     if (st == GDN_OK) st = check_counts(n_seqs, total_tokens);
     if (st == GDN_OK) st = check_prepare_inputs(q, k, v, g, beta, cu_seqlens);
     if (st == GDN_OK) st = check_scan_inputs(state_in, state_out, out, slot_in, slot_out);
-    if (st == GDN_OK) st = check_workspace(p, n_seqs, total_tokens, workspace, workspace_bytes);
+    if (st != GDN_OK) return st;
+    // consecutive chunk ranges within the cache budget, each writing its
+    // factors to the same per chunk slots
+    const int chunks = gdn::prefill_chunk_count(p, n_seqs, total_tokens);
+    const int per = gdn::segment_chunks(p, chunks);
+    const int n_seg = std::max(1, (chunks + per - 1) / per);
+    st = check_workspace(p, n_seqs, total_tokens, workspace, workspace_bytes, per);
     if (st != GDN_OK) return st;
     if (p.H_v > 65535) return fail(GDN_ERR_UNSUPPORTED, "H_v above 65535");
     gdn::PrefillArgs a{q, k, v, g, beta, ssm_part(p, state_in), ssm_part(p, state_out), out,
                        cu_seqlens, slot_in, slot_out, n_seqs, total_tokens, workspace,
-                       state_in, state_out};
+                       state_in, state_out, per};
     hipStream_t s = static_cast<hipStream_t>(stream);
     st = device_check(cu_seqlens, n_seqs, total_tokens, slot_in, slot_out, s);
     if (st != GDN_OK) return st;
-    // consecutive chunk ranges within the cache budget
-    const int chunks = gdn::prefill_chunk_count(p, n_seqs, total_tokens);
-    const int per = gdn::segment_chunks(p, chunks);
-    const int n_seg = std::max(1, (chunks + per - 1) / per);
     for (int k = 0; k < n_seg && st == GDN_OK; ++k) {
         gdn::Segment sg;
         sg.lo = k * per;

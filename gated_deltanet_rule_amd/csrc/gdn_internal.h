@@ -79,6 +79,10 @@ struct PrefillArgs {
     void *workspace;
     const float *conv_in;
     float *conv_out;
+    // WY-factor slots the workspace holds: 0 for one per chunk of the batch
+    // (the split-phase calls), else the chunk-range length (gdn_chunked_prefill,
+    // whose ranges reuse the slots of the first)
+    int ws_slots = 0;
 };
 
 // Chunk size of the WY form.
@@ -90,7 +94,7 @@ inline int64_t max_chunks(int32_t n_seqs, int64_t total_tokens) {
     return a;
 }
 
-size_t prefill_workspace_bytes(const Problem &p, int32_t n_seqs, int64_t total_tokens);
+size_t prefill_workspace_bytes(const Problem &p, int32_t n_seqs, int64_t total_tokens, int slots = 0);
 
 // A range of chunks run as one preparation + scan pair.  A long prefill is
 // run as several consecutive ranges so that the WY factors one range writes

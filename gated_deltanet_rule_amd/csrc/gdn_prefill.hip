@@ -132,18 +132,21 @@ int cu_count()
 bool op_bf16(const Problem &p) { return p.bf16 != 0; }
 bool op_split(const Problem &p) { return p.bf16 && p.conv_w; }
 
-WsLayout ws_layout(const Problem &p, int32_t n_seqs, int64_t T)
+// slots: WY-factor slots (chunks held at once); 0 or more than the batch has
+// means one per chunk.
+WsLayout ws_layout(const Problem &p, int32_t n_seqs, int64_t T, int slots)
 {
     WsLayout L;
     const bool bf = op_bf16(p);
     L.max_chunks = (int)max_chunks(n_seqs, T);
+    const size_t fs = slots > 0 && slots < L.max_chunks ? (size_t)slots : (size_t)L.max_chunks;
     L.entries = 256;
     L.cstart = align256(L.entries + sizeof(ChunkEntry) * (size_t)L.max_chunks);
     L.vblocks = align256(L.cstart + sizeof(int32_t) * ((size_t)n_seqs + 1));
     L.vblk = (size_t)vblk_kib(p.d_k, p.d_v, bf, op_split(p)) * 1024;
     L.kblk = (size_t)kblk_kib(p.d_k, bf, op_split(p)) * 1024;
-    L.kblocks = L.vblocks + L.vblk * (size_t)L.max_chunks * p.H_v;
-    L.obuf = align256(L.kblocks + L.kblk * (size_t)L.max_chunks * p.H_k);
+    L.kblocks = L.vblocks + L.vblk * fs * p.H_v;
+    L.obuf = align256(L.kblocks + L.kblk * fs * p.H_k);
     L.carry = align256(L.obuf + (stage_o(p) ? sizeof(float) * (size_t)T * p.H_v * p.d_v : 0));
     L.total = L.carry + sizeof(float) * (size_t)n_seqs * p.H_v * p.d_k * p.d_v;
     return L;
@@ -1407,7 +1410,7 @@ struct WsPtrs {
 WsPtrs ws_ptrs(const Problem &p, const PrefillArgs &a)
 {
     WsPtrs w;
-    w.L = ws_layout(p, a.n_seqs, a.total_tokens);
+    w.L = ws_layout(p, a.n_seqs, a.total_tokens, a.ws_slots);
     char *ws = static_cast<char *>(a.workspace);
     w.hdr = reinterpret_cast<int32_t *>(ws);
     w.ent = reinterpret_cast<ChunkEntry *>(ws + w.L.entries);
@@ -1532,9 +1535,9 @@ hipError_t scan_dk(const Problem &p, const PrefillArgs &a, const Segment &sg, hi
 
 }  // namespace
 
-size_t prefill_workspace_bytes(const Problem &p, int32_t n_seqs, int64_t total_tokens)
+size_t prefill_workspace_bytes(const Problem &p, int32_t n_seqs, int64_t total_tokens, int slots)
 {
-    return ws_layout(p, n_seqs, total_tokens).total;
+    return ws_layout(p, n_seqs, total_tokens, slots).total;
 }
 
 int prefill_chunk_count(const Problem &p, int32_t n_seqs, int64_t total_tokens)

@@ -87,7 +87,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 3
+#define GDN_VERSION 4
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -141,7 +141,7 @@ typedef enum gdn_gate_mode {
  * points use it in fp32, and with bf16 rows gdn_chunked_prefill feeds it to
  * the matrix cores as two-term bf16 operands (hi + lo, about 16 significant
  * bits; fp32 rows keep fp32 operands).  The prefill workspace grows
- * accordingly (gdn_prefill_workspace_size accounts for it).
+ * accordingly (the workspace sizes account for it).
  * The split-phase entry points do not support the prologue.
  *
  * Epilogue (z != NULL): llm_build_norm (RMS, weight ssm_norm) followed by
@@ -195,21 +195,32 @@ const char *gdn_status_string(int status);
 const char *gdn_last_error(void);
 
 /*
- * Workspace needed by gdn_chunked_prefill for a call with n_seqs sequences
- * and total_tokens tokens, written to *bytes.  Host-only, no device work.
- * The workspace holds the chunk table and the per-chunk WY factors
- * (build_delta_net_chunking: k_cumdecay, the beta-weighted values and the
- * decayed q.k attention, plus q and k in matrix-core operand order) between
- * the two phases, and one d_k x d_v fp32 state per (sequence, value head):
- * gdn_chunked_prefill runs a batch whose factors outgrow the GPU's 256 MB
- * last-level cache as consecutive ranges of chunks (preparation, then scan,
- * per range; results are bitwise those of one range), and a sequence that
- * crosses a range boundary keeps its state there in between.  The size
- * covers the factors of every chunk, as the split-phase calls need; the
- * ranges of gdn_chunked_prefill reuse the slots of the first range.
+ * Workspace needed by the split-phase calls (gdn_prefill_prepare and
+ * gdn_prefill_scan) for a batch of n_seqs sequences and total_tokens tokens,
+ * written to *bytes; enough for gdn_chunked_prefill too.  Host-only, no
+ * device work.  The workspace holds the chunk table and the per-chunk WY
+ * factors (build_delta_net_chunking: k_cumdecay, the beta-weighted values and
+ * the decayed q.k attention, plus q and k in matrix-core operand order)
+ * between the two phases, one slot per chunk of the batch, and one
+ * d_k x d_v fp32 state per (sequence, value head).
  */
 gdn_status gdn_prefill_workspace_size(const gdn_dims *dims, int32_t n_seqs,
                                       int64_t total_tokens, size_t *bytes);
+
+/*
+ * Workspace needed by gdn_chunked_prefill for the same batch, written to
+ * *bytes; at most gdn_prefill_workspace_size's.  Host-only, no device work
+ * (it reads the current device's compute-unit count, 256 when there is no
+ * device).  gdn_chunked_prefill runs a batch whose factors outgrow the GPU's
+ * 256 MB last-level cache as consecutive ranges of chunks (preparation, then
+ * scan, per range; results are bitwise those of one range); every range
+ * writes its factors to the same slots, so the workspace holds one range's
+ * factors (about 165 MiB at Qwen3-Next heads, against 2.6 GB for all of a
+ * 65 536-token call's chunks), and a sequence that crosses a range boundary
+ * keeps its state in the per-sequence states in between.
+ */
+gdn_status gdn_chunked_prefill_workspace_size(const gdn_dims *dims, int32_t n_seqs,
+                                              int64_t total_tokens, size_t *bytes);
 
 /*
  * Chunked prefill: runs every sequence of a packed varlen batch through the
@@ -228,7 +239,9 @@ gdn_status gdn_prefill_workspace_size(const gdn_dims *dims, int32_t n_seqs,
  *   slot_in/slot_out : [n_seqs] int32 (device)
  *   n_seqs >= 1, total_tokens >= 0 (0: only the state pass-through runs)
  *   workspace        : device buffer of at least the size reported by
- *                      gdn_prefill_workspace_size, 256-byte aligned
+ *                      gdn_chunked_prefill_workspace_size (that of
+ *                      gdn_prefill_workspace_size also serves), 256-byte
+ *                      aligned
  * A zero-length sequence copies its input state (or zeros) to its out slot.
  */
 gdn_status gdn_chunked_prefill(const gdn_dims *dims,

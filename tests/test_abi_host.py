@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert gdn.version() == 3
+    assert gdn.version() == 4
     for st in range(5):
         assert gdn.lib.gdn_status_string(st)
     assert gdn.lib.gdn_status_string(99) == b"unknown status"
@@ -56,6 +56,25 @@ def test_workspace_size_grows_with_tokens_and_is_aligned():
     assert 0 <= (b - a) - blocks <= 64 * 16 + 256  # + their chunk-table entries
     f = gdn.workspace_size(_dims(dtype=gdn.GDN_F32), 1, 4096)
     assert f > a
+
+
+def test_chunked_workspace_holds_one_range():
+    """gdn_chunked_prefill's workspace holds the factors of one chunk range
+    (at these heads: every chunk up to 212 MiB of factors, else 64 chunks);
+    the split-phase layout holds a slot for each of the batch's at most
+    T/64 + n_seqs chunks.  The rest of the two layouts is the same."""
+    d = _dims()
+    slot = (32 * (16 + 16 + 1 + 32) + 16 * 32) * 1024     # one chunk's factors, all heads
+    for n, T, held in ((1, 4096, 64), (1, 4160, 65), (1, 8229, 64), (1, 65536, 64),
+                       (8, 12221, 64), (8, 512, 16)):
+        full = gdn.workspace_size(d, n, T)
+        part = gdn.chunked_workspace_size(d, n, T)
+        bound = (T + 63) // 64 + n
+        if n > 1 and bound * slot <= 212 << 20:
+            held = bound                                  # one range over the bound
+        assert full - part == (bound - held) * slot, (n, T)
+    assert gdn.workspace_size(d, 1, 65536) > 2.7e9
+    assert gdn.chunked_workspace_size(d, 1, 65536) < 0.18e9
 
 
 @pytest.mark.parametrize("kw,status", [

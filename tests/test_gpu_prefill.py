@@ -204,6 +204,48 @@ def test_long_prefill_f32_runs_in_ranges():
     compare_prefill(case, out, pool, ref_o, ref_s, heads=heads)
 
 
+def test_one_range_workspace():
+    """gdn_chunked_prefill with exactly gdn_chunked_prefill_workspace_size
+    bytes (the factor slots of one 64-chunk range for 130 chunks) gives the
+    results of the split-phase layout's full-size workspace bit for bit, with
+    the workspace past that size untouched; 256 bytes less is rejected with
+    GDN_ERR_WORKSPACE before anything is enqueued (outputs untouched)."""
+    import gated_deltanet_rule_amd as gdn
+    case = gi.make_case("ranges_ws_T8229", [8229], dtype="bf16", seed=95, decay="weak",
+                        **gi.QWEN3_NEXT_HEADS)
+    d = dev_case(case)
+    T = case.total_tokens
+    dims = gdn._dims_from(d["q"], d["v"], torch.empty(d["v"].shape, device="meta"), 0.0, 1e-6,
+                          d["pool"])
+    small = gdn.chunked_workspace_size(dims, 1, T)
+    full = gdn.workspace_size(dims, 1, T)
+    assert small < full
+    say(f"workspace: {small} bytes for the call, {full} for the split-phase calls")
+
+    def run(ws):
+        out = torch.full(d["v"].shape, 7.0, dtype=torch.float32, device="cuda")
+        pool = d["pool"].clone()
+        gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], pool, out, d["cu"],
+                    d["slot_in"], d["slot_out"], ws)
+        torch.cuda.synchronize()
+        return out, pool
+
+    ws_full = torch.zeros(full, dtype=torch.uint8, device="cuda")
+    o1, p1 = run(ws_full)
+    ws_small = torch.zeros(full, dtype=torch.uint8, device="cuda")
+    o2, p2 = run(ws_small[:small])
+    assert torch.equal(o1, o2) and torch.equal(p1, p2)
+    assert not ws_small[small:].any()
+    out = torch.full(d["v"].shape, 7.0, dtype=torch.float32, device="cuda")
+    pool = d["pool"].clone()
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], pool, out, d["cu"],
+                    d["slot_in"], d["slot_out"], ws_small[:small - 256])
+    assert e.value.status == 3     # GDN_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert (out == 7.0).all() and torch.equal(pool, d["pool"])
+
+
 def test_varlen_sequences_across_range_boundaries():
     """Sequences that start and end inside ranges, end and start on a range
     boundary, span three ranges (9000 tokens), are empty or a single token,
