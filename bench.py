@@ -525,13 +525,31 @@ def bench_stream(gdn, dev, reps=2):
         gtimes.append(t.ms(0, 1))
     assert torch.equal(out, eager_out) and torch.equal(pool, eager_pool), "graph replay differs from eager"
     gms = statistics.median(gtimes[1:])
+    # the same 65536 tokens as one gdn_chunked_prefill call (chunk ranges of
+    # 64 chunks, one range of factor slots in the workspace)
+    cu1 = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    dims = gdn._dims_from(d["q"], d["v"], out, 0.0, 1e-6, pool)
+    ws1 = torch.empty(gdn.chunked_workspace_size(dims, 1, T), dtype=torch.uint8, device=dev)
+    one = lambda: gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], pool, out, cu1,
+                              d["slot_in"], d["slot_out"], ws1, stream=stream)
+    settle(one)
+    t = Timer(stream, 2)
+    torch.cuda.synchronize()
+    t.mark(0)
+    for _ in range(reps + 1):
+        one()
+    t.mark(1)
+    torch.cuda.synchronize()
+    oms = t.ms(0, 1) / (reps + 1)
     fp, fs = prefill_flops_per_token_head(case.H_k, case.H_v, case.d_k, case.d_v)
     tf = (fp + fs) * T * case.H_v / (ms * 1e-3) / 1e12
     return {"workload": "stream: 65536 tokens as 128 calls of 512, state carried in place",
             "ms_total": ms, "us_per_call": ms * 1e3 / (T // U), "tokens_s": T / (ms * 1e-3),
             "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS,
             "hip_graph": {"ms_total": gms, "us_per_call": gms * 1e3 / (T // U),
-                          "tokens_s": T / (gms * 1e-3)}}
+                          "tokens_s": T / (gms * 1e-3)},
+            "one_call": {"ms": oms, "tokens_s": T / (oms * 1e-3),
+                         "workspace_bytes": ws1.numel()}}
 
 
 def cpu_baseline(case, min_s=10.0, max_reps=40):
@@ -631,7 +649,8 @@ def main():
         log("stream 65536 ...")
         extra["stream"] = bench_stream(gdn, dev)
         log(f"  {extra['stream']['us_per_call']:.1f} us/call, "
-            f"{extra['stream']['hip_graph']['us_per_call']:.1f} us/call replayed from a HIP graph")
+            f"{extra['stream']['hip_graph']['us_per_call']:.1f} us/call replayed from a HIP graph; "
+            f"as one call {extra['stream']['one_call']['ms']:.2f} ms")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
