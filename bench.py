@@ -15,14 +15,18 @@ Alongside (same JSON line):
   roofline      the prefill's dominant kernel, from HIP events recorded on the
                 stream the kernels run on around K launches of that kernel
                 back to back (after the timed steps): algorithmic flops per launch
-                (per token per value head: 8*C*d + 6*d^2 for the whole
-                prefill, split 4*C*d_k/r + 2*C*d_k for the preparation and
-                4*C*d_v + 6*d_k*d_v for the scan) / mean launch time, against
-                the bf16 dense MFMA peak (2.5 PFLOP/s).
-  decode        gdn_recurrent_step on 64 sequences x 128 steps (state pool
-                128 MiB, in place), tokens/s and state bytes / kernel time
-                against the 8 TB/s HBM peak; also a ping-pong run (two pools,
-                256 MiB footprint).
+                (per token per value head, split by the kernel that forms each
+                product; see prefill_flops_per_token_head) / mean launch time,
+                against the bf16 dense MFMA peak (2.5 PFLOP/s spec, and the
+                peak measured on this GPU by libgdnpeak.so).
+  prefill_step_roofline  the whole step: 8*C*d + 6*d^2 flops per token-head
+                over ms_per_step, against both peaks.
+  measured_peaks  bf16 MFMA throughput and HBM copy / read rates measured here.
+  decode        gdn_recurrent_step on 64 sequences x 128 steps: tokens/s and
+                state + I/O bytes / kernel time against the 8 TB/s HBM peak
+                and the measured copy rate, headline from the ping-pong run
+                (two 128 MiB pools, 256 MiB footprint, beyond the 256 MB
+                last-level cache); the in-place run (128 MiB) alongside.
   decode_multi  gdn_recurrent_multi on 64 sequences x 4 tokens (speculative
                 verification), state in place; HBM roofline on state + I/O.
   varlen        8 packed sequences of 17..8192 tokens (12221), one call.
@@ -32,6 +36,9 @@ Alongside (same JSON line):
   layer_decode  the fused layer path on the decode workload, per step.
   cpu_baseline  the fp64 oracle (test infrastructure, never tuned) on the
                 same prefill workload, on this host's cores.
+The gates follow the workloads' recipe: beta = sigmoid(b) and
+g = -exp(A_log) softplus(a) of the raw draws a, b ~ N(0, 1), evaluated here
+(workload_gates).
 All inputs are seeded synthetic data (see gdn_inputs.py).
 """
 from __future__ import annotations
@@ -109,11 +116,87 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def workload_gates(a, b, ssm_a, ssm_dt):
+    """The workloads' gates from the generator's raw draws a, b ~ N(0, 1):
+    beta = sigmoid(b), g = ssm_a * softplus(a + ssm_dt) (ssm_dt = 0 for the
+    named workloads), evaluated in fp64 and rounded once to fp32."""
+    x = np.asarray(a, np.float64) + np.asarray(ssm_dt, np.float64)[None, :]
+    softplus = np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+    bb = np.asarray(b, np.float64)
+    e = np.exp(-np.abs(bb))
+    beta = np.where(bb >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    g = softplus * np.asarray(ssm_a, np.float64)[None, :]
+    return g.astype(np.float32), beta.astype(np.float32)
+
+
+WG = dict(final_gates=workload_gates)
+
+
 def prefill_flops_per_token_head(H_k, H_v, d_k, d_v):
+    """Algorithmic flops per token per value head, split by the kernel that
+    forms each product (C = 64):
+      preparation: K K^T and Q K^T once per key head (4 C d_k / r, r = H_v/H_k),
+                   W = T diag(.) K (2 C d_k), U0 = T diag(beta) V (2 C d_v)
+      scan:        W S, Q S, K^T U (6 d_k d_v) and P U (2 C d_v)
+    The sum is 8 C d + 6 d^2 = 163 840 at d = 128, r = 2 (the triangular
+    solve is not counted)."""
     r = H_v // H_k
-    prep = 4 * C * d_k // r + 2 * C * d_k
-    scan = 4 * C * d_v + 6 * d_k * d_v
+    prep = 4 * C * d_k // r + 2 * C * d_k + 2 * C * d_v
+    scan = 2 * C * d_v + 6 * d_k * d_v
     return prep, scan
+
+
+PEAK_LIB = os.path.join(ROOT, "gated_deltanet_rule_amd", "libgdnpeak.so")
+
+
+def measure_peaks(dev, reps=5):
+    """Measured machine peaks on this GPU (libgdnpeak.so): dense bf16 MFMA
+    throughput (independent 16x16x32 products on every SIMD), and HBM
+    streaming copy and read rates over 1 GiB buffers (4x the last-level
+    cache).  Median of `reps` timed launches after one untimed launch."""
+    import ctypes
+    lib = ctypes.CDLL(PEAK_LIB)
+    lib.gdn_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.gdn_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                  ctypes.c_void_p]
+    lib.gdn_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def timed(fn):
+        fn()
+        out = []
+        for _ in range(reps):
+            t = Timer(stream, 2)
+            t.mark(0)
+            fn()
+            t.mark(1)
+            torch.cuda.synchronize()
+            out.append(t.ms(0, 1))
+        return statistics.median(out)
+
+    sink = torch.zeros(1 << 16, dtype=torch.float32, device=dev)
+    grid, iters = 4 * cus, 4000
+    settle(lambda: lib.gdn_peak_mfma_bf16(grid, 200, ctypes.c_void_p(sink.data_ptr()), sp), ms=50)
+    ms = timed(lambda: lib.gdn_peak_mfma_bf16(grid, iters, ctypes.c_void_p(sink.data_ptr()), sp))
+    mfma = grid * 8 * iters * 8 * 16 * 16 * 32 * 2 / (ms * 1e-3) / 1e12
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    cgrid = 16 * cus
+    ms_c = timed(lambda: lib.gdn_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                           nbytes, cgrid, sp))
+    ms_r = timed(lambda: lib.gdn_peak_read(ctypes.c_void_p(src.data_ptr()), nbytes, cgrid,
+                                           ctypes.c_void_p(sink.data_ptr()), sp))
+    assert torch.equal(dst[:1024], src[:1024])
+    del src, dst
+    return {"mfma_bf16_tflops": mfma, "hbm_copy_gbs": 2 * nbytes / (ms_c * 1e-3) / 1e9,
+            "hbm_read_gbs": nbytes / (ms_r * 1e-3) / 1e9,
+            "what": "bf16 16x16x32 MFMA, 8 independent accumulators per wave, 4 x 512-thread "
+                    "workgroups per CU; copy and read of 1 GiB with 16-byte non-temporal accesses "
+                    "(copy counts read + written bytes)"}
 
 
 def to_dev(case, dev):
@@ -155,7 +238,7 @@ class Timer:
 
 
 def bench_prefill(gdn, dev, steps, warmup):
-    case = gi.config1()
+    case = gi.config1(**WG)
     d = to_dev(case, dev)
     out = torch.empty(d["v"].shape, dtype=torch.float32, device=dev)
     state_out = torch.empty_like(d["pool"])
@@ -201,7 +284,8 @@ def bench_prefill(gdn, dev, steps, warmup):
     fp, fs = prefill_flops_per_token_head(case.H_k, case.H_v, case.d_k, case.d_v)
     units = T * H_v
     kern = {
-        "prepare": {"kernels": "chunk_table_kernel + prep_kernel", "mean_ms": prep_ms,
+        # one sequence: the chunks follow from T, no chunk-table launch
+        "prepare": {"kernels": "prep_kernel", "mean_ms": prep_ms,
                     "flops_per_token_head": fp,
                     "tflops": fp * units / (prep_ms * 1e-3) / 1e12},
         "scan": {"kernels": "scan_kernel", "mean_ms": scan_ms, "flops_per_token_head": fs,
@@ -212,11 +296,15 @@ def bench_prefill(gdn, dev, steps, warmup):
     roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom),
             "traffic_unit": "bytes per launch", "kernel": kern[dom]["kernels"],
+            "flops_per_token_head": kern[dom]["flops_per_token_head"],
+            "units_per_launch": units,
             "flops_per_launch": kern[dom]["flops_per_token_head"] * units,
             "mean_launch_ms": kern[dom]["mean_ms"]}
     whole = (fp + fs) * units / (ms_step * 1e-3) / 1e12
+    step = {"flops_per_token_head": fp + fs, "flops_per_step": (fp + fs) * units,
+            "achieved": whole, "unit": "TFLOP/s", "frac": whole / PEAK_BF16_TFLOPS}
     return case, dict(ms_step=ms_step, tokens_s=T / (ms_step * 1e-3), roofline=roof,
-                      kernels=kern, step_tflops=whole, step_mfma_frac=whole / PEAK_BF16_TFLOPS)
+                      kernels=kern, step=step)
 
 
 def decode_bytes_per_step(dc, in_bytes=2, out_bytes=4):
@@ -230,7 +318,7 @@ def decode_bytes_per_step(dc, in_bytes=2, out_bytes=4):
 
 
 def bench_decode(gdn, dev, reps=3):
-    dc = gi.config2()
+    dc = gi.config2(**WG)
     dt = torch.bfloat16
     f = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(t)
     q, k, v = f(dc.q, dt), f(dc.k, dt), f(dc.v, dt)
@@ -288,24 +376,27 @@ def bench_decode(gdn, dev, reps=3):
     res["copy_reference"] = {"what": "torch copy_ of the 128 MiB pool into a second pool",
                              "bytes": cby, "ms": cms, "achieved_gbs": cby / (cms * 1e-3) / 1e9,
                              "frac": cby / (cms * 1e-3) / 1e9 / PEAK_HBM_GBS}
-    ip = res["in_place"]
+    ip, pp = res["in_place"], res["ping_pong"]
+    # the headline rate is the ping-pong run: its two pools (256 MiB) do not
+    # fit the 256 MB last-level cache, so its bytes come from HBM; the in-place
+    # pool (128 MiB) can be served partly from that cache
     return {"workload": "decode: 64 sequences x 128 steps, H_k=16 H_v=32 d=128, bf16 in, "
-                        "fp32 out, fp32 state slots (128 MiB pool)",
-            "value": ip["tokens_s"], "unit": "tokens/s",
-            "ms_per_step": ip["mean_launch_ms"],
-            "roofline": {"bound": "hbm", "achieved": ip["achieved_gbs"], "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": ip["frac"], "traffic": measured_traffic("decode"),
-                         "traffic_unit": "bytes per launch",
-                         "kernel": "decode_kernel", "bytes_per_launch": ip["bytes_per_launch"],
-                         "mean_launch_ms": ip["mean_launch_ms"]},
-            "ping_pong": res["ping_pong"], "in_place": ip, "copy_reference": res["copy_reference"]}
+                        "fp32 out, fp32 state slots (two 128 MiB pools, ping-pong)",
+            "value": pp["tokens_s"], "unit": "tokens/s",
+            "ms_per_step": pp["mean_launch_ms"],
+            "roofline": {"bound": "hbm", "achieved": pp["achieved_gbs"], "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": pp["frac"], "traffic": measured_traffic("decode"),
+                         "traffic_unit": "bytes per launch (in-place run)",
+                         "kernel": "decode_kernel", "bytes_per_launch": pp["bytes_per_launch"],
+                         "mean_launch_ms": pp["mean_launch_ms"]},
+            "ping_pong": pp, "in_place": ip, "copy_reference": res["copy_reference"]}
 
 
 def bench_decode_multi(gdn, dev, tokens=4, reps=200):
     """gdn_recurrent_multi: 64 sequences x `tokens` tokens (speculative
     verification), state pool in place; HBM roofline on state + I/O bytes."""
     case = gi.make_case(f"spec64x{tokens}", [tokens] * 64, dtype="bf16", seed=40 + tokens,
-                        **gi.QWEN3_NEXT_HEADS)
+                        final_gates=workload_gates, **gi.QWEN3_NEXT_HEADS)
     d = to_dev(case, dev)
     out = torch.empty(d["v"].shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -347,7 +438,7 @@ def bench_layer_prefill(gdn, dev, reps=50):
     """The fused layer path on the T=4096 prefill: mixed q|k|v rows through
     the convolution prologue, raw gate projections, gated RMSNorm epilogue,
     bf16 output; one gdn_chunked_prefill call per step."""
-    case = gi.config1()
+    case = gi.config1(**WG)
     L = gi.make_layer_inputs(case.total_tokens, case.pool.shape[0], case.H_k, case.H_v, case.d_k,
                              case.d_v, "bf16", 1)
     d = _layer_dev(case, L, dev)
@@ -383,7 +474,7 @@ def bench_layer_decode(gdn, dev, reps=3):
     """The fused layer path on the decode workload: 64 sequences x 128
     steps, one gdn_recurrent_step per step with the prologue (mixed rows,
     convolution state in the slot rows), raw gates and the epilogue."""
-    dc = gi.config2()
+    dc = gi.config2(**WG)
     S, N = dc.n_steps, dc.n_seqs
     L = gi.make_layer_inputs(S * N, N, dc.H_k, dc.H_v, dc.d_k, dc.d_v, "bf16", 2)
     f = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(t)
@@ -432,7 +523,7 @@ def bench_varlen(gdn, dev, reps=20):
     """The varlen batch as one gdn_chunked_prefill call (it runs as chunk
     ranges of about 64 chunks), and as the two split-phase calls (one range
     over the whole batch) for comparison."""
-    case = gi.config3()
+    case = gi.config3(**WG)
     d = to_dev(case, dev)
     out = torch.empty(d["v"].shape, dtype=torch.float32, device=dev)
     pool_out = d["pool"].clone()
@@ -467,7 +558,7 @@ def bench_varlen(gdn, dev, reps=20):
 
 
 def bench_stream(gdn, dev, reps=2):
-    case = gi.config4()
+    case = gi.config4(**WG)
     d = to_dev(case, dev)
     T, U = case.total_tokens, 512
     out = torch.empty(d["v"].shape, dtype=torch.float32, device=dev)
@@ -626,8 +717,17 @@ def main():
     log(f"  {pf['ms_step']:.4f} ms/step, {pf['tokens_s']:.4g} tok/s")
     if args.prefill_only:
         return
+    log("measured peaks ...")
+    peaks = measure_peaks(dev)
+    log(f"  bf16 MFMA {peaks['mfma_bf16_tflops']:.0f} TFLOP/s, HBM copy {peaks['hbm_copy_gbs']:.0f} GB/s, "
+        f"read {peaks['hbm_read_gbs']:.0f} GB/s")
+    for r in (pf["roofline"], pf["step"]):
+        r["peak_measured"] = peaks["mfma_bf16_tflops"]
+        r["frac_measured"] = r["achieved"] / peaks["mfma_bf16_tflops"]
     log("decode 64x128 ...")
     dec = bench_decode(gdn, dev)
+    dec["roofline"]["peak_measured"] = peaks["hbm_copy_gbs"]
+    dec["roofline"]["frac_measured"] = dec["roofline"]["achieved"] / peaks["hbm_copy_gbs"]
     log(f"  {dec['ms_per_step']*1e3:.2f} us/step, {dec['roofline']['achieved']:.0f} GB/s "
         f"(device copy of the pool: {dec['copy_reference']['achieved_gbs']:.0f} GB/s)")
     extra = {}
@@ -675,8 +775,8 @@ def main():
                    "chunk": C, "parallelism": "single GPU"},
         "roofline": pf["roofline"],
         "prefill_kernels": pf["kernels"],
-        "prefill_step_tflops": pf["step_tflops"],
-        "prefill_step_mfma_frac": pf["step_mfma_frac"],
+        "prefill_step_roofline": pf["step"],
+        "measured_peaks": peaks,
         "decode": dec,
         "cpu_baseline": cpu,
     }

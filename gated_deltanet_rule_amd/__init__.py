@@ -46,7 +46,8 @@ class Dims(ctypes.Structure):
                 ("eps", ctypes.c_float), ("gate_mode", ctypes.c_int32),
                 ("ssm_a", ctypes.c_void_p), ("ssm_dt", ctypes.c_void_p),
                 ("d_conv", ctypes.c_int32), ("conv_w", ctypes.c_void_p),
-                ("z", ctypes.c_void_p), ("norm_w", ctypes.c_void_p)]
+                ("z", ctypes.c_void_p), ("norm_w", ctypes.c_void_p),
+                ("n_slots", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -167,6 +168,13 @@ def _dims_from(q, v, out, scale, eps, state, gates=None, conv=None, z=None, norm
                      scale, eps, stride, gates, None, z, norm_w)
 
 
+def _n_slots(*pools) -> int:
+    """Slots of the state pools ([n_slots, ...] tensors), for check mode's
+    range check of the slot indices (the smallest pool bounds both lists)."""
+    n = [t.shape[0] for t in pools if t is not None and t.dim() in (2, 4)]
+    return min(n) if n else 0
+
+
 def _need_qkv(q, k, v, conv):
     dev = q.device
     if conv is None:
@@ -232,6 +240,7 @@ def prefill(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in, slo
     for t, name in ((cu_seqlens, "cu_seqlens"), (slot_in, "slot_in"), (slot_out, "slot_out")):
         _need(t, name, torch.int32, dev)
     dims = _dims_from(q, v, out, scale, eps, state_out, gates, conv, z, norm_w)
+    dims.n_slots = _n_slots(state_in, state_out)
     n_seqs = slot_out.shape[0]
     T = q.shape[0]
     if workspace is None:
@@ -292,6 +301,7 @@ class PrefillPlan:
                 _need(t, name, torch.float32, dev)
         for t, name in ((slot_in, "slot_in"), (slot_out, "slot_out")):
             _need(t, name, torch.int32, dev)
+        self.dims.n_slots = _n_slots(state_in, state_out)
         _check(lib.gdn_prefill_scan(ctypes.byref(self.dims), _ptr(state_in), _ptr(state_out),
                                     _ptr(out), _ptr(slot_in), _ptr(slot_out), self.n_seqs,
                                     self.T, _ptr(self.workspace), self.workspace.numel(),
@@ -312,6 +322,7 @@ def decode_step(q, k, v, g, beta, state_in, state_out, out, slot_in, slot_out, *
     for t, name in ((slot_in, "slot_in"), (slot_out, "slot_out")):
         _need(t, name, torch.int32, dev)
     dims = _dims_from(q, v, out, scale, eps, state_out, gates, conv, z, norm_w)
+    dims.n_slots = _n_slots(state_in, state_out)
     _check(lib.gdn_recurrent_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                   _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
                                   _ptr(slot_in), _ptr(slot_out), slot_out.shape[0],
@@ -333,6 +344,7 @@ def decode_multi(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in
     for t, name in ((cu_seqlens, "cu_seqlens"), (slot_in, "slot_in"), (slot_out, "slot_out")):
         _need(t, name, torch.int32, dev)
     dims = _dims_from(q, v, out, scale, eps, state_out, gates, conv, z, norm_w)
+    dims.n_slots = _n_slots(state_in, state_out)
     _check(lib.gdn_recurrent_multi(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                    _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
                                    _ptr(cu_seqlens), _ptr(slot_in), _ptr(slot_out),

@@ -25,6 +25,9 @@ LIB = os.path.join(PKG, "libgdn.so")
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["gdn_api.cpp", "gdn_check.hip", "gdn_decode.hip", "gdn_layer.hip", "gdn_prefill.hip"]
+# machine-peak microbenchmarks for the benchmark's roofline: a library of their own
+PEAK_SOURCES = ["gdn_peak.hip"]
+PEAK_LIB = os.path.join(PKG, "libgdnpeak.so")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -53,19 +56,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 0, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 0, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PEAK_SOURCES
+    jobs = jobs or min(len(srcs), os.cpu_count() or 1)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PEAK_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAK_LIB}")
     return LIB
 
 

@@ -83,6 +83,8 @@ gdn_status resolve(const gdn_dims *d, gdn::Problem *p)
     }
     p->rs_qk = d->d_conv ? conv_dim : (int64_t)d->H_k * d->d_k;
     p->rs_v = d->d_conv ? conv_dim : (int64_t)d->H_v * d->d_v;
+    if (d->n_slots < 0) return fail(GDN_ERR_INVALID_ARG, "n_slots must be >= 0 (got %d)", d->n_slots);
+    p->n_slots = d->n_slots;
     p->z = d->z;
     p->norm_w = nullptr;
     if (d->z) {
@@ -126,12 +128,13 @@ bool check_mode()
     return e && e[0] == '1' && e[1] == 0;
 }
 
-gdn_status device_check(const int32_t *cu, int32_t n, int64_t T, const int32_t *slot_in,
-                        const int32_t *slot_out, hipStream_t s)
+gdn_status device_check(const gdn::Problem &p, const int32_t *cu, int32_t n, int64_t T,
+                        const int32_t *slot_in, const int32_t *slot_out, hipStream_t s)
 {
     if (!check_mode()) return GDN_OK;
     int v = 0;
-    gdn_status st = hip_status(gdn::run_check(cu, n, T, slot_in, slot_out, s, &v), "GDN_CHECK validation");
+    gdn_status st = hip_status(gdn::run_check(cu, n, T, slot_in, slot_out, p.n_slots, s, &v),
+                               "GDN_CHECK validation");
     if (st != GDN_OK) return st;
     if (v & gdn::kCheckCuStart) return fail(GDN_ERR_INVALID_ARG, "GDN_CHECK: cu_seqlens[0] is not 0");
     if (v & gdn::kCheckCuEnd)
@@ -141,6 +144,8 @@ gdn_status device_check(const int32_t *cu, int32_t n, int64_t T, const int32_t *
     if (v & gdn::kCheckSlotDup) return fail(GDN_ERR_INVALID_ARG, "GDN_CHECK: two sequences write the same slot");
     if (v & gdn::kCheckSlotAlias)
         return fail(GDN_ERR_INVALID_ARG, "GDN_CHECK: a sequence writes a slot that another sequence reads");
+    if (v & gdn::kCheckSlotRange)
+        return fail(GDN_ERR_INVALID_ARG, "GDN_CHECK: a slot index is not below n_slots (%d)", p.n_slots);
     return GDN_OK;
 }
 
@@ -274,7 +279,7 @@ gdn_status gdn_prefill_prepare(const gdn_dims *dims, const void *q, const void *
     if (st == GDN_OK) st = check_prepare_inputs(q, k, v, g, beta, cu_seqlens);
     if (st == GDN_OK) st = check_workspace(p, n_seqs, total_tokens, workspace, workspace_bytes);
     if (st != GDN_OK) return st;
-    st = device_check(cu_seqlens, n_seqs, total_tokens, nullptr, nullptr, static_cast<hipStream_t>(stream));
+    st = device_check(p, cu_seqlens, n_seqs, total_tokens, nullptr, nullptr, static_cast<hipStream_t>(stream));
     if (st != GDN_OK) return st;
     gdn::PrefillArgs a{q, k, v, g, beta, nullptr, nullptr, nullptr, cu_seqlens, nullptr,
                        nullptr, n_seqs, total_tokens, workspace, nullptr, nullptr};
@@ -299,7 +304,7 @@ gdn_status gdn_prefill_scan(const gdn_dims *dims, const float *state_in, float *
     gdn::PrefillArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, state_in, state_out, out, nullptr, slot_in,
                        slot_out, n_seqs, total_tokens, const_cast<void *>(workspace), nullptr, nullptr};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    st = device_check(nullptr, n_seqs, n_seqs, slot_in, slot_out, s);
+    st = device_check(p, nullptr, n_seqs, n_seqs, slot_in, slot_out, s);
     if (st != GDN_OK) return st;
     return hip_status(gdn::launch_scan(p, a, gdn::Segment{}, s), "scan");
 }
@@ -333,12 +338,13 @@ gdn_status gdn_chunked_prefill(const gdn_dims *dims, const void *q, const void *
                        cu_seqlens, slot_in, slot_out, n_seqs, total_tokens, workspace,
                        state_in, state_out, per};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    st = device_check(cu_seqlens, n_seqs, total_tokens, slot_in, slot_out, s);
+    st = device_check(p, cu_seqlens, n_seqs, total_tokens, slot_in, slot_out, s);
     if (st != GDN_OK) return st;
     for (int k = 0; k < n_seg && st == GDN_OK; ++k) {
         gdn::Segment sg;
         sg.lo = k * per;
         sg.hi = k + 1 == n_seg ? 0x7fffffff : (k + 1) * per;
+        sg.idx = k;
         sg.first = k == 0;
         sg.last = k + 1 == n_seg;
         st = hip_status(gdn::launch_prepare(p, a, sg, s), "prepare");
@@ -372,7 +378,7 @@ gdn_status gdn_recurrent_step(const gdn_dims *dims, const void *q, const void *k
     gdn::DecodeArgs a{q, k, v, g, beta, ssm_part(p, state_in), ssm_part(p, state_out), out,
                       slot_in, slot_out, n_seqs, state_in, state_out};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    st = device_check(nullptr, n_seqs, n_seqs, slot_in, slot_out, s);
+    st = device_check(p, nullptr, n_seqs, n_seqs, slot_in, slot_out, s);
     if (st != GDN_OK) return st;
     st = hip_status(gdn::launch_decode(p, a, s), "decode");
     if (st == GDN_OK && p.conv_w)
@@ -402,7 +408,7 @@ gdn_status gdn_recurrent_multi(const gdn_dims *dims, const void *q, const void *
     gdn::DecodeMultiArgs a{q, k, v, g, beta, ssm_part(p, state_in), ssm_part(p, state_out), out,
                            cu_seqlens, slot_in, slot_out, n_seqs, total_tokens, state_in, state_out};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    st = device_check(cu_seqlens, n_seqs, total_tokens, slot_in, slot_out, s);
+    st = device_check(p, cu_seqlens, n_seqs, total_tokens, slot_in, slot_out, s);
     if (st != GDN_OK) return st;
     st = hip_status(gdn::launch_decode_multi(p, a, s), "multi-token decode");
     if (st == GDN_OK && p.conv_w)

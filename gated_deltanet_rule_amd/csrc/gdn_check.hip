@@ -4,6 +4,8 @@
 // give wrong results rather than faults.  In check mode the library runs this
 // kernel first, reads its flags back (synchronising the stream) and
 // rejects the call before any other kernel is launched.
+#include <atomic>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -13,12 +15,14 @@ namespace {
 constexpr int kCheckMaxPairs = 16384;
 
 // One workgroup.  cu: null for one token per sequence (decode); slot_out
-// null: no slot lists (slot_in may be null on its own).  The flags
+// null: no slot lists (slot_in may be null on its own); n_slots > 0 bounds
+// the slot indices.  The flags
 // (check_* bits) is gathered in LDS and written by thread 0 at the end, so
 // the result buffer needs no clearing.
 __global__ __launch_bounds__(1024) void check_kernel(const int32_t *__restrict__ cu, int32_t n, int64_t T,
                                                      const int32_t *__restrict__ slot_in,
-                                                     const int32_t *__restrict__ slot_out, int *result)
+                                                     const int32_t *__restrict__ slot_out, int n_slots,
+                                                     int *result)
 {
     __shared__ int flags;
     if (threadIdx.x == 0) flags = 0;
@@ -32,6 +36,13 @@ __global__ __launch_bounds__(1024) void check_kernel(const int32_t *__restrict__
         for (int i = threadIdx.x; i < n; i += blockDim.x)
             if (cu[i + 1] < cu[i]) bad |= kCheckCuOrder;
     }
+    // slot indices inside the pool (when its size is given); negative
+    // indices mean "zero state" / "not stored" and are always valid
+    if (n_slots > 0)
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+            if (slot_in && slot_in[i] >= n_slots) bad |= kCheckSlotRange;
+            if (slot_out && slot_out[i] >= n_slots) bad |= kCheckSlotRange;
+        }
     // out slots pairwise distinct; no sequence writes a slot another reads
     // (all pairs: batches above kCheckMaxPairs sequences skip this part; a
     // call without slot lists, the preparation half, has none to check)
@@ -49,17 +60,23 @@ __global__ __launch_bounds__(1024) void check_kernel(const int32_t *__restrict__
     if (threadIdx.x == 0) *result = flags;
 }
 
-__device__ int g_check_result;
+// One result word per checked call: calls take the words in turn (a
+// process-wide counter), so up to kCheckWords calls in flight on a device at
+// once never share one.  Each device holds its own copy of the array.
+constexpr int kCheckWords = 64;
+__device__ int g_check_result[kCheckWords];
+std::atomic<unsigned> g_check_next{0};
 
 }  // namespace
 
 hipError_t run_check(const int32_t *cu, int32_t n, int64_t T, const int32_t *slot_in, const int32_t *slot_out,
-                     hipStream_t s, int *flags)
+                     int n_slots, hipStream_t s, int *flags)
 {
-    int *res = nullptr;
-    hipError_t e = hipGetSymbolAddress(reinterpret_cast<void **>(&res), HIP_SYMBOL(g_check_result));
+    int *words = nullptr;
+    hipError_t e = hipGetSymbolAddress(reinterpret_cast<void **>(&words), HIP_SYMBOL(g_check_result));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(check_kernel, dim3(1), dim3(1024), 0, s, cu, n, T, slot_in, slot_out, res);
+    int *res = words + g_check_next.fetch_add(1, std::memory_order_relaxed) % kCheckWords;
+    hipLaunchKernelGGL(check_kernel, dim3(1), dim3(1024), 0, s, cu, n, T, slot_in, slot_out, n_slots, res);
     e = hipGetLastError();
     if (e == hipSuccess) e = hipMemcpyAsync(flags, res, sizeof(int), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);

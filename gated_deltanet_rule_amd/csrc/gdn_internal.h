@@ -29,6 +29,8 @@ struct Problem {
     // epilogue: out = o / sqrt(mean(o^2) + eps) * norm_w * silu(z); z null = off
     const void *z;
     const float *norm_w;
+    // slots in the state pools (0: unknown); read only by check mode
+    int n_slots;
 };
 
 // Taps of the fused convolution prologue.
@@ -104,6 +106,7 @@ size_t prefill_workspace_bytes(const Problem &p, int32_t n_seqs, int64_t total_t
 // workspace.
 struct Segment {
     int lo = 0, hi = 0x7fffffff;   // chunks [lo, hi) of the batch
+    int idx = 0;                   // index of the range
     bool first = true;             // the first range: builds the chunk table
     bool last = true;              // the last range: runs the epilogue
 };
@@ -136,8 +139,9 @@ constexpr int kCheckCuEnd = 2;       // cu_seqlens[n_seqs] != total_tokens
 constexpr int kCheckCuOrder = 4;     // cu_seqlens decreases somewhere
 constexpr int kCheckSlotDup = 8;     // two sequences write the same slot
 constexpr int kCheckSlotAlias = 16;  // a sequence writes a slot another one reads
+constexpr int kCheckSlotRange = 32;  // a slot index at or past n_slots (when given)
 hipError_t run_check(const int32_t *cu, int32_t n, int64_t T, const int32_t *slot_in, const int32_t *slot_out,
-                     hipStream_t s, int *flags);
+                     int n_slots, hipStream_t s, int *flags);
 
 // Layer fusion passes (gdn_layer.hip).
 // New convolution state of every sequence: the last kConv - 1 inputs of its

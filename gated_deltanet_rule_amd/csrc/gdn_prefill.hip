@@ -132,8 +132,15 @@ int cu_count()
 bool op_bf16(const Problem &p) { return p.bf16 != 0; }
 bool op_split(const Problem &p) { return p.bf16 && p.conv_w; }
 
+int chunk_count(int32_t n_seqs, int64_t T)
+{
+    return n_seqs == 1 ? (int)((T + C - 1) / C) : (int)max_chunks(n_seqs, T);
+}
+
 // slots: WY-factor slots (chunks held at once); 0 or more than the batch has
-// means one per chunk.
+// means one per chunk.  With fewer slots than chunks the batch runs as
+// several ranges, and two carry states pass a sequence's state from range to
+// range.
 WsLayout ws_layout(const Problem &p, int32_t n_seqs, int64_t T, int slots)
 {
     WsLayout L;
@@ -148,7 +155,8 @@ WsLayout ws_layout(const Problem &p, int32_t n_seqs, int64_t T, int slots)
     L.kblocks = L.vblocks + L.vblk * fs * p.H_v;
     L.obuf = align256(L.kblocks + L.kblk * fs * p.H_k);
     L.carry = align256(L.obuf + (stage_o(p) ? sizeof(float) * (size_t)T * p.H_v * p.d_v : 0));
-    L.total = L.carry + sizeof(float) * (size_t)n_seqs * p.H_v * p.d_k * p.d_v;
+    const bool ranges = slots > 0 && slots < chunk_count(n_seqs, T);
+    L.total = L.carry + (ranges ? 2 * sizeof(float) * (size_t)p.H_v * p.d_k * p.d_v : 0);
     return L;
 }
 
@@ -1023,10 +1031,14 @@ struct ScanParams {
     int H_k, H_v;
     int64_t slot_stride;
     int single_T;      // >= 0: one sequence of this many tokens, no chunk table
-    // chunks [seg_lo, seg_hi) of the batch; a sequence that began in an
-    // earlier range takes its state from carry, one that goes on past this
-    // range leaves it there ([sequence][H_v][DK][DV] fp32)
-    int seg_lo, seg_hi;
+    // chunks [seg_lo, seg_hi) of the batch, the seg_idx-th range; a sequence
+    // that began in an earlier range takes its state from the carry state of
+    // the previous range's parity, one that goes on past this range leaves
+    // it in the carry state of this range's parity ([2][H_v][DK][DV] fp32).
+    // At most one sequence crosses each range boundary, and consecutive
+    // ranges use the two states in turn, so the reads of one launch never
+    // meet its writes.
+    int seg_lo, seg_hi, seg_idx;
     float *carry;
 };
 
@@ -1131,7 +1143,8 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
     if (empty ? sp.seg_lo != 0 : cs >= ce) return;      // uniform over the workgroup
     const bool carried_in = !empty && cs_seq < sp.seg_lo;
     const bool carried_out = !empty && ce_seq > sp.seg_hi;
-    float *carry = sp.carry + ((int64_t)i * sp.H_v + h) * DK * DV + col0 + n;
+    const float *carry_in = sp.carry + ((int64_t)((sp.seg_idx + 1) & 1) * sp.H_v + h) * DK * DV + col0 + n;
+    float *carry_out = sp.carry + ((int64_t)(sp.seg_idx & 1) * sp.H_v + h) * DK * DV + col0 + n;
     const size_t vstride = (size_t)G::VBLK * 1024, kstride = (size_t)G::KBLK * 1024;
     const char *vbase = sp.vblocks + (size_t)h * vstride;
     const char *kbase = sp.kblocks + (size_t)kh * kstride;
@@ -1159,7 +1172,7 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
         floatx4 Sreg[NOWN][TPB];
         {
             const int sin = sp.state_in ? sp.slot_in[i] : -1;
-            const float *base = carried_in ? carry
+            const float *base = carried_in ? carry_in
                               : sin >= 0   ? sp.state_in + (int64_t)sin * sp.slot_stride + (int64_t)h * DK * DV + col0 + n
                                            : nullptr;
 #pragma unroll
@@ -1293,7 +1306,7 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
 
         const int sout = sp.slot_out[i];
         if (carried_out || sout >= 0) {
-            float *base = carried_out ? carry : sp.state_out + (int64_t)sout * sp.slot_stride + (int64_t)h * DK * DV + col0 + n;
+            float *base = carried_out ? carry_out : sp.state_out + (int64_t)sout * sp.slot_stride + (int64_t)h * DK * DV + col0 + n;
 #pragma unroll
             for (int o = 0; o < NOWN; ++o) {
                 const int kb = rt + 4 * o;
@@ -1476,7 +1489,7 @@ hipError_t scan_t(const Problem &p, const PrefillArgs &a, const Segment &sg, hip
     void *o = stage_o(p) ? static_cast<void *>(w.obuf) : a.out;
     ScanParams sp{a.state_in, a.state_out, o, a.slot_in, a.slot_out, w.cstart, w.ent,
                   w.vblocks, w.kblocks, p.H_k, p.H_v, p.slot_stride,
-                  a.n_seqs == 1 ? (int)a.total_tokens : -1, sg.lo, sg.hi, w.carry};
+                  a.n_seqs == 1 ? (int)a.total_tokens : -1, sg.lo, sg.hi, sg.idx, w.carry};
     // With several sequences, one scan workgroup per CU: two workgroups on
     // one CU contend for its vector-memory path and LDS (the varlen batch of
     // 12 221 tokens takes 0.39 instead of 0.30 ms in the scan), so the
@@ -1542,7 +1555,7 @@ size_t prefill_workspace_bytes(const Problem &p, int32_t n_seqs, int64_t total_t
 
 int prefill_chunk_count(const Problem &p, int32_t n_seqs, int64_t total_tokens)
 {
-    return n_seqs == 1 ? (int)((total_tokens + C - 1) / C) : (int)max_chunks(n_seqs, total_tokens);
+    return chunk_count(n_seqs, total_tokens);
 }
 
 int segment_chunks(const Problem &p, int chunks)

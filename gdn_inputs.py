@@ -14,17 +14,25 @@ distributions are:
 * q, k ~ N(0, 1), then scaled to unit L2 norm per head (fp64), then rounded to
   the storage dtype;
 * v ~ N(0, 1);
-* per value head a decay rate ssm_a = -U(lo, hi) (strong decay: lo, hi = 1, 16;
-  weak decay: 0.001, 0.01) and a gate bias ssm_dt = U(-1, 1);
-* the op's gate inputs g = ssm_a * E with E ~ Exponential(1) (so g <= 0), and
-  beta ~ U(0, 1);
-* the raw projections a, b ~ N(0, 1) for the in-kernel activation path (the
-  oracle, not this module, turns them into g and beta);
+* per value head a decay rate ssm_a = -exp(A_log), A_log = log U(lo, hi)
+  (strong decay: lo, hi = 1, 16, the workloads' recipe; weak decay: 0.001,
+  0.01), i.e. ssm_a = -U(lo, hi);
+* the raw gate projections a, b ~ N(0, 1) per token and value head, and a
+  per-head gate bias ssm_dt = 0 (U(-1, 1) with gate_bias=True, to exercise
+  the bias input of the in-kernel activations);
 * initial states ~ N(0, 0.02) (or zero).
 
-Draw order is fixed: ssm_a, q, k, v, E, beta, a, b, ssm_dt, initial states,
-slots.  bf16 storage is round-to-nearest-even of the fp32 value; arrays are
-returned as float32 numpy arrays that hold the exactly rounded values, so the
+The workloads state the operator's gates as beta = sigmoid(b) and
+g = ssm_a * softplus(a + ssm_dt) of these draws.  Those two functions are
+the layer's gate activations, part of the method under test when the kernels
+apply them (gate_mode GDN_GATES_RAW), so this module does not evaluate them:
+a caller that wants the final gates passes `final_gates(a, b, ssm_a, ssm_dt)
+-> (g, beta)`, evaluated by the test or benchmark harness.  Without it, g and
+beta are None and only the raw projections are available.  beta_mode
+"zero"/"one" and decay "zero" (g = 0) set the final gates directly.
+
+Draw order is fixed: ssm_a, q, k, v, a, b, [ssm_dt], initial states, slots.
+bf16 storage is round-to-nearest-even of the fp32 value; arrays are returned as float32 numpy arrays that hold the exactly rounded values, so the
 oracle (which upcasts to fp64) and the GPU (which converts to bf16 without
 further rounding) consume identical numbers.
 """
@@ -66,15 +74,15 @@ class Case:
     q: np.ndarray              # [T][H_k][d_k] float32 (values exact in dtype)
     k: np.ndarray              # [T][H_k][d_k]
     v: np.ndarray              # [T][H_v][d_v]
-    g: np.ndarray              # [T][H_v] float32, log-decay <= 0
-    beta: np.ndarray           # [T][H_v] float32 in [0, 1]
+    g: Optional[np.ndarray]    # [T][H_v] float32, log-decay <= 0 (None: not evaluated)
+    beta: Optional[np.ndarray]  # [T][H_v] float32 in [0, 1] (None: not evaluated)
     pool: np.ndarray           # [n_slots][H_v][d_k][d_v] float32 initial state pool
     slot_in: np.ndarray        # [N] int32 (-1 = zero initial state)
     slot_out: np.ndarray       # [N] int32
     ssm_a: np.ndarray          # [H_v] float32 decay rate (<= 0)
     raw_a: np.ndarray          # [T][H_v] float32 raw gate projection
     raw_b: np.ndarray          # [T][H_v] float32 raw write-strength projection
-    ssm_dt: np.ndarray         # [H_v] float32 gate bias
+    ssm_dt: np.ndarray         # [H_v] float32 gate bias (zero unless gate_bias)
 
     @property
     def n_seqs(self) -> int:
@@ -89,7 +97,8 @@ class Case:
         return np.concatenate([[0], np.cumsum(self.lengths)]).astype(np.int32)
 
 
-def _draw(rng, T, H_k, H_v, d_k, d_v, dtype, decay, beta_mode, a_lo, a_hi):
+def _draw(rng, T, H_k, H_v, d_k, d_v, dtype, decay, beta_mode, a_lo, a_hi,
+          final_gates=None, gate_bias=False):
     if decay == "strong":
         ssm_a = -rng.uniform(1.0, 16.0, size=H_v)
     elif decay == "weak":
@@ -100,25 +109,26 @@ def _draw(rng, T, H_k, H_v, d_k, d_v, dtype, decay, beta_mode, a_lo, a_hi):
         ssm_a = np.zeros(H_v)
     else:
         raise ValueError(decay)
+    if beta_mode not in ("random", "zero", "one"):
+        raise ValueError(beta_mode)
     q = _unit_rows(rng.standard_normal((T, H_k, d_k)))
     k = _unit_rows(rng.standard_normal((T, H_k, d_k)))
     v = rng.standard_normal((T, H_v, d_v))
-    e = rng.exponential(1.0, size=(T, H_v))
-    bu = rng.uniform(0.0, 1.0, size=(T, H_v))
     raw_a = rng.standard_normal((T, H_v))
     raw_b = rng.standard_normal((T, H_v))
-    ssm_dt = rng.uniform(-1.0, 1.0, size=H_v)
-    g = ssm_a[None, :] * e
+    ssm_dt = rng.uniform(-1.0, 1.0, size=H_v) if gate_bias else np.zeros(H_v)
+    f32 = lambda x: np.ascontiguousarray(x, dtype=np.float32)
+    ssm_a, raw_a, raw_b, ssm_dt = f32(ssm_a), f32(raw_a), f32(raw_b), f32(ssm_dt)
+    g = beta = None
+    if final_gates is not None:
+        g, beta = final_gates(raw_a, raw_b, ssm_a, ssm_dt)
+        g, beta = f32(g), f32(beta)
     if decay == "zero":
-        g = np.zeros_like(e)
-    if beta_mode == "random":
-        beta = bu
-    elif beta_mode == "zero":
-        beta = np.zeros_like(bu)
+        g = np.zeros((T, H_v), np.float32)
+    if beta_mode == "zero":
+        beta = np.zeros((T, H_v), np.float32)
     elif beta_mode == "one":
-        beta = np.ones_like(bu)
-    else:
-        raise ValueError(beta_mode)
+        beta = np.ones((T, H_v), np.float32)
     q = q.astype(np.float32)
     k = k.astype(np.float32)
     v = v.astype(np.float32)
@@ -126,22 +136,23 @@ def _draw(rng, T, H_k, H_v, d_k, d_v, dtype, decay, beta_mode, a_lo, a_hi):
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     elif dtype != "f32":
         raise ValueError(dtype)
-    f32 = lambda x: np.ascontiguousarray(x, dtype=np.float32)
-    return (f32(ssm_a), q, k, v, f32(g), f32(beta), f32(raw_a), f32(raw_b), f32(ssm_dt))
+    return (ssm_a, q, k, v, g, beta, raw_a, raw_b, ssm_dt)
 
 
 def make_case(name: str, lengths, H_k: int, H_v: int, d_k: int, d_v: int,
               dtype: str, seed: int, decay: str = "strong",
               beta_mode: str = "random", s0_std: float = 0.02,
               n_slots: Optional[int] = None, scatter_slots: bool = False,
-              a_lo: float = 1.0, a_hi: float = 16.0) -> Case:
-    """Generic generator. s0_std == 0 gives zero initial states (slot_in = -1)."""
+              a_lo: float = 1.0, a_hi: float = 16.0, final_gates=None,
+              gate_bias: bool = False) -> Case:
+    """Generic generator. s0_std == 0 gives zero initial states (slot_in = -1).
+    final_gates: see the module docstring (None leaves g and beta unset)."""
     lengths = [int(x) for x in lengths]
     N = len(lengths)
     T = int(sum(lengths))
     rng = np.random.default_rng(seed)
     ssm_a, q, k, v, g, beta, raw_a, raw_b, ssm_dt = _draw(
-        rng, T, H_k, H_v, d_k, d_v, dtype, decay, beta_mode, a_lo, a_hi)
+        rng, T, H_k, H_v, d_k, d_v, dtype, decay, beta_mode, a_lo, a_hi, final_gates, gate_bias)
     if n_slots is None:
         n_slots = N
     if s0_std > 0:
@@ -162,28 +173,32 @@ def make_case(name: str, lengths, H_k: int, H_v: int, d_k: int, d_v: int,
 # The five named workloads (seed = workload index) and the stress sets.
 # ---------------------------------------------------------------------------
 
-def config0() -> Case:
+def config0(final_gates=None) -> Case:
     """Tiny fp32 case: 1 sequence, T=128, H_k=H_v=2, d=32, zero initial state."""
-    return make_case("tiny_f32_T128", [128], 2, 2, 32, 32, "f32", seed=0, s0_std=0.0)
+    return make_case("tiny_f32_T128", [128], 2, 2, 32, 32, "f32", seed=0, s0_std=0.0,
+                     final_gates=final_gates)
 
 
-def config1(T: int = 4096) -> Case:
+def config1(T: int = 4096, final_gates=None) -> Case:
     """Single-layer prefill: 1 sequence, T=4096, Qwen3-Next heads, bf16."""
-    return make_case(f"prefill_T{T}", [T], dtype="bf16", seed=1, **QWEN3_NEXT_HEADS)
+    return make_case(f"prefill_T{T}", [T], dtype="bf16", seed=1, final_gates=final_gates,
+                     **QWEN3_NEXT_HEADS)
 
 
 CONFIG3_LENGTHS = [17, 64, 65, 300, 512, 1023, 2048, 8192]
 
 
-def config3() -> Case:
+def config3(final_gates=None) -> Case:
     """Mixed varlen batch: 8 sequences, scattered slots in a 64-slot pool."""
     return make_case("varlen8_T12221", CONFIG3_LENGTHS, dtype="bf16", seed=3,
-                     n_slots=64, scatter_slots=True, **QWEN3_NEXT_HEADS)
+                     n_slots=64, scatter_slots=True, final_gates=final_gates,
+                     **QWEN3_NEXT_HEADS)
 
 
-def config4(T: int = 65536) -> Case:
+def config4(T: int = 65536, final_gates=None) -> Case:
     """Long context: 1 sequence of 65536 tokens (fed as 128 ubatches of 512)."""
-    return make_case(f"stream_T{T}", [T], dtype="bf16", seed=4, **QWEN3_NEXT_HEADS)
+    return make_case(f"stream_T{T}", [T], dtype="bf16", seed=4, final_gates=final_gates,
+                     **QWEN3_NEXT_HEADS)
 
 
 @dataclasses.dataclass
@@ -214,10 +229,12 @@ def make_decode(name: str, n_seqs: int, n_steps: int, H_k: int, H_v: int,
                 d_k: int, d_v: int, dtype: str, seed: int,
                 decay: str = "strong", beta_mode: str = "random",
                 s0_std: float = 0.02, n_slots: Optional[int] = None,
-                scatter_slots: bool = False) -> DecodeCase:
+                scatter_slots: bool = False, final_gates=None,
+                gate_bias: bool = False) -> DecodeCase:
     rng = np.random.default_rng(seed)
     ssm_a, q, k, v, g, beta, raw_a, raw_b, ssm_dt = _draw(
-        rng, n_steps * n_seqs, H_k, H_v, d_k, d_v, dtype, decay, beta_mode, 1.0, 16.0)
+        rng, n_steps * n_seqs, H_k, H_v, d_k, d_v, dtype, decay, beta_mode, 1.0, 16.0,
+        final_gates, gate_bias)
     if n_slots is None:
         n_slots = n_seqs
     pool = (rng.standard_normal((n_slots, H_v, d_k, d_v)) * s0_std).astype(np.float32)
@@ -228,15 +245,16 @@ def make_decode(name: str, n_seqs: int, n_steps: int, H_k: int, H_v: int,
     S, N = n_steps, n_seqs
     return DecodeCase(name, H_k, H_v, d_k, d_v, dtype, N, S,
                       q.reshape(S, N, H_k, d_k), k.reshape(S, N, H_k, d_k),
-                      v.reshape(S, N, H_v, d_v), g.reshape(S, N, H_v),
-                      beta.reshape(S, N, H_v), pool, slots, ssm_a,
+                      v.reshape(S, N, H_v, d_v),
+                      None if g is None else g.reshape(S, N, H_v),
+                      None if beta is None else beta.reshape(S, N, H_v), pool, slots, ssm_a,
                       raw_a.reshape(S, N, H_v), raw_b.reshape(S, N, H_v), ssm_dt)
 
 
-def config2(n_steps: int = 128) -> DecodeCase:
+def config2(n_steps: int = 128, final_gates=None) -> DecodeCase:
     """Decode: 64 sequences x 128 steps, Qwen3-Next heads, bf16, 128 MiB pool."""
     return make_decode("decode64x128", 64, n_steps, dtype="bf16", seed=2,
-                       **QWEN3_NEXT_HEADS)
+                       final_gates=final_gates, **QWEN3_NEXT_HEADS)
 
 
 def decode_as_sequences(dc: DecodeCase):

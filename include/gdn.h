@@ -43,7 +43,8 @@
  *                  [cu_seqlens[i], cu_seqlens[i+1]); cu_seqlens[0] == 0,
  *                  non-decreasing, cu_seqlens[n_seqs] == total_tokens
  *       slot_in, slot_out [n_seqs] int32 device; slot_in[i] < 0 means the
- *                  sequence starts from the zero state
+ *                  sequence starts from the zero state, slot_out[i] < 0
+ *                  that its final state is not stored
  *   - The caller owns every buffer.  No call allocates, frees, synchronises
  *     or reads device memory on the host.  Work is enqueued on `stream`
  *     (a hipStream_t; NULL is the default stream) and completes
@@ -62,15 +63,16 @@
  *     clamp sequence bounds into [0, total_tokens], so bad cu_seqlens give
  *     wrong results, not out-of-range accesses; a slot index outside the
  *     pool addresses memory outside it.  With the environment variable
- *     GDN_CHECK=1 every call first
- *     validates them on the device (one small kernel), waits for the
- *     result (a stream synchronisation: a debugging aid, not for timed or
- *     captured code) and returns GDN_ERR_INVALID_ARG, enqueueing nothing
- *     else, if one fails (checked calls made at the same time on one device
- *     share the word the result is read from: make them one at a time).
- *     Slot indices are checked for distinctness and
- *     aliasing only (the pool size is not an argument), and only for up to
- *     16384 sequences per call.  The library never aborts or throws.
+ *     GDN_CHECK=1 every call first validates them on the device (one small
+ *     kernel), waits for the result (a stream synchronisation: a debugging
+ *     aid, not for timed or captured code) and returns GDN_ERR_INVALID_ARG,
+ *     enqueueing nothing else, if one fails.  Each checked call reads its
+ *     verdict from a word of its own (64 words per device, taken in turn:
+ *     up to 64 checked calls may be in flight on one device at once, from
+ *     any number of host threads).  Slot indices are checked for
+ *     distinctness and aliasing (for up to 16384 sequences per call) and,
+ *     when dims->n_slots > 0, against the pool size.  The library never
+ *     aborts or throws.
  *   - Thread safety: calls may be made from several host threads; the error
  *     message is thread-local.
  *   - Graph capture: a call enqueues kernels only (no allocation, memset or
@@ -87,7 +89,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 4
+#define GDN_VERSION 5
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -183,6 +185,11 @@ typedef struct gdn_dims {
                              (dims->dtype), 16-byte aligned                */
     const float *norm_w;  /* [d_v] device fp32 RMS-norm weight (with z),
                              16-byte aligned                                */
+    int32_t n_slots;      /* slots in the state pools (0: not given).  With
+                             n_slots > 0, GDN_CHECK=1 also rejects a call
+                             with slot_in[i] >= n_slots or
+                             slot_out[i] >= n_slots; the kernels never read
+                             it                                             */
 } gdn_dims;
 
 /* Library version (GDN_VERSION). */
@@ -201,8 +208,7 @@ const char *gdn_last_error(void);
  * device work.  The workspace holds the chunk table and the per-chunk WY
  * factors (build_delta_net_chunking: k_cumdecay, the beta-weighted values and
  * the decayed q.k attention, plus q and k in matrix-core operand order)
- * between the two phases, one slot per chunk of the batch, and one
- * d_k x d_v fp32 state per (sequence, value head).
+ * between the two phases, one slot per chunk of the batch.
  */
 gdn_status gdn_prefill_workspace_size(const gdn_dims *dims, int32_t n_seqs,
                                       int64_t total_tokens, size_t *bytes);
@@ -217,7 +223,9 @@ gdn_status gdn_prefill_workspace_size(const gdn_dims *dims, int32_t n_seqs,
  * writes its factors to the same slots, so the workspace holds one range's
  * factors (about 165 MiB at Qwen3-Next heads, against 2.6 GB for all of a
  * 65 536-token call's chunks), and a sequence that crosses a range boundary
- * keeps its state in the per-sequence states in between.
+ * keeps its state in one of two H_v x d_k x d_v fp32 carry states in between
+ * (consecutive ranges use them in turn; at most one sequence crosses each
+ * boundary).
  */
 gdn_status gdn_chunked_prefill_workspace_size(const gdn_dims *dims, int32_t n_seqs,
                                               int64_t total_tokens, size_t *bytes);

@@ -17,7 +17,7 @@ import sys
 import numpy as np
 import torch
 
-import gdn_inputs as gi
+import workloads as gi
 import oracle
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert gdn.version() == 4
+    assert gdn.version() == 5
     for st in range(5):
         assert gdn.lib.gdn_status_string(st)
     assert gdn.lib.gdn_status_string(99) == b"unknown status"
@@ -60,19 +60,24 @@ def test_workspace_size_grows_with_tokens_and_is_aligned():
 
 def test_chunked_workspace_holds_one_range():
     """gdn_chunked_prefill's workspace holds the factors of one chunk range
-    (at these heads: every chunk up to 212 MiB of factors, else 64 chunks);
-    the split-phase layout holds a slot for each of the batch's at most
-    T/64 + n_seqs chunks.  The rest of the two layouts is the same."""
+    (at these heads: every chunk up to 212 MiB of factors, else 64 chunks)
+    plus, when the batch runs as several ranges, two carry states; the
+    split-phase layout holds a slot for each of the batch's at most
+    T/64 + n_seqs chunks and no carry state.  The rest of the two layouts is
+    the same."""
     d = _dims()
     slot = (32 * (16 + 16 + 1 + 32) + 16 * 32) * 1024     # one chunk's factors, all heads
+    carry = 2 * 32 * 128 * 128 * 4                        # two H_v x d_k x d_v fp32 states
     for n, T, held in ((1, 4096, 64), (1, 4160, 65), (1, 8229, 64), (1, 65536, 64),
                        (8, 12221, 64), (8, 512, 16)):
         full = gdn.workspace_size(d, n, T)
         part = gdn.chunked_workspace_size(d, n, T)
         bound = (T + 63) // 64 + n
+        chunks = (T + 63) // 64 if n == 1 else bound
         if n > 1 and bound * slot <= 212 << 20:
             held = bound                                  # one range over the bound
-        assert full - part == (bound - held) * slot, (n, T)
+        ranges = held < chunks
+        assert full - part == (bound - held) * slot - (carry if ranges else 0), (n, T)
     assert gdn.workspace_size(d, 1, 65536) > 2.7e9
     assert gdn.chunked_workspace_size(d, 1, 65536) < 0.18e9
 
@@ -93,6 +98,7 @@ def test_chunked_workspace_holds_one_range():
     (dict(z=0x1008, norm_w=0x2000), 1), (dict(z=0x1000, norm_w=0x2004), 1),
     # with the prologue a slot row also holds 3 * conv_dim convolution state
     (dict(d_conv=4, conv_w=0x1000, slot_stride=32 * 128 * 128), 1),
+    (dict(n_slots=-1), 1),
 ])
 def test_bad_dims_rejected(kw, status):
     n = ctypes.c_size_t(0)
@@ -236,3 +242,23 @@ def test_prologue_argument_rules():
     st = gdn.lib.gdn_recurrent_multi(ctypes.byref(d), None, None, None, P(FAKE), P(FAKE),
                                      P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 4, 16, None)
     assert st == 1
+
+
+def test_dims_layout_matches_the_header(tmp_path):
+    """The binding's ctypes structure has the C struct's size and field
+    offsets (compiled from include/gdn.h with the host compiler)."""
+    import subprocess
+    fields = [f for f, _ in gdn.Dims._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "gdn.h"\nint main(void){\n'
+                   + 'printf("%zu\\n", sizeof(gdn_dims));\n'
+                   + "".join(f'printf("%zu\\n", offsetof(gdn_dims, {f}));\n' for f in fields)
+                   + "return 0;}\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(gdn.Dims)
+    for f, off in zip(fields, got[1:]):
+        assert getattr(gdn.Dims, f).offset == off, f

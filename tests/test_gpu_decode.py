@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 import torch
 
-import gdn_inputs as gi
+import workloads as gi
 from gpu_harness import compare_decode, oracle_decode, run_decode, say
 
 pytestmark = pytest.mark.gpu

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-import gdn_inputs as gi
+import workloads as gi
 from gpu_harness import (TOL, compare_prefill, dev_case, gpu_decode_multi, gpu_prefill,
                          oracle_case, rel_err, say)
 

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-import gdn_inputs as gi
+import workloads as gi
 from gpu_harness import dev_case
 
 pytestmark = pytest.mark.gpu

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 import torch
 
-import gdn_inputs as gi
+import workloads as gi
 from gpu_harness import (TOL, compare_layer, dev_layer, gpu_layer_multi, gpu_layer_prefill,
                          layer_pool, oracle_layer, rel_err, say, split_pool)
 

@@ -12,7 +12,7 @@ import itertools
 import pytest
 import torch
 
-import gdn_inputs as gi
+import workloads as gi
 from gpu_harness import (compare_decode, compare_layer, compare_prefill, gpu_decode_multi,
                          gpu_layer_prefill, gpu_prefill, oracle_case, oracle_decode, oracle_layer,
                          run_decode, say)

@@ -5,6 +5,8 @@ import numpy as np
 import torch
 
 import gdn_inputs as gi
+import oracle
+import workloads
 
 
 def _h(*arrs):
@@ -32,7 +34,7 @@ def test_generators_are_deterministic():
 
 
 def test_recipe_shapes_and_ranges():
-    c = gi.config0()
+    c = workloads.config0()
     assert c.q.shape == (128, 2, 32) and c.v.shape == (128, 2, 32)
     assert np.all(c.g <= 0) and np.all((c.beta > 0) & (c.beta < 1))
     assert not c.pool.any() and np.all(c.slot_in == -1)
@@ -42,16 +44,19 @@ def test_recipe_shapes_and_ranges():
     # bf16 storage: low 16 bits are zero
     assert not (b.q.view(np.uint32) & 0xFFFF).any()
     assert not (b.v.view(np.uint32) & 0xFFFF).any()
-    # strong decay: ssm_a = -U(1, 16); gate bias U(-1, 1); raw projections per token-head
+    # strong decay: ssm_a = -U(1, 16); no gate bias by default; raw projections per token-head
     assert np.all(b.ssm_a <= -1) and np.all(b.ssm_a >= -16)
-    assert np.all(np.abs(b.ssm_dt) <= 1)
+    assert not b.ssm_dt.any()
     assert b.raw_a.shape == (70, 4) and b.raw_b.shape == (70, 4)
+    assert b.g is None and b.beta is None      # the generator evaluates no activation
+    bb = gi.make_case("b", [70], 2, 4, 32, 32, "bf16", seed=3, gate_bias=True)
+    assert np.all(np.abs(bb.ssm_dt) <= 1) and bb.ssm_dt.any()
     w = gi.make_case("w", [70], 2, 4, 32, 32, "bf16", seed=3, decay="weak")
     assert np.all(w.ssm_a <= -0.001) and np.all(w.ssm_a >= -0.01)
 
 
 def test_decode_repacking():
-    dc = gi.make_decode("d", 3, 5, 1, 2, 8, 8, "f32", seed=1)
+    dc = workloads.make_decode("d", 3, 5, 1, 2, 8, 8, "f32", seed=1)
     q, k, v, g, beta, cu = gi.decode_as_sequences(dc)
     assert list(cu) == [0, 5, 10, 15]
     assert np.array_equal(q[5 + 2], dc.q[2, 1]) and np.array_equal(v[10 + 4], dc.v[4, 2])
@@ -76,3 +81,28 @@ def test_layer_inputs_recipe():
     c2 = gi.make_case("x", [33], 2, 4, 32, 64, "bf16", seed=9)
     assert np.array_equal(c1.q, c2.q)
     assert abs(float(np.std(a.qkv)) - 1.0) < 0.05
+
+
+def test_workload_gate_recipe():
+    """The workloads' gates: beta = sigmoid(N(0,1)), g = -exp(A_log) softplus(N(0,1))
+    with A_log = log U(1,16): the harness applies the activations to the
+    generator's raw draws (ssm_dt = 0), and the draws have the stated laws."""
+    c = workloads.config1(T=2048)
+    assert not c.ssm_dt.any()
+    g, beta = oracle.gates(c.raw_a, c.raw_b, c.ssm_a, c.ssm_dt)
+    assert np.array_equal(c.g, g.astype(np.float32))
+    assert np.array_equal(c.beta, beta.astype(np.float32))
+    # raw draws: standard normal
+    for x in (c.raw_a, c.raw_b):
+        assert abs(float(np.mean(x))) < 0.01 and abs(float(np.std(x)) - 1.0) < 0.01
+    # E[sigmoid(N(0,1))] = 1/2; E[softplus(N(0,1))] = 0.8063...
+    assert abs(float(np.mean(c.beta)) - 0.5) < 0.01
+    sp = c.g / c.ssm_a[None, :]
+    assert abs(float(np.mean(sp)) - 0.8063) < 0.01
+    # decay rate -exp(log U(1, 16)) per head
+    assert np.all((-c.ssm_a >= 1) & (-c.ssm_a <= 16))
+    # the decode workload uses the same recipe
+    d = workloads.config2(n_steps=4)
+    g2, b2 = oracle.gates(d.raw_a.reshape(-1, 32), d.raw_b.reshape(-1, 32), d.ssm_a, d.ssm_dt)
+    assert np.array_equal(d.g.reshape(-1, 32), g2.astype(np.float32))
+    assert np.array_equal(d.beta.reshape(-1, 32), b2.astype(np.float32))
