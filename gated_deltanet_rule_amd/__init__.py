@@ -67,6 +67,8 @@ def _load() -> ctypes.CDLL:
     lib.gdn_chunked_prefill_workspace_size.restype = ctypes.c_int
     lib.gdn_chunked_prefill.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, I32, I64, P, SZ, P]
     lib.gdn_chunked_prefill.restype = ctypes.c_int
+    lib.gdn_chunked_prefill_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, I32, I64, P]
+    lib.gdn_chunked_prefill_noalloc.restype = ctypes.c_int
     lib.gdn_recurrent_step.argtypes = [D, P, P, P, P, P, P, P, P, P, P, I32, P]
     lib.gdn_recurrent_step.restype = ctypes.c_int
     lib.gdn_prefill_prepare.argtypes = [D, P, P, P, P, P, P, I32, I64, P, SZ, P]
@@ -82,7 +84,7 @@ lib = _load()
 
 EXPORTED = ["gdn_version", "gdn_status_string", "gdn_last_error",
             "gdn_prefill_workspace_size", "gdn_chunked_prefill_workspace_size",
-            "gdn_chunked_prefill", "gdn_prefill_prepare",
+            "gdn_chunked_prefill", "gdn_chunked_prefill_noalloc", "gdn_prefill_prepare",
             "gdn_prefill_scan", "gdn_recurrent_step", "gdn_recurrent_multi"]
 
 
@@ -250,6 +252,29 @@ def prefill(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in, slo
                                    _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
                                    _ptr(cu_seqlens), _ptr(slot_in), _ptr(slot_out), n_seqs, T,
                                    _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def prefill_noalloc(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in, slot_out, *,
+                    scale: float = 0.0, eps: float = 1e-6, stream=None, gates=None, conv=None,
+                    z=None, norm_w=None) -> None:
+    """gdn_chunked_prefill_noalloc on torch tensors: prefill() without a
+    workspace (the library's own 64 MiB device scratch; nothing is allocated,
+    here or in the library)."""
+    dev = q.device
+    _need_qkv(q, k, v, conv)
+    _need(out, "out", None, dev)
+    for t, name in ((g, "g"), (beta, "beta"), (state_out, "state_out")):
+        _need(t, name, torch.float32, dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, dev)
+    for t, name in ((cu_seqlens, "cu_seqlens"), (slot_in, "slot_in"), (slot_out, "slot_out")):
+        _need(t, name, torch.int32, dev)
+    dims = _dims_from(q, v, out, scale, eps, state_out, gates, conv, z, norm_w)
+    dims.n_slots = _n_slots(state_in, state_out)
+    _check(lib.gdn_chunked_prefill_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                           _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
+                                           _ptr(cu_seqlens), _ptr(slot_in), _ptr(slot_out),
+                                           slot_out.shape[0], q.shape[0], _stream(stream)))
 
 
 def _prefill_common(q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in,

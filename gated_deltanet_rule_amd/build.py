@@ -24,7 +24,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["gdn_api.cpp", "gdn_check.hip", "gdn_decode.hip", "gdn_layer.hip", "gdn_prefill.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_check.hip", "gdn_decode.hip", "gdn_layer.hip", "gdn_prefill.hip",
+           "gdn_scratch.hip"]
 # machine-peak microbenchmarks for the benchmark's roofline: a library of their own
 PEAK_SOURCES = ["gdn_peak.hip"]
 PEAK_LIB = os.path.join(PKG, "libgdnpeak.so")

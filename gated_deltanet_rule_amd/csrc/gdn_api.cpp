@@ -215,6 +215,40 @@ gdn_status check_scan_inputs(const float *state_in, float *state_out, void *out,
     return GDN_OK;
 }
 
+// The chunked prefill of a validated call: device check, then `per`-chunk
+// ranges (preparation, scan) over the workspace, then the convolution state.
+gdn_status run_chunked(const gdn::Problem &p, const void *qkv, const void *q, const void *k,
+                       const void *v, const float *g, const float *beta, const float *state_in,
+                       float *state_out, void *out, const int32_t *cu_seqlens,
+                       const int32_t *slot_in, const int32_t *slot_out, int32_t n_seqs,
+                       int64_t total_tokens, void *workspace, int per, hipStream_t s)
+{
+    if (p.H_v > 65535) return fail(GDN_ERR_UNSUPPORTED, "H_v above 65535");
+    const int chunks = gdn::prefill_chunk_count(p, n_seqs, total_tokens);
+    const int n_seg = std::max(1, (chunks + per - 1) / per);
+    gdn::PrefillArgs a{q, k, v, g, beta, ssm_part(p, state_in), ssm_part(p, state_out), out,
+                       cu_seqlens, slot_in, slot_out, n_seqs, total_tokens, workspace,
+                       state_in, state_out, per};
+    gdn_status st = device_check(p, cu_seqlens, n_seqs, total_tokens, slot_in, slot_out, s);
+    if (st != GDN_OK) return st;
+    for (int r = 0; r < n_seg && st == GDN_OK; ++r) {
+        gdn::Segment sg;
+        sg.lo = r * per;
+        sg.hi = r + 1 == n_seg ? 0x7fffffff : (r + 1) * per;
+        sg.idx = r;
+        sg.first = r == 0;
+        sg.last = r + 1 == n_seg;
+        st = hip_status(gdn::launch_prepare(p, a, sg, s), "prepare");
+        if (st == GDN_OK) st = hip_status(gdn::launch_scan(p, a, sg, s), "scan");
+    }
+    // the convolution state is replaced only after the preparation has read it
+    if (st == GDN_OK && p.conv_w)
+        st = hip_status(gdn::launch_conv_state(p, qkv, cu_seqlens, n_seqs == 1 ? (int)total_tokens : -1,
+                                               n_seqs, total_tokens, state_in, state_out, slot_in,
+                                               slot_out, s), "convolution state");
+    return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -330,32 +364,49 @@ gdn_status gdn_chunked_prefill(const gdn_dims *dims, const void *q, const void *
     // factors to the same per chunk slots
     const int chunks = gdn::prefill_chunk_count(p, n_seqs, total_tokens);
     const int per = gdn::segment_chunks(p, chunks);
-    const int n_seg = std::max(1, (chunks + per - 1) / per);
     st = check_workspace(p, n_seqs, total_tokens, workspace, workspace_bytes, per);
     if (st != GDN_OK) return st;
-    if (p.H_v > 65535) return fail(GDN_ERR_UNSUPPORTED, "H_v above 65535");
-    gdn::PrefillArgs a{q, k, v, g, beta, ssm_part(p, state_in), ssm_part(p, state_out), out,
-                       cu_seqlens, slot_in, slot_out, n_seqs, total_tokens, workspace,
-                       state_in, state_out, per};
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    st = device_check(p, cu_seqlens, n_seqs, total_tokens, slot_in, slot_out, s);
+    return run_chunked(p, qkv, q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in,
+                       slot_out, n_seqs, total_tokens, workspace, per, static_cast<hipStream_t>(stream));
+}
+
+gdn_status gdn_chunked_prefill_noalloc(const gdn_dims *dims, const void *q, const void *k,
+                                       const void *v, const float *g, const float *beta,
+                                       const float *state_in, float *state_out, void *out,
+                                       const int32_t *cu_seqlens, const int32_t *slot_in,
+                                       const int32_t *slot_out, int32_t n_seqs,
+                                       int64_t total_tokens, void *stream)
+{
+    g_last_error[0] = 0;
+    gdn::Problem p;
+    gdn_status st = resolve(dims, &p);
+    const void *qkv = q;
+    if (st == GDN_OK) st = mixed_rows(p, q, k, v);
+    if (st == GDN_OK) st = check_counts(n_seqs, total_tokens);
+    if (st == GDN_OK) st = check_prepare_inputs(q, k, v, g, beta, cu_seqlens);
+    if (st == GDN_OK) st = check_scan_inputs(state_in, state_out, out, slot_in, slot_out);
     if (st != GDN_OK) return st;
-    for (int k = 0; k < n_seg && st == GDN_OK; ++k) {
-        gdn::Segment sg;
-        sg.lo = k * per;
-        sg.hi = k + 1 == n_seg ? 0x7fffffff : (k + 1) * per;
-        sg.idx = k;
-        sg.first = k == 0;
-        sg.last = k + 1 == n_seg;
-        st = hip_status(gdn::launch_prepare(p, a, sg, s), "prepare");
-        if (st == GDN_OK) st = hip_status(gdn::launch_scan(p, a, sg, s), "scan");
+    void *ws = nullptr;
+    size_t cap = 0;
+    st = hip_status(gdn::scratch_buffer(&ws, &cap), "scratch lookup");
+    if (st != GDN_OK) return st;
+    // the longest chunk range (at most the one gdn_chunked_prefill would
+    // use) whose workspace fits the scratch: the size is monotone in it
+    const int chunks = gdn::prefill_chunk_count(p, n_seqs, total_tokens);
+    int lo = 1, hi = gdn::segment_chunks(p, chunks);
+    const size_t need1 = gdn::prefill_workspace_bytes(p, n_seqs, total_tokens, lo);
+    if (need1 > cap)
+        return fail(GDN_ERR_WORKSPACE,
+                    "gdn_chunked_prefill_noalloc: this batch needs %zu bytes of scratch even in ranges "
+                    "of one chunk; the allocation-free entry point holds %zu (use gdn_chunked_prefill)",
+                    need1, cap);
+    while (lo < hi) {
+        const int mid = lo + (hi - lo + 1) / 2;
+        if (gdn::prefill_workspace_bytes(p, n_seqs, total_tokens, mid) <= cap) lo = mid;
+        else hi = mid - 1;
     }
-    // the convolution state is replaced only after the preparation has read it
-    if (st == GDN_OK && p.conv_w)
-        st = hip_status(gdn::launch_conv_state(p, qkv, cu_seqlens, n_seqs == 1 ? (int)total_tokens : -1,
-                                               n_seqs, total_tokens, state_in, state_out, slot_in,
-                                               slot_out, s), "convolution state");
-    return st;
+    return run_chunked(p, qkv, q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in,
+                       slot_out, n_seqs, total_tokens, ws, lo, static_cast<hipStream_t>(stream));
 }
 
 gdn_status gdn_recurrent_step(const gdn_dims *dims, const void *q, const void *k,

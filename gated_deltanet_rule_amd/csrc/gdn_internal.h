@@ -131,6 +131,12 @@ hipError_t launch_prepare(const Problem &p, const PrefillArgs &a, const Segment 
 // the gated RMSNorm epilogue when p.z is set)
 hipError_t launch_scan(const Problem &p, const PrefillArgs &a, const Segment &sg, hipStream_t s);
 
+// Allocation-free prefill (gdn_scratch.hip): the calling thread's current
+// device's copy of a file-scope device array of kScratchBytes, 256-byte
+// aligned, shared by every call on that device.
+constexpr size_t kScratchBytes = 64u << 20;
+hipError_t scratch_buffer(void **ptr, size_t *bytes);
+
 // Check mode (GDN_CHECK=1, gdn_check.hip): validates cu_seqlens (null: one
 // token per sequence) and the slot lists of a call on the device, then
 // synchronises the stream and returns its findings, a set of these bits.

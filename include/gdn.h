@@ -263,6 +263,31 @@ gdn_status gdn_chunked_prefill(const gdn_dims *dims,
                                void *stream);
 
 /*
+ * gdn_chunked_prefill without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It allocates nothing: its workspace is a
+ * 64 MiB device array inside the library (each GPU the library runs on holds
+ * its own copy until the process ends), and a batch whose factors outgrow it
+ * runs as more, shorter chunk ranges (results are bitwise those of
+ * gdn_chunked_prefill).  A batch that needs more than 64 MiB even in ranges
+ * of one chunk (for example many thousands of sequences, or the epilogue
+ * with a bf16 out, which stages 4*T*H_v*d_v bytes of fp32 output) is
+ * rejected with GDN_ERR_WORKSPACE before anything is enqueued.  Every call
+ * on one GPU uses that GPU's array, which keeps the last call's contents (no
+ * call relies on them): calls that overlap on one GPU, from several streams
+ * or host threads, race on it and must be ordered by the caller.  Other
+ * arguments, layouts and errors as for gdn_chunked_prefill.
+ */
+gdn_status gdn_chunked_prefill_noalloc(const gdn_dims *dims,
+                                       const void *q, const void *k, const void *v,
+                                       const float *g, const float *beta,
+                                       const float *state_in, float *state_out,
+                                       void *out, const int32_t *cu_seqlens,
+                                       const int32_t *slot_in, const int32_t *slot_out,
+                                       int32_t n_seqs, int64_t total_tokens,
+                                       void *stream);
+
+/*
  * The two phases of gdn_chunked_prefill, for callers that schedule them
  * separately (for example, preparing ubatch n+1 on a second stream while the
  * scan of ubatch n runs; the scan is sequential over a sequence's chunks,
