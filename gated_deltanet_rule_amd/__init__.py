@@ -50,6 +50,16 @@ class Dims(ctypes.Structure):
                 ("n_slots", ctypes.c_int32)]
 
 
+class DebugChunk(ctypes.Structure):
+    """gdn_debug_chunk: one chunk's intermediates recorded under GDN_DEBUG_DUMP."""
+    _fields_ = [("token", ctypes.c_int32), ("head", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("t0", ctypes.c_int32), ("len", ctypes.c_int32), ("d_k", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("prepared", ctypes.c_int32), ("scanned", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("G", ctypes.c_double * 64),
+                ("T", ctypes.c_float * (64 * 64)), ("W", ctypes.c_float * (64 * 128)),
+                ("U", ctypes.c_float * (64 * 128))]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libgdn.so not built at {LIB_PATH}; run "
@@ -77,6 +87,8 @@ def _load() -> ctypes.CDLL:
     lib.gdn_prefill_scan.restype = ctypes.c_int
     lib.gdn_recurrent_multi.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, I32, I64, P]
     lib.gdn_recurrent_multi.restype = ctypes.c_int
+    lib.gdn_debug_dump.argtypes = [ctypes.POINTER(DebugChunk)]
+    lib.gdn_debug_dump.restype = ctypes.c_int
     return lib
 
 
@@ -85,11 +97,31 @@ lib = _load()
 EXPORTED = ["gdn_version", "gdn_status_string", "gdn_last_error",
             "gdn_prefill_workspace_size", "gdn_chunked_prefill_workspace_size",
             "gdn_chunked_prefill", "gdn_chunked_prefill_noalloc", "gdn_prefill_prepare",
-            "gdn_prefill_scan", "gdn_recurrent_step", "gdn_recurrent_multi"]
+            "gdn_prefill_scan", "gdn_recurrent_step", "gdn_recurrent_multi", "gdn_debug_dump"]
 
 
 def version() -> int:
     return lib.gdn_version()
+
+
+def debug_dump() -> dict:
+    """The last chunk recorded under GDN_DEBUG_DUMP=<token>,<head>: the
+    header fields, and as float64 arrays the valid parts G[len], T[len][len],
+    W[len][d_k] and U[len][d_v] (absent when not written).  Raises GdnError
+    when no prefill has run with the variable set."""
+    import numpy as np
+    rec = DebugChunk()
+    _check(lib.gdn_debug_dump(ctypes.byref(rec)))
+    out = {f: getattr(rec, f) for f in ("token", "head", "chunk", "t0", "len", "d_k", "d_v",
+                                        "prepared", "scanned")}
+    n = rec.len
+    if rec.prepared:
+        out["G"] = np.ctypeslib.as_array(rec.G)[:n].astype(np.float64)
+        out["T"] = np.ctypeslib.as_array(rec.T).reshape(64, 64)[:n, :n].astype(np.float64)
+        out["W"] = np.ctypeslib.as_array(rec.W).reshape(64, 128)[:n, :rec.d_k].astype(np.float64)
+    if rec.scanned:
+        out["U"] = np.ctypeslib.as_array(rec.U).reshape(64, 128)[:n, :rec.d_v].astype(np.float64)
+    return out
 
 
 def _check(status: int):

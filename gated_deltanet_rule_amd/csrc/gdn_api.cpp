@@ -1,7 +1,9 @@
 // gdn_api.cpp -- the libgdn C ABI: argument validation, workspace sizing and
 // dispatch to the kernel launchers.  No allocation, no synchronisation and no
-// host reads of device memory happen here.
+// host reads of device memory happen here, except in the two debugging modes
+// (GDN_CHECK, GDN_DEBUG_DUMP).
 #include <algorithm>
+#include <mutex>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -128,6 +130,77 @@ bool check_mode()
     return e && e[0] == '1' && e[1] == 0;
 }
 
+// GDN_DEBUG_DUMP=<token>,<head>: the prefill records one chunk's
+// intermediates (gdn_debug_dump).  The device record is allocated once per
+// device and kept until the process ends; the last host copy is shared by
+// every thread.
+constexpr int kMaxDevices = 64;
+std::mutex g_dbg_mu;
+gdn_debug_chunk *g_dbg_dev[kMaxDevices] = {};
+gdn_debug_chunk g_dbg_last;
+bool g_dbg_have = false;
+
+bool debug_target(int *token, int *head)
+{
+    const char *e = getenv("GDN_DEBUG_DUMP");
+    if (!e || !*e) return false;
+    char extra;
+    return sscanf(e, "%d,%d%c", token, head, &extra) == 2 && *token >= 0 && *head >= 0;
+}
+
+// Attach the device record to `p` when the variable is set; `clear` marks it
+// unwritten (the call that runs the preparation).
+gdn_status debug_setup(gdn::Problem &p, hipStream_t s, bool clear)
+{
+    int token, head;
+    if (!debug_target(&token, &head)) return GDN_OK;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "GDN_DEBUG_DUMP: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(GDN_ERR_UNSUPPORTED, "GDN_DEBUG_DUMP: device %d", dev);
+    {
+        std::lock_guard<std::mutex> lk(g_dbg_mu);
+        if (!g_dbg_dev[dev]) {
+            e = hipMalloc(reinterpret_cast<void **>(&g_dbg_dev[dev]), sizeof(gdn_debug_chunk));
+            if (e != hipSuccess) {
+                g_dbg_dev[dev] = nullptr;
+                return fail(GDN_ERR_HIP, "GDN_DEBUG_DUMP: %s", hipGetErrorString(e));
+            }
+        }
+    }
+    p.dbg = g_dbg_dev[dev];
+    p.dbg_token = token;
+    p.dbg_head = head;
+    // all-ones: chunk -1 and the written flags -1 until a kernel sets them
+    if (clear) e = hipMemsetAsync(p.dbg, 0xff, sizeof(gdn_debug_chunk), s);
+    return e == hipSuccess ? GDN_OK : fail(GDN_ERR_HIP, "GDN_DEBUG_DUMP: %s", hipGetErrorString(e));
+}
+
+// After the scan: wait for the stream and keep a host copy of the record.
+gdn_status debug_collect(const gdn::Problem &p, hipStream_t s)
+{
+    if (!p.dbg) return GDN_OK;
+    gdn_debug_chunk rec;
+    hipError_t e = hipMemcpyAsync(&rec, p.dbg, sizeof rec, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "GDN_DEBUG_DUMP: %s", hipGetErrorString(e));
+    rec.token = p.dbg_token;
+    rec.head = p.dbg_head;
+    rec.d_k = p.d_k;
+    rec.d_v = p.d_v;
+    rec.reserved = 0;
+    if (rec.prepared != 1) {
+        rec.prepared = 0;
+        rec.chunk = -1;
+        rec.t0 = rec.len = 0;
+    }
+    if (rec.scanned != 1) rec.scanned = 0;
+    std::lock_guard<std::mutex> lk(g_dbg_mu);
+    g_dbg_last = rec;
+    g_dbg_have = true;
+    return GDN_OK;
+}
+
 gdn_status device_check(const gdn::Problem &p, const int32_t *cu, int32_t n, int64_t T,
                         const int32_t *slot_in, const int32_t *slot_out, hipStream_t s)
 {
@@ -217,11 +290,12 @@ gdn_status check_scan_inputs(const float *state_in, float *state_out, void *out,
 
 // The chunked prefill of a validated call: device check, then `per`-chunk
 // ranges (preparation, scan) over the workspace, then the convolution state.
-gdn_status run_chunked(const gdn::Problem &p, const void *qkv, const void *q, const void *k,
+gdn_status run_chunked(gdn::Problem p, const void *qkv, const void *q, const void *k,
                        const void *v, const float *g, const float *beta, const float *state_in,
                        float *state_out, void *out, const int32_t *cu_seqlens,
                        const int32_t *slot_in, const int32_t *slot_out, int32_t n_seqs,
-                       int64_t total_tokens, void *workspace, int per, hipStream_t s)
+                       int64_t total_tokens, void *workspace, int per, hipStream_t s,
+                       bool debug = true)
 {
     if (p.H_v > 65535) return fail(GDN_ERR_UNSUPPORTED, "H_v above 65535");
     const int chunks = gdn::prefill_chunk_count(p, n_seqs, total_tokens);
@@ -230,6 +304,7 @@ gdn_status run_chunked(const gdn::Problem &p, const void *qkv, const void *q, co
                        cu_seqlens, slot_in, slot_out, n_seqs, total_tokens, workspace,
                        state_in, state_out, per};
     gdn_status st = device_check(p, cu_seqlens, n_seqs, total_tokens, slot_in, slot_out, s);
+    if (st == GDN_OK && debug) st = debug_setup(p, s, true);
     if (st != GDN_OK) return st;
     for (int r = 0; r < n_seg && st == GDN_OK; ++r) {
         gdn::Segment sg;
@@ -246,6 +321,7 @@ gdn_status run_chunked(const gdn::Problem &p, const void *qkv, const void *q, co
         st = hip_status(gdn::launch_conv_state(p, qkv, cu_seqlens, n_seqs == 1 ? (int)total_tokens : -1,
                                                n_seqs, total_tokens, state_in, state_out, slot_in,
                                                slot_out, s), "convolution state");
+    if (st == GDN_OK) st = debug_collect(p, s);
     return st;
 }
 
@@ -254,6 +330,16 @@ gdn_status run_chunked(const gdn::Problem &p, const void *qkv, const void *q, co
 extern "C" {
 
 int gdn_version(void) { return GDN_VERSION; }
+
+gdn_status gdn_debug_dump(gdn_debug_chunk *out)
+{
+    g_last_error[0] = 0;
+    if (!out) return fail(GDN_ERR_INVALID_ARG, "gdn_debug_dump: out is NULL");
+    std::lock_guard<std::mutex> lk(g_dbg_mu);
+    if (!g_dbg_have) return fail(GDN_ERR_INVALID_ARG, "gdn_debug_dump: no prefill has run with GDN_DEBUG_DUMP set");
+    *out = g_dbg_last;
+    return GDN_OK;
+}
 
 const char *gdn_status_string(int status)
 {
@@ -314,6 +400,7 @@ gdn_status gdn_prefill_prepare(const gdn_dims *dims, const void *q, const void *
     if (st == GDN_OK) st = check_workspace(p, n_seqs, total_tokens, workspace, workspace_bytes);
     if (st != GDN_OK) return st;
     st = device_check(p, cu_seqlens, n_seqs, total_tokens, nullptr, nullptr, static_cast<hipStream_t>(stream));
+    if (st == GDN_OK) st = debug_setup(p, static_cast<hipStream_t>(stream), true);
     if (st != GDN_OK) return st;
     gdn::PrefillArgs a{q, k, v, g, beta, nullptr, nullptr, nullptr, cu_seqlens, nullptr,
                        nullptr, n_seqs, total_tokens, workspace, nullptr, nullptr};
@@ -339,8 +426,11 @@ gdn_status gdn_prefill_scan(const gdn_dims *dims, const float *state_in, float *
                        slot_out, n_seqs, total_tokens, const_cast<void *>(workspace), nullptr, nullptr};
     hipStream_t s = static_cast<hipStream_t>(stream);
     st = device_check(p, nullptr, n_seqs, n_seqs, slot_in, slot_out, s);
+    if (st == GDN_OK) st = debug_setup(p, s, false);
     if (st != GDN_OK) return st;
-    return hip_status(gdn::launch_scan(p, a, gdn::Segment{}, s), "scan");
+    st = hip_status(gdn::launch_scan(p, a, gdn::Segment{}, s), "scan");
+    if (st == GDN_OK) st = debug_collect(p, s);
+    return st;
 }
 
 gdn_status gdn_chunked_prefill(const gdn_dims *dims, const void *q, const void *k,
@@ -406,7 +496,7 @@ gdn_status gdn_chunked_prefill_noalloc(const gdn_dims *dims, const void *q, cons
         else hi = mid - 1;
     }
     return run_chunked(p, qkv, q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in,
-                       slot_out, n_seqs, total_tokens, ws, lo, static_cast<hipStream_t>(stream));
+                       slot_out, n_seqs, total_tokens, ws, lo, static_cast<hipStream_t>(stream), false);
 }
 
 gdn_status gdn_recurrent_step(const gdn_dims *dims, const void *q, const void *k,

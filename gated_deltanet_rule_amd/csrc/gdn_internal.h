@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct gdn_debug_chunk;   // include/gdn.h
+
 namespace gdn {
 
 // Validated, fully resolved problem description handed to the launchers.
@@ -31,6 +33,10 @@ struct Problem {
     const float *norm_w;
     // slots in the state pools (0: unknown); read only by check mode
     int n_slots;
+    // debug record (GDN_DEBUG_DUMP): null when off, else the device record of
+    // the chunk holding packed token dbg_token, for value head dbg_head
+    gdn_debug_chunk *dbg = nullptr;
+    int dbg_token = -1, dbg_head = -1;
 };
 
 // Taps of the fused convolution prologue.

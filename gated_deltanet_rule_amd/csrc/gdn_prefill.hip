@@ -45,6 +45,7 @@
 // g = 0 and zero norms, which makes them the identity on the state.
 #include <atomic>
 
+#include "../../include/gdn.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
@@ -379,6 +380,10 @@ struct PrepParams {
     // per value head)
     int head_split;
     int chunk_base;    // blockIdx.x = 0 is this chunk of the batch; its factors go to slot 0
+    // debug record (null: off): G, T and W of the chunk holding packed token
+    // dbg_t, for value head dbg_h
+    gdn_debug_chunk *dbg = nullptr;
+    int dbg_t = -1, dbg_h = -1;
 };
 
 // LDS of the preparation kernel.  Rows are padded so that the row stride is
@@ -990,6 +995,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
                     store_quarter2<E>(Wf, Wlf, tt * NKD + dt / TPB, lane, dt % TPB, a4);
                 else
                     store_quarter<E>(Wf, tt * NKD + dt / TPB, lane, dt % TPB, a4);
+
             }
         }
         {
@@ -1014,6 +1020,40 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
             }
         }
         lds_sync();
+    }
+    // Debug record of the requested chunk and head (launched with one value
+    // head per workgroup, so that the head's G, T, column scalars and K are
+    // still in LDS here and nothing else is live): G, T, and W from the
+    // products of 4d again (same operands, same order).
+    if (pp.dbg && jend - jbeg == 1 && kh * ratio + jbeg == pp.dbg_h && pp.dbg_t >= t0 && pp.dbg_t < t0 + len) {
+        const int hs = jbeg % NH;
+        const double *sG = sGh + hs * C;
+        const float *sCol = sColh + hs * C;
+        for (int x = tid; x < C * C; x += 256) pp.dbg->T[x / C][x % C] = sT[(x / C) * LDA + x % C];
+        if (tid < C) pp.dbg->G[tid] = sG[tid];
+        if (tid == 0) {
+            pp.dbg->chunk = chunk;
+            pp.dbg->t0 = t0;
+            pp.dbg->len = len;
+            pp.dbg->prepared = 1;
+        }
+        const int tt = w;
+        const int nkb = (16 * tt + 15) / KB + 1;
+#pragma unroll 1
+        for (int dt = 0; dt < NMT; ++dt) {
+            floatx4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+            for (int kb = 0; kb < nkb; ++kb) {
+                Frag bh, bl;
+                SP::rm_f32(sT + (16 * tt + n) * LDA, kb * KB, qd, sCol, bh, bl);
+                const Frag a = TR::frag(sK, LDK, kb * KB, 16 * dt, lane);
+                M::mma(a4, a, bh);
+                if constexpr (NS == 2) M::mma(a4, a, bl);
+                if constexpr (SI) M::mma(a4, TR::frag(sKL, LDK, kb * KB, 16 * dt, lane), bh);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pp.dbg->W[16 * tt + n][16 * dt + 4 * qd + j] = a4[j];
+        }
     }
 }
 
@@ -1040,6 +1080,10 @@ struct ScanParams {
     // meet its writes.
     int seg_lo, seg_hi, seg_idx;
     float *carry;
+    // debug record (null: off): U of the chunk the preparation recorded, for
+    // value head dbg_h
+    gdn_debug_chunk *dbg = nullptr;
+    int dbg_h = -1;
 };
 
 template <int DK, int DV, int CT, typename E> struct ScanLds {
@@ -1211,6 +1255,9 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
         floatx4 u0 = __builtin_bit_cast(floatx4, vblk(c0)[u0f * 64 + lane]);
         floatx4 ks4 = scal4(c0, 64 + ro);
         float gn = scal1(c0, 128);
+        // debug record: the chunk whose U is recorded (-1: none here)
+        int dbg_c = -1;
+        if (sp.dbg && h == sp.dbg_h) dbg_c = __builtin_amdgcn_readfirstlane(sp.dbg->chunk);
         // Let the first chunk's operands land before the loop: the loop's
         // waits then only have to account for the loads issued inside it.
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
@@ -1234,6 +1281,12 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
             }
             const floatx4 U = u0 - (WSh + WSl);
             const floatx4 Uk = U * ks4;
+            if (c == dbg_c) {
+                const __amdgpu_buffer_rsrc_t dbg_u = raw_buffer(&sp.dbg->U[0][0], (uint32_t)sizeof(sp.dbg->U));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) buffer_store(U[j], dbg_u, (uint32_t)(((ro + j) * 128 + col0 + n) * 4));
+                if (ct == 0 && rt == 0 && lane == 0) sp.dbg->scanned = 1;
+            }
             u0 = __builtin_bit_cast(floatx4, vblk(cn)[u0f * 64 + lane]);
             ks4 = scal4(cn, 64 + ro);
             {
@@ -1456,6 +1509,9 @@ hipError_t prepare_t(const Problem &p, const PrefillArgs &a, const Segment &sg, 
                   p.rs_qk, p.rs_v, p.conv_w,
                   // without a state pool the history loads read the taps (unused)
                   a.conv_in ? a.conv_in : p.conv_w, a.slot_in, p.slot_stride, a.conv_in != nullptr, 0, sg.lo};
+    pp.dbg = p.dbg;
+    pp.dbg_t = p.dbg_token;
+    pp.dbg_h = p.dbg_head;
     const int all = single ? (int)((a.total_tokens + C - 1) / C) : w.L.max_chunks;
     const int chunks = std::min(all, sg.hi) - sg.lo;
     if (chunks <= 0) return hipSuccess;
@@ -1465,6 +1521,7 @@ hipError_t prepare_t(const Problem &p, const PrefillArgs &a, const Segment &sg, 
     const int per_cu = (sizeof(E) == 2 && !p.conv_w) ? 2 : 1;
     const int ratio = p.H_v / p.H_k;
     if (ratio > 1 && (int64_t)chunks * p.H_v <= (int64_t)per_cu * cu_count()) pp.head_split = 1;
+    if (p.dbg && ratio > 1) pp.head_split = 1;     // the debug record is written after the head loop
     const dim3 grid(chunks, pp.head_split ? p.H_v : p.H_k);
     if (p.conv_w) {
         // bf16 rows: two-term bf16 operands (SI); fp32 rows: fp32 operands
@@ -1490,6 +1547,8 @@ hipError_t scan_t(const Problem &p, const PrefillArgs &a, const Segment &sg, hip
     ScanParams sp{a.state_in, a.state_out, o, a.slot_in, a.slot_out, w.cstart, w.ent,
                   w.vblocks, w.kblocks, p.H_k, p.H_v, p.slot_stride,
                   a.n_seqs == 1 ? (int)a.total_tokens : -1, sg.lo, sg.hi, sg.idx, w.carry};
+    sp.dbg = p.dbg;
+    sp.dbg_h = p.dbg_head;
     // With several sequences, one scan workgroup per CU: two workgroups on
     // one CU contend for its vector-memory path and LDS (the varlen batch of
     // 12 221 tokens takes 0.39 instead of 0.30 ms in the scan), so the

@@ -77,7 +77,10 @@
  *     message is thread-local.
  *   - Graph capture: a call enqueues kernels only (no allocation, memset or
  *     synchronisation), so it may be captured into a HIP graph and replayed
- *     (with GDN_CHECK=1 a call synchronises and cannot be captured).
+ *     (with GDN_CHECK=1 or GDN_DEBUG_DUMP set a call synchronises and cannot
+ *     be captured).
+ *   - Debugging: GDN_DEBUG_DUMP=<token>,<head> makes the chunked prefill
+ *     record the intermediates of one chunk (see gdn_debug_dump).
  */
 #ifndef GDN_H
 #define GDN_H
@@ -89,7 +92,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 5
+#define GDN_VERSION 6
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -335,6 +338,47 @@ gdn_status gdn_recurrent_step(const gdn_dims *dims,
                               void *out, const int32_t *slot_in,
                               const int32_t *slot_out, int32_t n_seqs,
                               void *stream);
+
+/*
+ * Debug record of the chunked form: the intermediates of one 64-token chunk
+ * and one value head as the kernels computed them, for comparison with a
+ * chunked reference.  They are the quantities of build_delta_net_chunking on
+ * the page "Optimization: Qwen3 next autoregressive pass (#17996)":
+ * g_cumsum (G), the solved and unit-diagonal attn (T = (I + A)^-1 with
+ * A = strict_lower(diag(beta) k^ k^T * decay_mask)), k_cumdecay
+ * (W = T diag(beta e^G) k^) and v_new (U = T diag(beta) v - W S, S the state
+ * entering the chunk).
+ *
+ * With the environment variable GDN_DEBUG_DUMP=<token>,<head> (packed token
+ * index and value head, both >= 0), gdn_chunked_prefill and the pair
+ * gdn_prefill_prepare / gdn_prefill_scan record the chunk holding that token
+ * for that head: the preparation writes G, T and W, the scan U, into a
+ * device buffer the library allocates once per device; the call that ends
+ * the prefill (gdn_chunked_prefill, or gdn_prefill_scan) then synchronises
+ * its stream and copies the record to the host.  A call whose batch does not
+ * reach the token leaves `prepared` and `scanned` at 0.  A debugging aid:
+ * such calls allocate (once), synchronise and cannot be captured, and calls
+ * that overlap in time share the record.  gdn_chunked_prefill_noalloc
+ * ignores the variable.  Rows at or past `len` and columns at or past d_k
+ * (W) or d_v (U) are unspecified.
+ */
+typedef struct gdn_debug_chunk {
+    int32_t token, head;      /* as requested                                   */
+    int32_t chunk;            /* index of the chunk within the batch            */
+    int32_t t0, len;          /* its packed tokens [t0, t0 + len)               */
+    int32_t d_k, d_v;
+    int32_t prepared;         /* 1: G, T and W were written                     */
+    int32_t scanned;          /* 1: U was written                               */
+    int32_t reserved;
+    double G[64];             /* cumulative log-decay within the chunk          */
+    float T[64][64];          /* row-major                                      */
+    float W[64][128];         /* token rows, d_k columns                        */
+    float U[64][128];         /* token rows, d_v columns                        */
+} gdn_debug_chunk;
+
+/* Copy the last debug record into *out (host memory).  GDN_ERR_INVALID_ARG
+ * when out is NULL or no prefill has run with GDN_DEBUG_DUMP set. */
+gdn_status gdn_debug_dump(gdn_debug_chunk *out);
 
 /*
  * Several tokens per sequence in the recurrent form: the single-chunk case

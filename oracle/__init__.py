@@ -8,6 +8,9 @@ does, and shares no code with it.
   ``gdn_oracle.c``), threaded over independent (sequence, value head) chains.
 * ``chunked(...)``: the same operator in the chunked WY form of the pages'
   chunked graph, in fp64 (C), for the chunked-vs-sequential pin.
+* ``chunk_dump(...)``: the chunked form for one value head, returning the
+  intermediates (g_cumsum, T, k_cumdecay, v_new) of the chunk holding a given
+  token, for comparison with the library's debug record.
 * ``bruteforce.materialised(...)``: the whole-sequence O(T^2) materialised
   form solved with a library triangular solver (numpy/scipy).
 * ``gates(...)``: the gate activations of the layer (raw projections to the
@@ -50,6 +53,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                   ctypes.c_double, ctypes.c_double, P, ctypes.c_int32, P, P,
                   ctypes.c_int32, ctypes.c_int32]
     f.restype = ctypes.c_int
+    d = lib.gdn_oracle_chunk_dump
+    d.argtypes = [ctypes.c_int32, P, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P,
+                  ctypes.c_double, ctypes.c_double, ctypes.c_int32, ctypes.c_int64,
+                  ctypes.c_int32, P, P, P, P, P, P, P]
+    d.restype = ctypes.c_int
     return lib
 
 
@@ -142,6 +151,42 @@ def run(q, k, v, g, beta, cu_seqlens, s0=None, *, scale: Optional[float] = None,
     if rc != 0:
         raise RuntimeError(f"oracle failed with code {rc}")
     return out, s_out
+
+
+def chunk_dump(q, k, v, g, beta, cu_seqlens, s0=None, *, token: int, head: int,
+               scale: Optional[float] = None, eps: float = 1e-6, chunk: int = 64,
+               lib_path: Optional[str] = None) -> dict:
+    """The chunked form for value head ``head`` with the intermediates of the
+    chunk holding packed token ``token``: a dict with t0 and len (0 when no
+    chunk holds it), G [len], T [len, len], W [len, d_k] (k_cumdecay) and
+    U [len, d_v] (v_new), all fp64, plus that head's out and final states."""
+    q, k, v, g, beta = _f64(q), _f64(k), _f64(v), _f64(g), _f64(beta)
+    T, H_k, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    N = cu.shape[0] - 1
+    assert cu[-1] == T
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_k)
+    if s0 is not None:
+        s0 = np.ascontiguousarray(s0, dtype=np.float64)
+        assert s0.shape == (N, H_v, d_k, d_v)
+    out = np.zeros((T, H_v, d_v), np.float64)
+    s_out = np.zeros((N, H_v, d_k, d_v), np.float64)
+    G = np.zeros(chunk, np.float64)
+    Tm = np.zeros((chunk, chunk), np.float64)
+    W = np.zeros((chunk, d_k), np.float64)
+    U = np.zeros((chunk, d_v), np.float64)
+    meta = np.zeros(2, np.int64)
+    rc = _get(lib_path).gdn_oracle_chunk_dump(
+        N, _ptr(cu), H_k, H_v, d_k, d_v, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+        _ptr(beta), _ptr(s0), float(scale), float(eps), int(chunk), int(token), int(head),
+        _ptr(out), _ptr(s_out), _ptr(G), _ptr(Tm), _ptr(W), _ptr(U), _ptr(meta))
+    if rc != 0:
+        raise RuntimeError(f"oracle failed with code {rc}")
+    n = int(meta[1])
+    return {"t0": int(meta[0]), "len": n, "G": G[:n].copy(), "T": Tm[:n, :n].copy(),
+            "W": W[:n].copy(), "U": U[:n].copy(), "out": out[:, head], "s_out": s_out[:, head]}
 
 
 def recurrent(*args, **kw):

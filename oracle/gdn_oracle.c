@@ -72,6 +72,12 @@ typedef struct {
     int32_t n_heads;
     double *out, *s_out;
     int32_t chunk;          /* 0 = sequential recurrence, else chunk size */
+    /* chunk record (gdn_oracle_chunk_dump): the intermediates of the chunk
+       holding packed token dump_token for value head dump_head */
+    int64_t dump_token;     /* < 0: none */
+    int32_t dump_head;
+    double *dump_G, *dump_T, *dump_W, *dump_U;   /* C, C x C, C x d_k, C x d_v */
+    int64_t *dump_meta;     /* t0, n */
     int32_t n_threads;
     int32_t next;           /* work counter */
     pthread_mutex_t lock;
@@ -207,6 +213,17 @@ static void run_chunked(const job_t *J, int s, int h, double *S, double *wk)
                 for (int i = 0; i < dk; ++i) acc += KCD[a * dk + i] * S[i * dv + j];
                 VN[a * dv + j] = VAL[a * dv + j] - acc;
             }
+        /* chunk record: copies of g_cumsum, T, k_cumdecay and v_new */
+        if (J->dump_token >= t0 && J->dump_token < t0 + n && h == J->dump_head) {
+            for (int a = 0; a < n; ++a) {
+                J->dump_G[a] = G[a];
+                for (int c = 0; c < n; ++c) J->dump_T[a * C + c] = M[a * C + c];
+                for (int i = 0; i < dk; ++i) J->dump_W[a * dk + i] = KCD[a * dk + i];
+                for (int j = 0; j < dv; ++j) J->dump_U[a * dv + j] = VN[a * dv + j];
+            }
+            J->dump_meta[0] = t0;
+            J->dump_meta[1] = n;
+        }
         /* out = (exp(G) Q) S + qk v_new */
         for (int a = 0; a < n; ++a) {
             double *o = J->out + ((t0 + a) * J->H_v + h) * dv;
@@ -312,5 +329,41 @@ int gdn_oracle_run(int32_t n_seqs, const int64_t *cu_seqlens,
     J.out = out; J.s_out = s_out;
     J.chunk = chunk < 0 ? 0 : chunk;
     J.n_threads = n_threads;
+    J.dump_token = -1;
+    return run(&J);
+}
+
+/*
+ * The chunked form (chunk size `chunk`) for value head `head` only, keeping
+ * a copy of the intermediates of the chunk that holds packed token `token`:
+ * G (g_cumsum, chunk entries), T (the solved attn plus identity, chunk x
+ * chunk row-major), W (k_cumdecay, chunk x d_k) and U (v_new, chunk x d_v);
+ * meta receives the chunk's first token and length (length 0: no chunk holds
+ * the token).  out and s_out receive that head's results as gdn_oracle_run
+ * gives them.
+ */
+int gdn_oracle_chunk_dump(int32_t n_seqs, const int64_t *cu_seqlens,
+                          int32_t H_k, int32_t H_v, int32_t d_k, int32_t d_v,
+                          const double *q, const double *k, const double *v,
+                          const double *g, const double *beta, const double *s0,
+                          double scale, double eps, int32_t chunk, int64_t token, int32_t head,
+                          double *out, double *s_out,
+                          double *G, double *T, double *W, double *U, int64_t *meta)
+{
+    if (chunk <= 0 || head < 0 || head >= H_v) return -1;
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.n_seqs = n_seqs; J.cu = cu_seqlens;
+    J.H_k = H_k; J.H_v = H_v; J.d_k = d_k; J.d_v = d_v;
+    J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.s0 = s0;
+    J.scale = scale; J.eps = eps;
+    J.heads = &head; J.n_heads = 1;
+    J.out = out; J.s_out = s_out;
+    J.chunk = chunk;
+    J.n_threads = 1;
+    J.dump_token = token; J.dump_head = head;
+    J.dump_G = G; J.dump_T = T; J.dump_W = W; J.dump_U = U; J.dump_meta = meta;
+    meta[0] = 0;
+    meta[1] = 0;
     return run(&J);
 }

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert gdn.version() == 5
+    assert gdn.version() == 6
     for st in range(5):
         assert gdn.lib.gdn_status_string(st)
     assert gdn.lib.gdn_status_string(99) == b"unknown status"
@@ -262,3 +262,32 @@ def test_dims_layout_matches_the_header(tmp_path):
     assert got[0] == ctypes.sizeof(gdn.Dims)
     for f, off in zip(fields, got[1:]):
         assert getattr(gdn.Dims, f).offset == off, f
+
+
+def test_debug_record_layout_matches_the_header(tmp_path):
+    """gdn_debug_chunk: the binding's structure has the C struct's size and
+    field offsets."""
+    import subprocess
+    fields = [f for f, _ in gdn.DebugChunk._fields_]
+    src = tmp_path / "dbg.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "gdn.h"\nint main(void){\n'
+                   + 'printf("%zu\\n", sizeof(gdn_debug_chunk));\n'
+                   + "".join(f'printf("%zu\\n", offsetof(gdn_debug_chunk, {f}));\n' for f in fields)
+                   + "return 0;}\n")
+    exe = tmp_path / "dbg"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(gdn.DebugChunk)
+    for f, off in zip(fields, got[1:]):
+        assert getattr(gdn.DebugChunk, f).offset == off, f
+
+
+def test_debug_dump_without_a_record():
+    """No prefill has run with GDN_DEBUG_DUMP in this process: the accessor
+    reports it (and a NULL destination) without touching a device."""
+    assert gdn.lib.gdn_debug_dump(None) == 1
+    rec = gdn.DebugChunk()
+    assert gdn.lib.gdn_debug_dump(ctypes.byref(rec)) == 1
+    assert "GDN_DEBUG_DUMP" in gdn.lib.gdn_last_error().decode()
