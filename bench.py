@@ -516,7 +516,8 @@ def bench_layer_decode(gdn, dev, reps=3):
                         "+ SiLU, raw gates, gated RMSNorm, bf16 out, state + conv state in slot rows",
             "ms_per_step": ms / S, "tokens_s": N * S / (ms * 1e-3),
             "bytes_per_step": by, "achieved_gbs": gbs, "frac": gbs / PEAK_HBM_GBS,
-            "kernels": "decode_kernel + conv_state_kernel"}
+            "kernels": "decode_kernel (prologue, epilogue and the convolution state update in one "
+                       "launch: one workgroup per (sequence, key head))"}
 
 
 def bench_varlen(gdn, dev, reps=20):

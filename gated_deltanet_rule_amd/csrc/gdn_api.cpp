@@ -522,7 +522,7 @@ gdn_status gdn_recurrent_step(const gdn_dims *dims, const void *q, const void *k
     st = device_check(p, nullptr, n_seqs, n_seqs, slot_in, slot_out, s);
     if (st != GDN_OK) return st;
     st = hip_status(gdn::launch_decode(p, a, s), "decode");
-    if (st == GDN_OK && p.conv_w)
+    if (st == GDN_OK && p.conv_w && !gdn::decode_folds_conv(p))
         st = hip_status(gdn::launch_conv_state(p, qkv, nullptr, -1, n_seqs, n_seqs, state_in, state_out,
                                                slot_in, slot_out, s), "convolution state");
     return st;
@@ -552,7 +552,7 @@ gdn_status gdn_recurrent_multi(const gdn_dims *dims, const void *q, const void *
     st = device_check(p, cu_seqlens, n_seqs, total_tokens, slot_in, slot_out, s);
     if (st != GDN_OK) return st;
     st = hip_status(gdn::launch_decode_multi(p, a, s), "multi-token decode");
-    if (st == GDN_OK && p.conv_w)
+    if (st == GDN_OK && p.conv_w && !gdn::decode_folds_conv(p))
         st = hip_status(gdn::launch_conv_state(p, qkv, cu_seqlens, -1, n_seqs, total_tokens, state_in,
                                                state_out, slot_in, slot_out, s), "convolution state");
     return st;

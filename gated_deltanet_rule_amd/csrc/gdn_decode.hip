@@ -21,6 +21,13 @@
 //   epilogue: the workgroup holds a whole output row of its head, so the
 //     gated RMSNorm o / sqrt(mean(o^2) + eps) * w * silu(z) is applied in
 //     registers before the row is stored (one extra wave-level reduction).
+// With the prologue and H_v / H_k = 1 or 2, a workgroup takes every value
+// head of one key head (GR = H_v / H_k groups of 256 threads, one value head
+// each): it is then the only reader of the convolution state of the key
+// head's q and k channels and of its value heads' v channels, and replaces
+// that state (the last three inputs of each channel) itself, in place, once
+// every thread has read the old values.  Other head ratios keep one value
+// head per workgroup and leave the state to conv_state_kernel.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -43,6 +50,7 @@ struct RecParams {
     Gates gates;
     const float *conv_w;         // [conv_dim][4]; null: no prologue
     const float *conv_in;        // slot rows (convolution state first); null: zero
+    float *conv_out;             // slot rows receiving the new convolution state
     const void *z;               // [T][H_v][DV] gate, element type E; null: no epilogue
     const float *norm_w;         // [DV]
 };
@@ -59,12 +67,13 @@ Gates gates_of(const Problem &p, const float *g)
 RecParams rec_params(const Problem &p, const void *q, const void *k, const void *v, const float *g,
                      const float *beta, const float *state_in, float *state_out, void *out,
                      const int32_t *cu, const int32_t *slot_in, const int32_t *slot_out, int T,
-                     const float *conv_in)
+                     const float *conv_in, float *conv_out)
 {
     return RecParams{q, k, v, g, beta, state_in, state_out, out, cu, slot_in, slot_out, T,
                      p.H_k, p.H_v, p.slot_stride, p.rs_qk, p.rs_v, p.scale, p.eps, gates_of(p, g),
-                     p.conv_w, conv_in, p.z, p.norm_w};
+                     p.conv_w, conv_in, conv_out, p.z, p.norm_w};
 }
+
 
 // One channel of the prologue: silu(w0 h0 + w1 h1 + w2 h2 + w3 x), with h the
 // channel's three previous inputs (oldest first) and x the current one.
@@ -113,8 +122,10 @@ __device__ __forceinline__ void gated_norm_row(float o[4], const float zz[4], co
     for (int j = 0; j < 4; ++j) o[j] = o[j] * rn * nw[j] * silu(zz[j]);
 }
 
-template <int DK, int DV, typename E, typename OT, bool FUSED>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(RecParams P)
+// GR > 1 only with the prologue: GR value heads (those of key head
+// blockIdx.y), one per group of kDecodeThreads threads.
+template <int DK, int DV, typename E, typename OT, bool FUSED, int GR>
+__global__ __launch_bounds__(kDecodeThreads * GR) void decode_kernel(RecParams P)
 {
     constexpr int CG = DV / 4;                  // float4 column groups
     constexpr int RG = kDecodeThreads / CG;     // row groups
@@ -122,11 +133,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(RecParams P)
     static_assert(RPT >= 1 && RPT * RG == DK && 2 * DK <= kDecodeThreads, "bad decode tiling");
 
     const int i = blockIdx.x;                   // sequence (= token)
-    const int h = blockIdx.y;                   // value head
-    const int tid = threadIdx.x;
+    const int grp = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kDecodeThreads);
+    const int tid = (int)threadIdx.x % kDecodeThreads;
     const int cg = tid % CG;
     const int rg = tid / CG;
     const int col = cg * 4;
+    const int h = GR > 1 ? (int)blockIdx.y * GR + grp : (int)blockIdx.y;   // value head
     const int kh = h / (P.H_v / P.H_k);         // blocked key-head sharing
     const E *q = static_cast<const E *>(P.q);
     const E *k = static_cast<const E *>(P.k);
@@ -134,9 +146,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(RecParams P)
     const bool conv = FUSED && P.conv_w != nullptr;
     const bool norm = FUSED && P.z != nullptr;
 
-    __shared__ float sk[DK];
-    __shared__ float sq[DK];
-    __shared__ float4 red[2][RG][CG];
+    __shared__ float sk_[GR][DK];
+    __shared__ float sq_[GR][DK];
+    __shared__ float4 red_[GR][2][RG][CG];
+    float *sk = sk_[grp];
+    float *sq = sq_[grp];
+    float4(&red)[2][RG][CG] = red_[grp];
 
     const int sin = P.state_in ? P.slot_in[i] : -1;
     const int sout = P.slot_out[i];
@@ -155,6 +170,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(RecParams P)
 
     // 2. q, k of the key head, v of this column group, scalars
     const int64_t qk_off = (int64_t)i * P.rs_qk + (int64_t)kh * DK;
+    // prologue: the new convolution state [h1, h2, x] of this thread's q or k
+    // channel and of its four v channels, written after the barrier below
+    float4 nqk = make_float4(0.f, 0.f, 0.f, 0.f);
+    float nv[12];
     if (tid < 2 * DK) {
         const bool isk = tid < DK;
         const int e = isk ? tid : tid - DK;
@@ -163,6 +182,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(RecParams P)
             const int64_t ch = (isk ? (int64_t)P.H_k * DK : 0) + (int64_t)kh * DK + e;
             float h0, h1, h2;
             conv_hist(P, sin, ch, h0, h1, h2);
+            nqk = make_float4(h1, h2, x, 0.f);
             x = conv1(*reinterpret_cast<const float4 *>(P.conv_w + ch * 4), h0, h1, h2, x);
         }
         (isk ? sk : sq)[e] = x;
@@ -182,7 +202,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(RecParams P)
         conv_hist4(P, sin, ch0, hv);
         const float4 *wp = reinterpret_cast<const float4 *>(P.conv_w + ch0 * 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) vv[j] = conv1(wp[j], hv[3 * j], hv[3 * j + 1], hv[3 * j + 2], vv[j]);
+        for (int j = 0; j < 4; ++j) {
+            nv[3 * j] = hv[3 * j + 1];
+            nv[3 * j + 1] = hv[3 * j + 2];
+            nv[3 * j + 2] = vv[j];
+            vv[j] = conv1(wp[j], hv[3 * j], hv[3 * j + 1], hv[3 * j + 2], vv[j]);
+        }
     }
     float zz[4] = {0.f, 0.f, 0.f, 0.f}, nw[4] = {0.f, 0.f, 0.f, 0.f};
     if (norm) {
@@ -192,7 +217,30 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(RecParams P)
         for (int j = 0; j < 4; ++j) zz[j] = to_f32(zp[j]);
         nw[0] = w4.x; nw[1] = w4.y; nw[2] = w4.z; nw[3] = w4.w;
     }
-    lds_sync();
+    if (conv && P.conv_out) {
+        // every thread's loads of the old convolution state are complete
+        // (this barrier waits for them), so each group's v channels and the
+        // key head's q and k channels take their new state; no other
+        // workgroup reads them
+        __syncthreads();
+        if (sout >= 0) {
+            float *cs = P.conv_out + (int64_t)sout * P.slot_stride;
+            if (rg == 0) {
+                float4 *vp4 = reinterpret_cast<float4 *>(cs + (2 * (int64_t)P.H_k * DK + (int64_t)h * DV + col) * 3);
+                vp4[0] = make_float4(nv[0], nv[1], nv[2], nv[3]);
+                vp4[1] = make_float4(nv[4], nv[5], nv[6], nv[7]);
+                vp4[2] = make_float4(nv[8], nv[9], nv[10], nv[11]);
+            }
+            if (grp == 0 && tid < 2 * DK) {
+                const int64_t ch = (tid < DK ? (int64_t)P.H_k * DK + tid : (int64_t)(tid - DK)) + (int64_t)kh * DK;
+                cs[ch * 3] = nqk.x;
+                cs[ch * 3 + 1] = nqk.y;
+                cs[ch * 3 + 2] = nqk.z;
+            }
+        }
+    } else {
+        lds_sync();
+    }
 
     // 3. norms (every wave reduces redundantly; no extra barrier)
     float kk = 0.f, qq = 0.f, kq = 0.f;
@@ -291,8 +339,8 @@ __device__ __forceinline__ float rg_wave_sum(float x)
     return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
 }
 
-template <int DK, int DV, typename E, typename OT, bool FUSED>
-__global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(RecParams P)
+template <int DK, int DV, typename E, typename OT, bool FUSED, int GR>
+__global__ __launch_bounds__(kDecodeThreads * GR) void decode_multi_kernel(RecParams P)
 {
     constexpr int CG = DV / 4;                  // float4 column groups
     constexpr int RG = kDecodeThreads / CG;     // row groups
@@ -300,11 +348,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(RecParams 
     static_assert(RPT >= 1 && RPT * RG == DK && 2 * DK <= kDecodeThreads, "bad decode tiling");
 
     const int i = blockIdx.x;                   // sequence
-    const int h = blockIdx.y;                   // value head
-    const int tid = threadIdx.x;
+    const int grp = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kDecodeThreads);
+    const int tid = (int)threadIdx.x % kDecodeThreads;
     const int cg = tid % CG;
     const int rg = tid / CG;
     const int col = cg * 4;
+    const int h = GR > 1 ? (int)blockIdx.y * GR + grp : (int)blockIdx.y;   // value head
     const int kh = h / (P.H_v / P.H_k);
     const int lane = tid & 63;
     const E *q = static_cast<const E *>(P.q);
@@ -313,10 +362,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(RecParams 
     const bool conv = FUSED && P.conv_w != nullptr;
     const bool norm = FUSED && P.z != nullptr;
 
-    __shared__ float sk[2][DK];
-    __shared__ float sq[2][DK];
+    __shared__ float sk_[GR][2][DK];
+    __shared__ float sq_[GR][2][DK];
     constexpr int NW = kDecodeThreads / 64;
-    __shared__ float4 red[2][2][NW][CG];
+    __shared__ float4 red_[GR][2][2][NW][CG];
+    float(&sk)[2][DK] = sk_[grp];
+    float(&sq)[2][DK] = sq_[grp];
+    float4(&red)[2][2][NW][CG] = red_[grp];
 
     // tokens of this sequence (clamped so that bad cu_seqlens stay in range)
     const int tb = min(max(P.cu[i], 0), P.T);
@@ -493,18 +545,54 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(RecParams 
         for (int r = 0; r < RPT; ++r)
             *reinterpret_cast<float4 *>(base + (int64_t)(rg + r * RG) * DV) = s[r];
     }
+    if (conv && P.conv_out) {
+        // The windows hold the last three inputs of each channel (the old
+        // state shifted by the sequence's rows): the new convolution state.
+        // Every thread's loads of the old state are complete past this
+        // barrier; each group's v channels and the key head's q and k
+        // channels are read by no other workgroup.
+        __syncthreads();
+        if (sout >= 0) {
+            float *cs = P.conv_out + (int64_t)sout * P.slot_stride;
+            if (rg == 0) {
+                float4 *vp4 = reinterpret_cast<float4 *>(cs + chv * 3);
+                vp4[0] = make_float4(hv[0], hv[1], hv[2], hv[3]);
+                vp4[1] = make_float4(hv[4], hv[5], hv[6], hv[7]);
+                vp4[2] = make_float4(hv[8], hv[9], hv[10], hv[11]);
+            }
+            if (grp == 0 && tid < 2 * DK) {
+                cs[chq * 3] = hq[0];
+                cs[chq * 3 + 1] = hq[1];
+                cs[chq * 3 + 2] = hq[2];
+            }
+        }
+    }
+}
+
+// Value heads per workgroup with the prologue: H_v / H_k when it is 1 or 2,
+// else 0 (one value head per workgroup, the state left to
+// conv_state_kernel).  Four groups would not fit the kernels' registers into
+// the 128 per thread of a 1024-thread workgroup.
+int conv_groups(const Problem &p)
+{
+    const int r = p.H_v / p.H_k;
+    return r == 1 || r == 2 ? r : 0;
 }
 
 template <int DK, int DV, typename E, typename OT>
 hipError_t launch_multi_t(const Problem &p, const DecodeMultiArgs &a, hipStream_t st)
 {
     const RecParams P = rec_params(p, a.q, a.k, a.v, a.g, a.beta, a.state_in, a.state_out, a.out,
-                                   a.cu_seqlens, a.slot_in, a.slot_out, (int)a.total_tokens, a.conv_in);
-    if (p.conv_w || p.z)
-        hipLaunchKernelGGL((decode_multi_kernel<DK, DV, E, OT, true>), dim3(a.n_seqs, p.H_v),
+                                   a.cu_seqlens, a.slot_in, a.slot_out, (int)a.total_tokens, a.conv_in,
+                                   decode_folds_conv(p) ? a.conv_out : nullptr);
+    if (!p.conv_w && !p.z)
+        hipLaunchKernelGGL((decode_multi_kernel<DK, DV, E, OT, false, 1>), dim3(a.n_seqs, p.H_v),
                            dim3(kDecodeThreads), 0, st, P);
+    else if (p.conv_w && conv_groups(p) == 2)
+        hipLaunchKernelGGL((decode_multi_kernel<DK, DV, E, OT, true, 2>), dim3(a.n_seqs, p.H_k),
+                           dim3(2 * kDecodeThreads), 0, st, P);
     else
-        hipLaunchKernelGGL((decode_multi_kernel<DK, DV, E, OT, false>), dim3(a.n_seqs, p.H_v),
+        hipLaunchKernelGGL((decode_multi_kernel<DK, DV, E, OT, true, 1>), dim3(a.n_seqs, p.H_v),
                            dim3(kDecodeThreads), 0, st, P);
     return hipGetLastError();
 }
@@ -513,13 +601,17 @@ template <int DK, int DV, typename E, typename OT>
 hipError_t launch_t(const Problem &p, const DecodeArgs &a, hipStream_t st)
 {
     const RecParams P = rec_params(p, a.q, a.k, a.v, a.g, a.beta, a.state_in, a.state_out, a.out,
-                                   nullptr, a.slot_in, a.slot_out, a.n_seqs, a.conv_in);
-    if (p.conv_w || p.z)
-        hipLaunchKernelGGL((decode_kernel<DK, DV, E, OT, true>), dim3(a.n_seqs, p.H_v), dim3(kDecodeThreads), 0,
-                           st, P);
+                                   nullptr, a.slot_in, a.slot_out, a.n_seqs, a.conv_in,
+                                   decode_folds_conv(p) ? a.conv_out : nullptr);
+    if (!p.conv_w && !p.z)
+        hipLaunchKernelGGL((decode_kernel<DK, DV, E, OT, false, 1>), dim3(a.n_seqs, p.H_v), dim3(kDecodeThreads),
+                           0, st, P);
+    else if (p.conv_w && conv_groups(p) == 2)
+        hipLaunchKernelGGL((decode_kernel<DK, DV, E, OT, true, 2>), dim3(a.n_seqs, p.H_k),
+                           dim3(2 * kDecodeThreads), 0, st, P);
     else
-        hipLaunchKernelGGL((decode_kernel<DK, DV, E, OT, false>), dim3(a.n_seqs, p.H_v), dim3(kDecodeThreads), 0,
-                           st, P);
+        hipLaunchKernelGGL((decode_kernel<DK, DV, E, OT, true, 1>), dim3(a.n_seqs, p.H_v), dim3(kDecodeThreads),
+                           0, st, P);
     return hipGetLastError();
 }
 
@@ -562,6 +654,11 @@ hipError_t launch_any(const Problem &p, const Args &a, hipStream_t st)
 }
 
 }  // namespace
+
+bool decode_folds_conv(const Problem &p)
+{
+    return p.conv_w && conv_groups(p) != 0;
+}
 
 hipError_t launch_decode(const Problem &p, const DecodeArgs &a, hipStream_t st)
 {

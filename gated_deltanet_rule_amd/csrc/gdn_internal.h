@@ -59,6 +59,11 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const Problem &p, const DecodeArgs &a, hipStream_t s);
 
+// With the prologue and H_v / H_k in {1, 2} the recurrent kernels replace the
+// convolution state themselves (one workgroup per (sequence, key head));
+// otherwise the caller runs launch_conv_state after them.
+bool decode_folds_conv(const Problem &p);
+
 // several tokens per sequence, recurrent form, no workspace
 struct DecodeMultiArgs {
     const void *q, *k, *v;

@@ -196,6 +196,34 @@ def test_decode_step_layer_f32_tight():
     assert np.array_equal(cs[dc.slots].astype(np.float64), ref_c)
 
 
+@pytest.mark.parametrize("H_k,H_v", [(2, 2), (1, 4)])
+def test_decode_step_layer_head_ratios(H_k, H_v):
+    """The prologue at head ratios 1 (one value head per workgroup, state
+    replaced by the decode kernel) and 4 (state replaced by the separate
+    pass), with in-place pools."""
+    dc = gi.make_decode("layer_ratio", 5, 4, H_k, H_v, 64, 64, "f32", seed=90, decay="weak")
+    L = gi.make_layer_inputs(5 * 4, 5, H_k, H_v, 64, 64, "f32", 90)
+    say(f"layer decode ratios H_k={H_k} H_v={H_v}")
+    outs, pool = _decode_steps(dc, L)
+    case, Lc = _decode_as_case(dc, L)
+    ref_o, ref_s, ref_c = oracle_layer(case, Lc)
+    ref_o = ref_o.reshape(5, 4, H_v, 64).swapaxes(0, 1)
+    eo, _ = rel_err(outs.cpu().numpy(), ref_o)
+    cs, st = split_pool(case, Lc, pool)
+    es, _ = rel_err(st[dc.slots].astype(np.float64), ref_s)
+    assert eo <= TOL["f32"] and es <= TOL["f32"]
+    assert np.array_equal(cs[dc.slots].astype(np.float64), ref_c)
+
+
+@pytest.mark.parametrize("H_k,H_v", [(2, 2), (1, 4)])
+def test_multi_layer_head_ratios(H_k, H_v):
+    case = gi.make_case("layer_multi_ratio", [0, 1, 3, 9], H_k, H_v, 64, 64, "f32", seed=91,
+                        decay="weak", n_slots=6, scatter_slots=True)
+    L = _layer(case, 91)
+    out, pool = gpu_layer_multi(case, L)
+    compare_layer(case, L, out, pool, oracle_layer(case, L))
+
+
 def test_multi_layer_speculative_qwen_heads():
     case = gi.make_case("layer_spec64x4", [4] * 64, dtype="bf16", seed=87, n_slots=64,
                         scatter_slots=True, **gi.QWEN3_NEXT_HEADS)
