@@ -1,10 +1,12 @@
 """GDN_DEBUG_DUMP: the library's record of one chunk's intermediates (G, T,
 W = k_cumdecay, U = v_new) against the oracle's chunk record on the same
 inputs.  Bounds: G is the same fp64 cumulative sum of the same fp32 gates; T
-and W are formed in fp32 from exact bf16 products and two-term operands
-(relative error ~1e-6 of their magnitude); U carries the rounding of W to a
-bf16 operand in the scan (2^-9 relative) and is held to the output bound of
-the bf16 parity tests."""
+is formed in fp32 from exact bf16 products by substitution (held to 1e-6 of
+max|T|; measured up to 5e-8), W from two-term bf16 operands (16 significant
+bits: held to 5e-5 of max|W|; measured up to 4e-6); U carries the rounding of
+W to a bf16 operand in the scan (2^-9 relative) and the state carried from
+earlier chunks, and is held to the output bound of the bf16 parity tests
+(measured 2e-5 in a sequence's second chunk, 3e-3 after 70 chunks)."""
 import os
 
 import numpy as np
@@ -35,7 +37,7 @@ def _s0(case):
 def _compare(rec, ref, dtype):
     assert rec["prepared"] == 1 and rec["scanned"] == 1
     assert rec["t0"] == ref["t0"] and rec["len"] == ref["len"]
-    for name, tol in (("G", 1e-12), ("T", 2e-4), ("W", 2e-4)):
+    for name, tol in (("G", 1e-12), ("T", 1e-6), ("W", 5e-5)):
         err = np.abs(rec[name] - ref[name]).max() / max(np.abs(ref[name]).max(), 1e-30)
         say(f"  {name}: max err {err:.2e} of max|ref|")
         assert err <= tol, name
@@ -94,3 +96,21 @@ def test_debug_record_split_phase_and_outside(dump_env):
     gpu_prefill(case, d=d, inplace=False)
     rec3 = gdn.debug_dump()
     assert rec3["prepared"] == 0 and rec3["scanned"] == 0 and rec3["chunk"] == -1
+
+
+@pytest.mark.parametrize("chunk", [70, 128])
+def test_debug_record_in_a_later_chunk_range(dump_env, chunk):
+    """A 8229-token call runs as several chunk ranges (64 chunks each at
+    these heads): the record of a chunk in the second range (chunk 70) and of
+    the partial last chunk (128, 37 tokens), whose state entered through the
+    ranges' carry, matches the oracle's."""
+    import gated_deltanet_rule_amd as gdn
+    case = gi.make_case("dump_ranges", [8229], dtype="bf16", seed=43, decay="weak", **gi.QWEN3_NEXT_HEADS)
+    token, head = 64 * chunk + 5, 17
+    os.environ["GDN_DEBUG_DUMP"] = f"{token},{head}"
+    gpu_prefill(case, inplace=False)
+    rec = gdn.debug_dump()
+    ref = oracle.chunk_dump(case.q, case.k, case.v, case.g, case.beta, case.cu_seqlens.astype(np.int64),
+                            _s0(case), token=token, head=head)
+    assert rec["chunk"] == chunk
+    _compare(rec, ref, "bf16")
