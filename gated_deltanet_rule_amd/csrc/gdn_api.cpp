@@ -290,7 +290,7 @@ gdn_status check_scan_inputs(const float *state_in, float *state_out, void *out,
 
 // The chunked prefill of a validated call: device check, then `per`-chunk
 // ranges (preparation, scan) over the workspace, then the convolution state.
-gdn_status run_chunked(gdn::Problem p, const void *qkv, const void *q, const void *k,
+gdn_status run_chunked(gdn::Problem p, const void *q, const void *k,
                        const void *v, const float *g, const float *beta, const float *state_in,
                        float *state_out, void *out, const int32_t *cu_seqlens,
                        const int32_t *slot_in, const int32_t *slot_out, int32_t n_seqs,
@@ -316,11 +316,8 @@ gdn_status run_chunked(gdn::Problem p, const void *qkv, const void *q, const voi
         st = hip_status(gdn::launch_prepare(p, a, sg, s), "prepare");
         if (st == GDN_OK) st = hip_status(gdn::launch_scan(p, a, sg, s), "scan");
     }
-    // the convolution state is replaced only after the preparation has read it
-    if (st == GDN_OK && p.conv_w)
-        st = hip_status(gdn::launch_conv_state(p, qkv, cu_seqlens, n_seqs == 1 ? (int)total_tokens : -1,
-                                               n_seqs, total_tokens, state_in, state_out, slot_in,
-                                               slot_out, s), "convolution state");
+    // (with the prologue the scans also replace each sequence's convolution
+    // state, in the range that holds its last chunk)
     if (st == GDN_OK) st = debug_collect(p, s);
     return st;
 }
@@ -444,7 +441,6 @@ gdn_status gdn_chunked_prefill(const gdn_dims *dims, const void *q, const void *
     g_last_error[0] = 0;
     gdn::Problem p;
     gdn_status st = resolve(dims, &p);
-    const void *qkv = q;
     if (st == GDN_OK) st = mixed_rows(p, q, k, v);
     if (st == GDN_OK) st = check_counts(n_seqs, total_tokens);
     if (st == GDN_OK) st = check_prepare_inputs(q, k, v, g, beta, cu_seqlens);
@@ -456,7 +452,7 @@ gdn_status gdn_chunked_prefill(const gdn_dims *dims, const void *q, const void *
     const int per = gdn::segment_chunks(p, chunks);
     st = check_workspace(p, n_seqs, total_tokens, workspace, workspace_bytes, per);
     if (st != GDN_OK) return st;
-    return run_chunked(p, qkv, q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in,
+    return run_chunked(p, q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in,
                        slot_out, n_seqs, total_tokens, workspace, per, static_cast<hipStream_t>(stream));
 }
 
@@ -470,7 +466,6 @@ gdn_status gdn_chunked_prefill_noalloc(const gdn_dims *dims, const void *q, cons
     g_last_error[0] = 0;
     gdn::Problem p;
     gdn_status st = resolve(dims, &p);
-    const void *qkv = q;
     if (st == GDN_OK) st = mixed_rows(p, q, k, v);
     if (st == GDN_OK) st = check_counts(n_seqs, total_tokens);
     if (st == GDN_OK) st = check_prepare_inputs(q, k, v, g, beta, cu_seqlens);
@@ -495,7 +490,7 @@ gdn_status gdn_chunked_prefill_noalloc(const gdn_dims *dims, const void *q, cons
         if (gdn::prefill_workspace_bytes(p, n_seqs, total_tokens, mid) <= cap) lo = mid;
         else hi = mid - 1;
     }
-    return run_chunked(p, qkv, q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in,
+    return run_chunked(p, q, k, v, g, beta, state_in, state_out, out, cu_seqlens, slot_in,
                        slot_out, n_seqs, total_tokens, ws, lo, static_cast<hipStream_t>(stream), false);
 }
 

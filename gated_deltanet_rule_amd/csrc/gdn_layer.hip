@@ -6,9 +6,11 @@
 //     last kConv - 1 rows of (old state ++ the sequence's rows), per channel
 //     (the page's new_conv_states view of the ssm_conv result).  It is its own
 //     launch, after every kernel that read the old state, so that the state
-//     can be updated in place: a key head's channels are read by several
-//     workgroups of the operator kernels, and none of them could know when the
-//     others are done with the old values.
+//     can be updated in place: with H_v / H_k other than 1 or 2 a key head's
+//     channels are read by several workgroups of the recurrent kernels, and
+//     none of them could know when the others are done with the old values.
+//     (The chunked prefill's scan and the recurrent kernels at ratios 1 and 2
+//     replace the state themselves.)
 //   gated_norm_kernel: out = o / sqrt(mean(o^2) + eps) * norm_w * silu(z)
 //     over every (token, value head) row of the chunked prefill's fp32 o (its
 //     scan spreads a row's columns over several workgroups; the recurrent

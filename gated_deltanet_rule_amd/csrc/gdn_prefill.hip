@@ -37,7 +37,8 @@
 //                (state rows):  S = gn * S + K^T (ks * U)
 //      U and S are exchanged through LDS as ready-made operand fragments;
 //      each wave loads its own operands from the workspace straight into
-//      registers, one chunk ahead.
+//      registers, one chunk ahead.  With the layer prologue the launch that
+//      holds a sequence's last chunk also writes its new convolution state.
 //
 // Norms, scale, beta and decay are folded into per-row / per-column scalars
 // of raw (bf16) operands, so the inputs are used as MFMA operands exactly as
@@ -1084,6 +1085,14 @@ struct ScanParams {
     // value head dbg_h
     gdn_debug_chunk *dbg = nullptr;
     int dbg_h = -1;
+    // layer prologue (conv_out non-null): the new convolution state of each
+    // sequence, the last kConv - 1 inputs of (its state ++ its rows), per
+    // channel of the mixed rows conv_x ([T][conv_dim], element type E); the
+    // state rows of slot s start at conv_in / conv_out + s * slot_stride
+    const void *conv_x = nullptr;
+    const float *conv_in = nullptr;
+    float *conv_out = nullptr;
+    int conv_dim = 0;
 };
 
 template <int DK, int DV, int CT, typename E> struct ScanLds {
@@ -1451,6 +1460,51 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
             lds_sync();
         }
     }
+
+    // The layer prologue's new convolution state, written by the launch that
+    // holds the sequence's last chunk (an empty sequence's, which only copies
+    // the state, by the first range's): every preparation that read the old
+    // state ran before this launch.  The workgroups of a sequence split its
+    // channels: each its column tile of its value head's v channels, and a
+    // share of its key head's q and k channels.  One wave each.
+    if (sp.conv_out && (empty ? sp.seg_lo == 0 : !carried_out) && role == 1 && rt == 0 && ctl == 0) {
+        constexpr int kH = kConv - 1;
+        const int sout = sp.slot_out[i];
+        if (sout >= 0) {
+            const int sin = sp.conv_in ? sp.slot_in[i] : -1;
+            int64_t tb = 0, te = 0;
+            if (single) {
+                te = sp.single_T;
+            } else if (!empty) {
+                tb = sp.ent[cs_seq].t0;
+                te = sp.ent[ce_seq - 1].t0 + sp.ent[ce_seq - 1].len;
+            }
+            const int64_t len = te - tb;
+            const E *x = static_cast<const E *>(sp.conv_x);
+            const int ratio = sp.H_v / sp.H_k, ntile = DV / 16;
+            const int parts = ratio * ntile, part = (h % ratio) * ntile + ct;
+            const int nqk = (2 * DK + parts - 1 - part) / parts;      // q/k channels part + parts * m
+            // one lane per channel: its three new values are read before any is written
+            for (int m = lane; m < 16 + nqk; m += 64) {
+                int64_t ch;
+                if (m < 16) {
+                    ch = 2 * (int64_t)sp.H_k * DK + (int64_t)h * DV + col0 + m;
+                } else {
+                    const int c = part + parts * (m - 16);           // of the key head's q then k channels
+                    ch = (c < DK ? (int64_t)kh * DK + c : (int64_t)sp.H_k * DK + (int64_t)kh * DK + (c - DK));
+                }
+                float nu[kH];
+#pragma unroll
+                for (int jj = 0; jj < kH; ++jj) {
+                    const int64_t el = len + jj;                     // element len + jj of (state ++ rows)
+                    nu[jj] = el < kH ? (sin >= 0 ? sp.conv_in[(int64_t)sin * sp.slot_stride + ch * kH + el] : 0.f)
+                                     : to_f32(x[(tb + el - kH) * sp.conv_dim + ch]);
+                }
+#pragma unroll
+                for (int jj = 0; jj < kH; ++jj) sp.conv_out[(int64_t)sout * sp.slot_stride + ch * kH + jj] = nu[jj];
+            }
+        }
+    }
 }
 
 // --------------------------------------------------------------------------
@@ -1549,6 +1603,12 @@ hipError_t scan_t(const Problem &p, const PrefillArgs &a, const Segment &sg, hip
                   a.n_seqs == 1 ? (int)a.total_tokens : -1, sg.lo, sg.hi, sg.idx, w.carry};
     sp.dbg = p.dbg;
     sp.dbg_h = p.dbg_head;
+    if (p.conv_w) {
+        sp.conv_x = a.q;               // the mixed rows (q is their first channel range)
+        sp.conv_in = a.conv_in;
+        sp.conv_out = a.conv_out;
+        sp.conv_dim = p.conv_dim;
+    }
     // With several sequences, one scan workgroup per CU: two workgroups on
     // one CU contend for its vector-memory path and LDS (the varlen batch of
     // 12 221 tokens takes 0.39 instead of 0.30 ms in the scan), so the
