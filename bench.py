@@ -72,9 +72,9 @@ C = 64
 PREFILL_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
                for f in ("gdn_prefill.hip", "gdn_mfma.h", "gdn_device.h", "gdn_internal.h")]
 MEASURED_TRAFFIC = {
-    "source_sha256": "c1cd259b4acaecb45cd7a9c4b1cfe1c7d0841760bd1435124206e384df3a714a",
-    "scan": (83629.5 * 2.000 + 67584.0 * 1.000) * 1024,
-    "prepare": (42073.5 * 2.000 + 165273.0 * 1.000) * 1024,
+    "source_sha256": "ba591a3a9e070a8af89fa40beee94859e76b484d2be4e9d41653c2425db1975a",
+    "scan": (83638.5 * 2.000 + 67584.0 * 1.000) * 1024,
+    "prepare": (42070.5 * 2.000 + 165281.4 * 1.000) * 1024,
 }
 
 
