@@ -110,22 +110,67 @@ __device__ __forceinline__ void conv_hist4(const RecParams &P, int sin, int64_t 
     }
 }
 
-// Gated RMSNorm of a row spread over CG consecutive lanes, four values each.
+// Gated RMSNorm of a row spread over CG consecutive lanes, four values each;
+// zg = w * silu(z) of the same four columns.
 template <int CG, int DV>
-__device__ __forceinline__ void gated_norm_row(float o[4], const float zz[4], const float nw[4], float eps)
+__device__ __forceinline__ void gated_norm_row(float o[4], const float zg[4], float eps)
 {
     float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
 #pragma unroll
     for (int off = CG / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
     const float rn = rsqrtf(ss / DV + eps);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = o[j] * rn * nw[j] * silu(zz[j]);
+    for (int j = 0; j < 4; ++j) o[j] = o[j] * rn * zg[j];
 }
+
+// Four consecutive values of E through a buffer resource (one 8- or
+// 16-byte access; zeros past the range's end).
+template <typename E> __device__ __forceinline__ void buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off, float f[4]);
+template <> __device__ __forceinline__ void buf_load4<bf16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off, float f[4]) {
+    const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    f[0] = __uint_as_float(u.x << 16);
+    f[1] = __uint_as_float(u.x & 0xffff0000u);
+    f[2] = __uint_as_float(u.y << 16);
+    f[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+template <> __device__ __forceinline__ void buf_load4<float>(__amdgpu_buffer_rsrc_t r, uint32_t off, float f[4]) {
+    const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    f[0] = __uint_as_float(u.x);
+    f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z);
+    f[3] = __uint_as_float(u.w);
+}
+__device__ __forceinline__ float4 buf_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+__device__ __forceinline__ void buf_store_f4(float4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)}, r, off, 0, 0);
+}
+// A buffer offset past every range used here: the hardware range check drops
+// a store to it (a lane that must not write gets this offset instead of a
+// branch around the store).
+constexpr uint32_t kDropOffset = 0x80000000u;
+// The loads that produced v are complete at this point of the program (the
+// compiler's wait for them is placed here); no code is emitted.
+__device__ __forceinline__ void loaded(float v) { asm volatile("" ::"v"(v)); }
 
 // GR > 1 only with the prologue: GR value heads (those of key head
 // blockIdx.y), one per group of kDecodeThreads threads.
+//
+// Order of memory operations: every small input (q, k, v, the gates and,
+// when fused, the convolution taps and state, z and the norm weight) is
+// loaded before the state block, and none of these loads sits behind a
+// branch.  The wait counter completes loads in issue order, so the prologue's
+// wait for them leaves the state block's loads in flight: the prologue, the
+// norms of q and k and their exchange through LDS overlap the stream of the
+// state, instead of each following it as a further round trip.  Inputs that
+// may be absent (a state slot of -1, no state pool, a part of the fusion
+// switched off) are read through empty buffer ranges, which return zeros
+// without touching memory.
 template <int DK, int DV, typename E, typename OT, bool FUSED, int GR>
-__global__ __launch_bounds__(kDecodeThreads * GR) void decode_kernel(RecParams P)
+__global__ __launch_bounds__(kDecodeThreads * GR, 4) void decode_kernel(RecParams P)
 {
     constexpr int CG = DV / 4;                  // float4 column groups
     constexpr int RG = kDecodeThreads / CG;     // row groups
@@ -149,6 +194,9 @@ __global__ __launch_bounds__(kDecodeThreads * GR) void decode_kernel(RecParams P
     __shared__ float sk_[GR][DK];
     __shared__ float sq_[GR][DK];
     __shared__ float4 red_[GR][2][RG][CG];
+    // fused: v after the prologue and w * silu(z), one value per channel
+    __shared__ __attribute__((aligned(16))) float sv_[FUSED ? GR : 1][FUSED ? DV : 1];
+    __shared__ __attribute__((aligned(16))) float sz_[FUSED ? GR : 1][FUSED ? DV : 1];
     float *sk = sk_[grp];
     float *sq = sq_[grp];
     float4(&red)[2][RG][CG] = red_[grp];
@@ -156,88 +204,101 @@ __global__ __launch_bounds__(kDecodeThreads * GR) void decode_kernel(RecParams P
     const int sin = P.state_in ? P.slot_in[i] : -1;
     const int sout = P.slot_out[i];
 
-    // 1. stream the state block in (independent of everything else)
-    float4 s[RPT];
-    if (sin >= 0) {
-        const float *base = P.state_in + (int64_t)sin * P.slot_stride + (int64_t)h * DK * DV + col;
-#pragma unroll
-        for (int r = 0; r < RPT; ++r)
-            s[r] = *reinterpret_cast<const float4 *>(base + (int64_t)(rg + r * RG) * DV);
-    } else {
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) s[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-
-    // 2. q, k of the key head, v of this column group, scalars
-    const int64_t qk_off = (int64_t)i * P.rs_qk + (int64_t)kh * DK;
-    // prologue: the new convolution state [h1, h2, x] of this thread's q or k
-    // channel and of its four v channels, written after the barrier below
-    float4 nqk = make_float4(0.f, 0.f, 0.f, 0.f);
-    float nv[12];
-    if (tid < 2 * DK) {
-        const bool isk = tid < DK;
-        const int e = isk ? tid : tid - DK;
-        float x = to_f32((isk ? k : q)[qk_off + e]);
-        if (conv) {
-            const int64_t ch = (isk ? (int64_t)P.H_k * DK : 0) + (int64_t)kh * DK + e;
-            float h0, h1, h2;
-            conv_hist(P, sin, ch, h0, h1, h2);
-            nqk = make_float4(h1, h2, x, 0.f);
-            x = conv1(*reinterpret_cast<const float4 *>(P.conv_w + ch * 4), h0, h1, h2, x);
-        }
-        (isk ? sk : sq)[e] = x;
-    }
+    // 1. small inputs: one q or k channel of the key head per thread (the
+    //    threads past 2 DK repeat one), the scalars, and v: four columns per
+    //    thread, or (fused) one channel per thread, whose convolution and
+    //    norm gate are formed once and shared through LDS
+    const int e2 = tid % (2 * DK);
+    const bool isk = e2 < DK;
+    const int e = isk ? e2 : e2 - DK;
+    const int ev = tid % DV;
+    float x = to_f32((isk ? k : q)[(int64_t)i * P.rs_qk + (int64_t)kh * DK + e]);
+    const E *vrow = v + (int64_t)i * P.rs_v + (int64_t)h * DV;
+    float vv[4];
+    float xv = 0.f;
+    if constexpr (FUSED)
+        xv = to_f32(vrow[ev]);
+    else
+        buf_load4<E>(raw_buffer(const_cast<E *>(vrow), DV * sizeof(E)), col * sizeof(E), vv);
     float gi = P.g[(int64_t)i * P.H_v + h];
     float bi = P.beta[(int64_t)i * P.H_v + h];
+    const float rate = P.gates.rate[h], bias = P.gates.bias[h];
+    // prologue and epilogue inputs: taps and stored inputs of this thread's q
+    // or k channel and v channel, its z and norm weight
+    const int conv_dim = 2 * P.H_k * DK + P.H_v * DV;
+    const int64_t ch = (isk ? (int64_t)P.H_k * DK : 0) + (int64_t)kh * DK + e;
+    const int64_t chv = 2 * (int64_t)P.H_k * DK + (int64_t)h * DV + ev;
+    u32x3 hq = {0u, 0u, 0u}, hv = {0u, 0u, 0u};
+    float4 wq = make_float4(0.f, 0.f, 0.f, 0.f), wv = wq;
+    float zs = 0.f, nws = 0.f;
+    if constexpr (FUSED) {
+        const bool hist = conv && sin >= 0;
+        const auto hb = raw_buffer(hist ? const_cast<float *>(P.conv_in + (int64_t)sin * P.slot_stride) : nullptr,
+                                   hist ? (uint32_t)conv_dim * 12u : 0u);
+        const auto tb = raw_buffer(const_cast<float *>(P.conv_w), conv ? (uint32_t)conv_dim * 16u : 0u);
+        hq = __builtin_amdgcn_raw_buffer_load_b96(hb, (uint32_t)ch * 12u, 0, 0);
+        wq = buf_load_f4(tb, (uint32_t)ch * 16u);
+        hv = __builtin_amdgcn_raw_buffer_load_b96(hb, (uint32_t)chv * 12u, 0, 0);
+        wv = buf_load_f4(tb, (uint32_t)chv * 16u);
+        const E *zrow = norm ? static_cast<const E *>(P.z) + ((int64_t)i * P.H_v + h) * DV : nullptr;
+        const auto zb = raw_buffer(const_cast<E *>(zrow), norm ? DV * sizeof(E) : 0u);
+        if constexpr (sizeof(E) == 2)
+            zs = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(zb, ev * 2u, 0, 0) << 16);
+        else
+            zs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(zb, ev * 4u, 0, 0));
+        nws = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            raw_buffer(const_cast<float *>(P.norm_w), norm ? DV * 4u : 0u), ev * 4u, 0, 0));
+    }
+    // the state block, last (zeros without a state)
+    __builtin_amdgcn_sched_barrier(0);
+    float4 s[RPT];
     {
-        const float rate = P.gates.rate[h], bias = P.gates.bias[h];
-        gi = P.gates.raw ? gate_g(gi, bias, rate) : gi;
-        bi = P.gates.raw ? gate_beta(bi) : bi;
+        const auto sb = raw_buffer(sin >= 0 ? const_cast<float *>(P.state_in + (int64_t)sin * P.slot_stride +
+                                                                  (int64_t)h * DK * DV)
+                                            : nullptr,
+                                   sin >= 0 ? (uint32_t)(DK * DV * 4) : 0u);
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) s[r] = buf_load_f4(sb, (uint32_t)(((rg + r * RG) * DV + col) * 4));
     }
-    const E *vp = v + (int64_t)i * P.rs_v + (int64_t)h * DV + col;
-    float vv[4] = {to_f32(vp[0]), to_f32(vp[1]), to_f32(vp[2]), to_f32(vp[3])};
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. gates and prologue, while the state streams in
+    gi = P.gates.raw ? gate_g(gi, bias, rate) : gi;
+    bi = P.gates.raw ? gate_beta(bi) : bi;
+    float4 nqk = make_float4(0.f, 0.f, 0.f, 0.f), nvv = nqk;
     if (conv) {
-        const int64_t ch0 = 2 * (int64_t)P.H_k * DK + (int64_t)h * DV + col;
-        float hv[12];
-        conv_hist4(P, sin, ch0, hv);
-        const float4 *wp = reinterpret_cast<const float4 *>(P.conv_w + ch0 * 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            nv[3 * j] = hv[3 * j + 1];
-            nv[3 * j + 1] = hv[3 * j + 2];
-            nv[3 * j + 2] = vv[j];
-            vv[j] = conv1(wp[j], hv[3 * j], hv[3 * j + 1], hv[3 * j + 2], vv[j]);
-        }
+        const float h0 = __uint_as_float(hq.x), h1 = __uint_as_float(hq.y), h2 = __uint_as_float(hq.z);
+        nqk = make_float4(h1, h2, x, 0.f);
+        x = conv1(wq, h0, h1, h2, x);
+        const float g0 = __uint_as_float(hv.x), g1 = __uint_as_float(hv.y), g2 = __uint_as_float(hv.z);
+        nvv = make_float4(g1, g2, xv, 0.f);
+        xv = conv1(wv, g0, g1, g2, xv);
     }
-    float zz[4] = {0.f, 0.f, 0.f, 0.f}, nw[4] = {0.f, 0.f, 0.f, 0.f};
-    if (norm) {
-        const E *zp = static_cast<const E *>(P.z) + ((int64_t)i * P.H_v + h) * DV + col;
-        const float4 w4 = *reinterpret_cast<const float4 *>(P.norm_w + col);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) zz[j] = to_f32(zp[j]);
-        nw[0] = w4.x; nw[1] = w4.y; nw[2] = w4.z; nw[3] = w4.w;
-    }
-    if (conv && P.conv_out) {
-        // every thread's loads of the old convolution state are complete
-        // (this barrier waits for them), so each group's v channels and the
-        // key head's q and k channels take their new state; no other
-        // workgroup reads them
-        __syncthreads();
-        if (sout >= 0) {
-            float *cs = P.conv_out + (int64_t)sout * P.slot_stride;
-            if (rg == 0) {
-                float4 *vp4 = reinterpret_cast<float4 *>(cs + (2 * (int64_t)P.H_k * DK + (int64_t)h * DV + col) * 3);
-                vp4[0] = make_float4(nv[0], nv[1], nv[2], nv[3]);
-                vp4[1] = make_float4(nv[4], nv[5], nv[6], nv[7]);
-                vp4[2] = make_float4(nv[8], nv[9], nv[10], nv[11]);
-            }
-            if (grp == 0 && tid < 2 * DK) {
-                const int64_t ch = (tid < DK ? (int64_t)P.H_k * DK + tid : (int64_t)(tid - DK)) + (int64_t)kh * DK;
-                cs[ch * 3] = nqk.x;
-                cs[ch * 3 + 1] = nqk.y;
-                cs[ch * 3 + 2] = nqk.z;
-            }
+    if (tid < 2 * DK) (isk ? sk : sq)[e] = x;
+    if constexpr (FUSED) {
+        if (tid < DV) {
+            sv_[grp][ev] = xv;
+            sz_[grp][ev] = norm ? nws * silu(zs) : 0.f;
         }
+        // this thread's reads of the old convolution state are complete
+        // before the barrier (x and xv are formed from them): after it, each
+        // group's v channels and the key head's q and k channels take their
+        // new state (no other workgroup reads them); lanes that do not write
+        // get an offset past the range
+        loaded(x);
+        loaded(xv);
+        lds_sync();
+        const bool wr = conv && P.conv_out && sout >= 0;
+        const auto cb = raw_buffer(wr ? P.conv_out + (int64_t)sout * P.slot_stride : nullptr,
+                                   wr ? (uint32_t)conv_dim * 12u : 0u);
+        const uint32_t vo = tid < DV ? (uint32_t)chv * 12u : kDropOffset;
+        __builtin_amdgcn_raw_buffer_store_b96(
+            u32x3{__float_as_uint(nvv.x), __float_as_uint(nvv.y), __float_as_uint(nvv.z)}, cb, vo, 0, 0);
+        const uint32_t qo = grp == 0 && tid < 2 * DK ? (uint32_t)ch * 12u : kDropOffset;
+        __builtin_amdgcn_raw_buffer_store_b96(
+            u32x3{__float_as_uint(nqk.x), __float_as_uint(nqk.y), __float_as_uint(nqk.z)}, cb, qo, 0, 0);
+        const float4 v4 = *reinterpret_cast<const float4 *>(&sv_[grp][col]);
+        vv[0] = v4.x; vv[1] = v4.y; vv[2] = v4.z; vv[3] = v4.w;
     } else {
         lds_sync();
     }
@@ -286,7 +347,11 @@ __global__ __launch_bounds__(kDecodeThreads * GR) void decode_kernel(RecParams P
     d.w = bi * (vv[3] - dk_ * tk.w);
     const float dq = dec * rq, kqh = rk * rq * kq;
     float o[4] = {dq * tq.x + kqh * d.x, dq * tq.y + kqh * d.y, dq * tq.z + kqh * d.z, dq * tq.w + kqh * d.w};
-    if (norm) gated_norm_row<CG, DV>(o, zz, nw, P.eps);
+    if (norm) {
+        const float4 z4 = *reinterpret_cast<const float4 *>(&sz_[grp][col]);
+        const float zg[4] = {z4.x, z4.y, z4.z, z4.w};
+        gated_norm_row<CG, DV>(o, zg, P.eps);
+    }
 
     if (rg == 0) {
         OT *op = static_cast<OT *>(P.out) + ((int64_t)i * P.H_v + h) * DV + col;
@@ -515,7 +580,12 @@ __global__ __launch_bounds__(kDecodeThreads * GR) void decode_multi_kernel(RecPa
         const float dq = dec * rq, kqh = rk * rq * kq;
         float o[4] = {dq * tq.x + kqh * d.x, dq * tq.y + kqh * d.y, dq * tq.z + kqh * d.z,
                       dq * tq.w + kqh * d.w};
-        if (norm) gated_norm_row<CG, DV>(o, cur.zz, nw, P.eps);
+        if (norm) {
+            float zg[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) zg[j] = nw[j] * silu(cur.zz[j]);
+            gated_norm_row<CG, DV>(o, zg, P.eps);
+        }
         {
             // row group 0 writes the row; the other lanes' offsets fall past
             // the buffer's end and are dropped.  No branch: a store inside one

@@ -8,6 +8,8 @@ namespace gdn {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // raw 16-byte word
+typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));   // raw 12-byte word
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));   // raw 8-byte word
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
