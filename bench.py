@@ -72,9 +72,9 @@ C = 64
 PREFILL_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
                for f in ("gdn_prefill.hip", "gdn_mfma.h", "gdn_device.h", "gdn_internal.h")]
 MEASURED_TRAFFIC = {
-    "source_sha256": "ba591a3a9e070a8af89fa40beee94859e76b484d2be4e9d41653c2425db1975a",
+    "source_sha256": "abcab3b5cbe8557a567a9eaa3e290476381c7f6b20062549762f57b3719acf76",
     "scan": (83638.5 * 2.000 + 67584.0 * 1.000) * 1024,
-    "prepare": (42070.5 * 2.000 + 165281.4 * 1.000) * 1024,
+    "prepare": (42074.3 * 2.000 + 165270.9 * 1.000) * 1024,
 }
 
 
@@ -83,8 +83,8 @@ MEASURED_TRAFFIC = {
 DECODE_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
               for f in ("gdn_decode.hip", "gdn_device.h", "gdn_internal.h")]
 MEASURED_DECODE_TRAFFIC = {
-    "source_sha256": "4219dcbb20d0a97c00b51a8780f0dfd6711f158def44fd6575a557d0f0c3c0ef",
-    "decode": (66132.1 * 2.000 + 132096.0 * 1.000) * 1024,
+    "source_sha256": "29c6ff040a584a0d8d09fdabf2fdb6b34938c1ac6d4d4b50e39094345de49ac8",
+    "decode": (66151.2 * 2.000 + 132096.0 * 1.000) * 1024,
 }
 
 

@@ -82,34 +82,6 @@ __device__ __forceinline__ float conv1(float4 w, float h0, float h1, float h2, f
     return silu(w.x * h0 + w.y * h1 + w.z * h2 + w.w * x);
 }
 
-// The three stored inputs of channel ch (zero without a state).
-__device__ __forceinline__ void conv_hist(const RecParams &P, int sin, int64_t ch, float &h0, float &h1,
-                                          float &h2)
-{
-    h0 = h1 = h2 = 0.f;
-    if (sin >= 0) {
-        const float *hp = P.conv_in + (int64_t)sin * P.slot_stride + ch * 3;
-        h0 = hp[0];
-        h1 = hp[1];
-        h2 = hp[2];
-    }
-}
-
-// Four consecutive channels from ch0 (a multiple of 4): 12 stored inputs.
-__device__ __forceinline__ void conv_hist4(const RecParams &P, int sin, int64_t ch0, float hv[12])
-{
-#pragma unroll
-    for (int j = 0; j < 12; ++j) hv[j] = 0.f;
-    if (sin >= 0) {
-        const float4 *hp = reinterpret_cast<const float4 *>(P.conv_in + (int64_t)sin * P.slot_stride + ch0 * 3);
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            const float4 x = hp[j];
-            hv[4 * j] = x.x; hv[4 * j + 1] = x.y; hv[4 * j + 2] = x.z; hv[4 * j + 3] = x.w;
-        }
-    }
-}
-
 // Gated RMSNorm of a row spread over CG consecutive lanes, four values each;
 // zg = w * silu(z) of the same four columns.
 template <int CG, int DV>
@@ -381,8 +353,8 @@ __global__ __launch_bounds__(kDecodeThreads * GR, 4) void decode_kernel(RecParam
 // once per token.  q, k, v, g, beta (and z) of the next token are fetched
 // while the current one is processed; k, q and the reduction partials
 // alternate between two LDS buffers, so a token needs two barriers.  With the
-// prologue, each thread keeps the convolution window of its channels in
-// registers from token to token.  FUSED (here and in decode_kernel):
+// prologue, each thread keeps the convolution window of its q or k channel
+// and of its v channel in registers from token to token.  FUSED (here and in decode_kernel):
 // prologue and/or epilogue present; the plain instantiation carries none of
 // their code or registers.
 // Sum over the row groups of one wave: lanes that hold the same column group
@@ -431,6 +403,9 @@ __global__ __launch_bounds__(kDecodeThreads * GR) void decode_multi_kernel(RecPa
     __shared__ float sq_[GR][2][DK];
     constexpr int NW = kDecodeThreads / 64;
     __shared__ float4 red_[GR][2][2][NW][CG];
+    // fused: v after the prologue and w * silu(z) of a token, per channel
+    __shared__ __attribute__((aligned(16))) float sv_[FUSED ? GR : 1][2][FUSED ? DV : 1];
+    __shared__ __attribute__((aligned(16))) float sz_[FUSED ? GR : 1][2][FUSED ? DV : 1];
     float(&sk)[2][DK] = sk_[grp];
     float(&sq)[2][DK] = sq_[grp];
     float4(&red)[2][2][NW][CG] = red_[grp];
@@ -441,8 +416,88 @@ __global__ __launch_bounds__(kDecodeThreads * GR) void decode_multi_kernel(RecPa
     const int sin = P.state_in ? P.slot_in[i] : -1;
     const int sout = P.slot_out[i];
 
+    // this thread's channels: one q or k channel of the key head (threads
+    // past 2 DK repeat one) and, fused, one v channel (threads past DV repeat
+    // one); plain, four v columns
+    const int e2 = tid % (2 * DK);
+    const bool isk = e2 < DK;
+    const int e = isk ? e2 : e2 - DK;
+    const int ev = tid % DV;
+    const int conv_dim = 2 * P.H_k * DK + P.H_v * DV;
+    const int64_t chq = (isk ? (int64_t)P.H_k * DK : 0) + (int64_t)kh * DK + e;
+    const int64_t chv = 2 * (int64_t)P.H_k * DK + (int64_t)h * DV + ev;
+
+    // Order of memory operations as in decode_kernel: the prologue's taps and
+    // stored inputs, the norm weight and the first token are loaded before
+    // the state block, and a token's inputs are only fetched (the gate
+    // activations are applied when the token is processed), so the next
+    // token's loads stay in flight while the current one is processed.
+    u32x3 hq3 = {0u, 0u, 0u}, hv3 = {0u, 0u, 0u};
+    float4 wq = make_float4(0.f, 0.f, 0.f, 0.f), wv = wq;
+    float nws = 0.f;
+    if constexpr (FUSED) {
+        const bool hist = conv && sin >= 0;
+        const auto hb = raw_buffer(hist ? const_cast<float *>(P.conv_in + (int64_t)sin * P.slot_stride) : nullptr,
+                                   hist ? (uint32_t)conv_dim * 12u : 0u);
+        const auto tbuf = raw_buffer(const_cast<float *>(P.conv_w), conv ? (uint32_t)conv_dim * 16u : 0u);
+        hq3 = __builtin_amdgcn_raw_buffer_load_b96(hb, (uint32_t)chq * 12u, 0, 0);
+        wq = buf_load_f4(tbuf, (uint32_t)chq * 16u);
+        hv3 = __builtin_amdgcn_raw_buffer_load_b96(hb, (uint32_t)chv * 12u, 0, 0);
+        wv = buf_load_f4(tbuf, (uint32_t)chv * 16u);
+        nws = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            raw_buffer(const_cast<float *>(P.norm_w), norm ? DV * 4u : 0u), ev * 4u, 0, 0));
+    }
+
+    // a token's inputs for this thread: its q or k value, v (fused: its
+    // channel and z; plain: four columns), and the raw g and beta
+    struct Tok {
+        float kq, gt, bt;
+        float vv[4];
+        float zs;
+    };
+    auto fetch = [&](int t) {
+        Tok r;
+        r.kq = to_f32((isk ? k : q)[(int64_t)t * P.rs_qk + (int64_t)kh * DK + e]);
+        r.gt = P.g[(int64_t)t * P.H_v + h];
+        r.bt = P.beta[(int64_t)t * P.H_v + h];
+        const E *vrow = v + (int64_t)t * P.rs_v + (int64_t)h * DV;
+        if constexpr (FUSED) {
+            r.vv[0] = to_f32(vrow[ev]);
+            r.vv[1] = r.vv[2] = r.vv[3] = 0.f;
+            const E *zrow = norm ? static_cast<const E *>(P.z) + ((int64_t)t * P.H_v + h) * DV : nullptr;
+            const auto zb = raw_buffer(const_cast<E *>(zrow), norm ? DV * sizeof(E) : 0u);
+            if constexpr (sizeof(E) == 2)
+                r.zs = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(zb, ev * 2u, 0, 0) << 16);
+            else
+                r.zs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(zb, ev * 4u, 0, 0));
+        } else {
+            buf_load4<E>(raw_buffer(const_cast<E *>(vrow), DV * sizeof(E)), col * sizeof(E), r.vv);
+            r.zs = 0.f;
+        }
+        return r;
+    };
+    Tok cur{};
+    float rate = 0.f, bias = 0.f;
+    if (tb < te) {                              // an empty sequence reads no token
+        cur = fetch(tb);
+        rate = P.gates.rate[h];
+        bias = P.gates.bias[h];
+    }
+
+    // the state block, last.  Fused: through a buffer resource (zeros
+    // without a state, no branch).  Plain: global loads behind a branch; the
+    // buffer form would cost this instantiation about 20 registers and a
+    // wave per SIMD, more than the branch costs it.
+    __builtin_amdgcn_sched_barrier(0);
     float4 s[RPT];
-    if (sin >= 0) {
+    if constexpr (FUSED) {
+        const auto sb = raw_buffer(sin >= 0 ? const_cast<float *>(P.state_in + (int64_t)sin * P.slot_stride +
+                                                                  (int64_t)h * DK * DV)
+                                            : nullptr,
+                                   sin >= 0 ? (uint32_t)(DK * DV * 4) : 0u);
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) s[r] = buf_load_f4(sb, (uint32_t)(((rg + r * RG) * DV + col) * 4));
+    } else if (sin >= 0) {
         const float *base = P.state_in + (int64_t)sin * P.slot_stride + (int64_t)h * DK * DV + col;
 #pragma unroll
         for (int r = 0; r < RPT; ++r)
@@ -451,85 +506,40 @@ __global__ __launch_bounds__(kDecodeThreads * GR) void decode_multi_kernel(RecPa
 #pragma unroll
         for (int r = 0; r < RPT; ++r) s[r] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // prologue: taps and stored inputs of this thread's k or q channel and of
-    // its four v channels
-    const bool isk = tid < DK;
-    const int64_t chq = (isk ? (int64_t)P.H_k * DK : 0) + (int64_t)kh * DK + (isk ? tid : tid - DK);
-    const int64_t chv = 2 * (int64_t)P.H_k * DK + (int64_t)h * DV + col;
-    float4 wq = make_float4(0.f, 0.f, 0.f, 0.f), wv[4];
-    float hq[3] = {0.f, 0.f, 0.f}, hv[12];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wv[j] = wq;
-#pragma unroll
-    for (int j = 0; j < 12; ++j) hv[j] = 0.f;
-    if (conv) {
-        if (tid < 2 * DK) {
-            wq = *reinterpret_cast<const float4 *>(P.conv_w + chq * 4);
-            conv_hist(P, sin, chq, hq[0], hq[1], hq[2]);
-        }
-        const float4 *wp = reinterpret_cast<const float4 *>(P.conv_w + chv * 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wv[j] = wp[j];
-        conv_hist4(P, sin, chv, hv);
-    }
-    float nw[4] = {0.f, 0.f, 0.f, 0.f};
-    if (norm) {
-        const float4 w4 = *reinterpret_cast<const float4 *>(P.norm_w + col);
-        nw[0] = w4.x; nw[1] = w4.y; nw[2] = w4.z; nw[3] = w4.w;
-    }
-
-    // this thread's share of a token: one of k (tid < DK) or q (DK <= tid <
-    // 2 DK), four values of v (and of z), and the token's g and beta
-    struct Tok {
-        float kq, gt, bt;
-        float vv[4], zz[4];
-    };
-    auto fetch = [&](int t) {
-        Tok r;
-        const int64_t qk_off = (int64_t)t * P.rs_qk + (int64_t)kh * DK;
-        r.kq = tid < DK ? to_f32(k[qk_off + tid]) : tid < 2 * DK ? to_f32(q[qk_off + tid - DK]) : 0.f;
-        r.gt = P.g[(int64_t)t * P.H_v + h];
-        r.bt = P.beta[(int64_t)t * P.H_v + h];
-        const float rate = P.gates.rate[h], bias = P.gates.bias[h];
-        r.gt = P.gates.raw ? gate_g(r.gt, bias, rate) : r.gt;
-        r.bt = P.gates.raw ? gate_beta(r.bt) : r.bt;
-        const E *vp = v + (int64_t)t * P.rs_v + (int64_t)h * DV + col;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) r.vv[j] = to_f32(vp[j]);
-        // z (read from v, same layout, when there is no epilogue: an
-        // unconditional load keeps the compiler's count of loads exact)
-        if constexpr (FUSED) {
-            const E *zp = norm ? static_cast<const E *>(P.z) + ((int64_t)t * P.H_v + h) * DV + col
-                               : v + (int64_t)t * P.rs_v + (int64_t)h * DV + col;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) r.zz[j] = to_f32(zp[j]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) r.zz[j] = 0.f;
-        }
-        return r;
-    };
-    Tok cur{};
-    if (tb < te) cur = fetch(tb);               // an empty sequence reads no token
+    // convolution windows: the last three inputs of each channel
+    float hq[3] = {__uint_as_float(hq3.x), __uint_as_float(hq3.y), __uint_as_float(hq3.z)};
+    float hv[3] = {__uint_as_float(hv3.x), __uint_as_float(hv3.y), __uint_as_float(hv3.z)};
 
     for (int t = tb; t < te; ++t) {
         const int b = (t - tb) & 1;
+        const float gt = P.gates.raw ? gate_g(cur.gt, bias, rate) : cur.gt;
+        const float bt = P.gates.raw ? gate_beta(cur.bt) : cur.bt;
         float kqv = cur.kq;
-        float vv[4] = {cur.vv[0], cur.vv[1], cur.vv[2], cur.vv[3]};
         if (conv) {
             kqv = conv1(wq, hq[0], hq[1], hq[2], cur.kq);
             hq[0] = hq[1]; hq[1] = hq[2]; hq[2] = cur.kq;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                vv[j] = conv1(wv[j], hv[3 * j], hv[3 * j + 1], hv[3 * j + 2], cur.vv[j]);
-                hv[3 * j] = hv[3 * j + 1]; hv[3 * j + 1] = hv[3 * j + 2]; hv[3 * j + 2] = cur.vv[j];
+        }
+        if (tid < 2 * DK) (isk ? sk[b] : sq[b])[e] = kqv;
+        if constexpr (FUSED) {
+            float xv = cur.vv[0];
+            if (conv) {
+                xv = conv1(wv, hv[0], hv[1], hv[2], cur.vv[0]);
+                hv[0] = hv[1]; hv[1] = hv[2]; hv[2] = cur.vv[0];
+            }
+            if (tid < DV) {
+                sv_[grp][b][ev] = xv;
+                sz_[grp][b][ev] = norm ? nws * silu(cur.zs) : 0.f;
             }
         }
-        if (tid < DK) sk[b][tid] = kqv;
-        else if (tid < 2 * DK) sq[b][tid - DK] = kqv;
         const Tok nxt = fetch(min(t + 1, te - 1));
         lds_sync();
+        float vv[4] = {cur.vv[0], cur.vv[1], cur.vv[2], cur.vv[3]};
+        if constexpr (FUSED) {
+            const float4 v4 = *reinterpret_cast<const float4 *>(&sv_[grp][b][col]);
+            vv[0] = v4.x; vv[1] = v4.y; vv[2] = v4.z; vv[3] = v4.w;
+        }
 
         // norms (every wave reduces redundantly; no extra barrier)
         float kk = 0.f, qq = 0.f, kq = 0.f;
@@ -570,20 +580,19 @@ __global__ __launch_bounds__(kDecodeThreads * GR) void decode_multi_kernel(RecPa
         }
 
         // delta rule and read-out
-        const float dec = expf(cur.gt);
+        const float dec = expf(gt);
         const float dk_ = dec * rk;
         float4 d;
-        d.x = cur.bt * (vv[0] - dk_ * tk.x);
-        d.y = cur.bt * (vv[1] - dk_ * tk.y);
-        d.z = cur.bt * (vv[2] - dk_ * tk.z);
-        d.w = cur.bt * (vv[3] - dk_ * tk.w);
+        d.x = bt * (vv[0] - dk_ * tk.x);
+        d.y = bt * (vv[1] - dk_ * tk.y);
+        d.z = bt * (vv[2] - dk_ * tk.z);
+        d.w = bt * (vv[3] - dk_ * tk.w);
         const float dq = dec * rq, kqh = rk * rq * kq;
         float o[4] = {dq * tq.x + kqh * d.x, dq * tq.y + kqh * d.y, dq * tq.z + kqh * d.z,
                       dq * tq.w + kqh * d.w};
         if (norm) {
-            float zg[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) zg[j] = nw[j] * silu(cur.zz[j]);
+            const float4 z4 = *reinterpret_cast<const float4 *>(&sz_[grp][b][col]);
+            const float zg[4] = {z4.x, z4.y, z4.z, z4.w};
             gated_norm_row<CG, DV>(o, zg, P.eps);
         }
         {
@@ -593,7 +602,7 @@ __global__ __launch_bounds__(kDecodeThreads * GR) void decode_multi_kernel(RecPa
             // too (on gfx9 stores and loads share the counter).
             const __amdgpu_buffer_rsrc_t ob =
                 raw_buffer(static_cast<OT *>(P.out) + ((int64_t)t * P.H_v + h) * DV, (uint32_t)(DV * sizeof(OT)));
-            const uint32_t off = rg == 0 ? (uint32_t)(col * sizeof(OT)) : 0x80000000u;
+            const uint32_t off = rg == 0 ? (uint32_t)(col * sizeof(OT)) : kDropOffset;
 #pragma unroll
             for (int j = 0; j < 4; ++j) buffer_store(from_f32<OT>(o[j]), ob, off + (uint32_t)(j * sizeof(OT)));
         }
@@ -609,33 +618,35 @@ __global__ __launch_bounds__(kDecodeThreads * GR) void decode_multi_kernel(RecPa
         cur = nxt;
     }
 
+    if constexpr (FUSED) {
+        if (conv && P.conv_out) {
+            // The windows hold the last three inputs of each channel (the old
+            // state shifted by the sequence's rows): the new convolution
+            // state.  This thread's reads of the old state are complete
+            // before the barrier (the windows are formed from them); each
+            // group's v channels and the key head's q and k channels are read
+            // by no other workgroup.
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                loaded(hq[j]);
+                loaded(hv[j]);
+            }
+            lds_sync();
+            const auto cb = raw_buffer(sout >= 0 ? P.conv_out + (int64_t)sout * P.slot_stride : nullptr,
+                                       sout >= 0 ? (uint32_t)conv_dim * 12u : 0u);
+            const uint32_t vo = tid < DV ? (uint32_t)chv * 12u : kDropOffset;
+            __builtin_amdgcn_raw_buffer_store_b96(
+                u32x3{__float_as_uint(hv[0]), __float_as_uint(hv[1]), __float_as_uint(hv[2])}, cb, vo, 0, 0);
+            const uint32_t qo = grp == 0 && tid < 2 * DK ? (uint32_t)chq * 12u : kDropOffset;
+            __builtin_amdgcn_raw_buffer_store_b96(
+                u32x3{__float_as_uint(hq[0]), __float_as_uint(hq[1]), __float_as_uint(hq[2])}, cb, qo, 0, 0);
+        }
+    }
     if (sout >= 0) {
         float *base = P.state_out + (int64_t)sout * P.slot_stride + (int64_t)h * DK * DV + col;
 #pragma unroll
         for (int r = 0; r < RPT; ++r)
             *reinterpret_cast<float4 *>(base + (int64_t)(rg + r * RG) * DV) = s[r];
-    }
-    if (conv && P.conv_out) {
-        // The windows hold the last three inputs of each channel (the old
-        // state shifted by the sequence's rows): the new convolution state.
-        // Every thread's loads of the old state are complete past this
-        // barrier; each group's v channels and the key head's q and k
-        // channels are read by no other workgroup.
-        __syncthreads();
-        if (sout >= 0) {
-            float *cs = P.conv_out + (int64_t)sout * P.slot_stride;
-            if (rg == 0) {
-                float4 *vp4 = reinterpret_cast<float4 *>(cs + chv * 3);
-                vp4[0] = make_float4(hv[0], hv[1], hv[2], hv[3]);
-                vp4[1] = make_float4(hv[4], hv[5], hv[6], hv[7]);
-                vp4[2] = make_float4(hv[8], hv[9], hv[10], hv[11]);
-            }
-            if (grp == 0 && tid < 2 * DK) {
-                cs[chq * 3] = hq[0];
-                cs[chq * 3 + 1] = hq[1];
-                cs[chq * 3 + 2] = hq[2];
-            }
-        }
     }
 }
 
