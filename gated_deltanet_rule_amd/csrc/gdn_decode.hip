@@ -120,10 +120,6 @@ __device__ __forceinline__ void buf_store_f4(float4 v, __amdgpu_buffer_rsrc_t r,
     __builtin_amdgcn_raw_buffer_store_b128(
         u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)}, r, off, 0, 0);
 }
-// A buffer offset past every range used here: the hardware range check drops
-// a store to it (a lane that must not write gets this offset instead of a
-// branch around the store).
-constexpr uint32_t kDropOffset = 0x80000000u;
 // The loads that produced v are complete at this point of the program (the
 // compiler's wait for them is placed here); no code is emitted.
 __device__ __forceinline__ void loaded(float v) { asm volatile("" ::"v"(v)); }

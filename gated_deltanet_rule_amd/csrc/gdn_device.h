@@ -48,6 +48,10 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
 }
+// A buffer offset past every range used here: a load from it reads zero and
+// a store to it is dropped (a lane that must not access memory gets this
+// offset instead of a branch around the access).
+constexpr uint32_t kDropOffset = 0x80000000u;
 __device__ __forceinline__ void buffer_store(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }

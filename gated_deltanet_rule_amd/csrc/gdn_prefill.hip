@@ -418,6 +418,16 @@ __device__ __forceinline__ float conv_silu4(float4 w, float x0, float x1, float 
     return silu(w.x * x0 + w.y * x1 + w.z * x2 + w.w * x3);
 }
 
+// Raw fp32 bits of one element of E through a buffer resource (zero past the
+// range's end).
+template <typename E> __device__ __forceinline__ uint32_t buf_bits(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <> __device__ __forceinline__ uint32_t buf_bits<bf16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0) << 16;
+}
+template <> __device__ __forceinline__ uint32_t buf_bits<float>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
 // The VEC values of a 16-byte vector as fp32, and back (rounded to E).
 template <typename E> __device__ __forceinline__ void unpack16(u32x4 u, float *f);
 template <> __device__ __forceinline__ void unpack16<bf16_t>(u32x4 u, float *f) {
@@ -563,17 +573,17 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     // outstanding memory operations, and the next wait for it then also waits
     // for every store issued before.  A wave past the last head repeats the
     // last one (identical values written twice).
-    float gq = 0.f, bq = 0.f;
+    // The raw gate activations are applied in head_scalars, where the values
+    // are used: applied here, they would make the loads' first wait a wait
+    // for every load issued before them.
+    float gq = 0.f, bq = 0.f, grate = 0.f, gbias = 0.f;
     const int lrow = min(lane, len - 1);
     auto load_gb = [&](int j0) {
         const int hh = kh * ratio + min(j0 + w, ratio - 1);
-        float gl = pp.g[(size_t)(t0 + lrow) * pp.H_v + hh];
-        float bl = pp.beta[(size_t)(t0 + lrow) * pp.H_v + hh];
-        const float rate = pp.gates.rate[hh], bias = pp.gates.bias[hh];
-        gl = pp.gates.raw ? gate_g(gl, bias, rate) : gl;
-        bl = pp.gates.raw ? gate_beta(bl) : bl;
-        gq = lane < len ? gl : 0.f;
-        bq = lane < len ? bl : 0.f;
+        gq = pp.g[(size_t)(t0 + lrow) * pp.H_v + hh];
+        bq = pp.beta[(size_t)(t0 + lrow) * pp.H_v + hh];
+        grate = pp.gates.rate[hh];
+        gbias = pp.gates.bias[hh];
     };
     // cumulative log-decay (fp64) and the per-row scalars of those heads
     auto head_scalars = [&](int j0) {
@@ -582,7 +592,11 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
         float *scal = reinterpret_cast<float *>(pp.vblocks + ((size_t)slot * pp.H_v + hh) * ((size_t)G::VBLK * 1024) +
                                                 G::F_SCAL * 1024);
         const int r = lane;
-        double Gc = gq;
+        const float gl = pp.gates.raw ? gate_g(gq, gbias, grate) : gq;
+        const float bl = pp.gates.raw ? gate_beta(bq) : bq;
+        const float gv = lane < len ? gl : 0.f;
+        const float bv = lane < len ? bl : 0.f;
+        double Gc = gv;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const double y = __shfl_up(Gc, off, 64);
@@ -592,9 +606,9 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
         const float rk = sRK[r];
         const float eG = expf((float)Gc);
         sGh[hs * C + r] = Gc;
-        sRAh[hs * C + r] = bq * rk;
-        sBetah[hs * C + r] = bq;
-        sColh[hs * C + r] = bq * eG * rk;
+        sRAh[hs * C + r] = bv * rk;
+        sBetah[hs * C + r] = bv;
+        sColh[hs * C + r] = bv * eG * rk;
         scal[r] = sRQ[r] * eG;                              // qs: q scale * e^{G_r}
         scal[64 + r] = rk * expf((float)(Gn - Gc));         // ks: e^{G_n - G_r} / |k_r|
         // gn = e^{G_n}, the chunk's first token and length (int bits): lanes
@@ -611,6 +625,10 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
         state_ok = pp.has_state && s_in >= 0;
         cslot = state_ok ? s_in : 0;
     }
+    // the slot's stored convolution inputs, read only for a sequence's first
+    // chunk (an empty range otherwise, and without a state)
+    const auto hs = raw_buffer(const_cast<float *>(pp.conv_in) + (size_t)cslot * pp.slot_stride,
+                               CONV && first && state_ok ? (uint32_t)(2 * pp.H_k * DK + pp.H_v * DV) * 12u : 0u);
     const size_t vch0 = 2 * (size_t)pp.H_k * DK;          // first v channel of the mixed rows
 
     // V rows of one value head, loaded one head ahead into registers (with
@@ -640,13 +658,18 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
                 const int rr = min(vrow0 + p, len - 1);
                 vpre[p] = load_once(vg + (size_t)(t0 + rr) * pp.rs_v + (size_t)hh * DV + vcv * VEC);
             }
+            // history: the three rows before the chunk, or for a sequence's
+            // first chunk the slot's stored inputs (see the K and Q history)
+            const auto hr = raw_buffer(const_cast<E *>(vg) + (first ? 0 : (size_t)(t0 - 3) * pp.rs_v),
+                                       first ? 0u : 3u * (uint32_t)pp.rs_v * (uint32_t)sizeof(E));
 #pragma unroll
             for (int j = 0; j < NHV; ++j) {
                 const int idx = min(tid + 256 * j, 3 * DV - 1);
                 const int m = idx / DV, c = idx % DV;
-                const float xr = to_f32(vg[(size_t)max(t0 - 3 + m, 0) * pp.rs_v + (size_t)hh * DV + c]);
-                const float xs = pp.conv_in[(size_t)cslot * pp.slot_stride + (vch0 + (size_t)hh * DV + c) * 3 + m];
-                vh[j] = first ? (state_ok ? xs : 0.f) : xr;
+                const uint32_t br = buf_bits<E>(hr, (uint32_t)((size_t)m * pp.rs_v + (size_t)hh * DV + c) * sizeof(E));
+                const uint32_t bs = __builtin_amdgcn_raw_buffer_load_b32(
+                    hs, (uint32_t)((vch0 + (size_t)hh * DV + c) * 3 + m) * 4u, 0, 0);
+                vh[j] = __uint_as_float(br | bs);
             }
 #pragma unroll
             for (int j = 0; j < NWV; ++j)
@@ -682,17 +705,29 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
             kraw[u] = load_once(kg + off);
             qraw[u] = load_once(qg + off);
         }
-        // three history rows of the key head's q and k channels, [m][q | k]
+        // three history rows of the key head's q and k channels, [m][q | k]:
+        // the rows before the chunk, or for a sequence's first chunk the
+        // slot's stored inputs (zero without a state).  Each is read through a
+        // buffer range that is empty when it does not apply (reads as zero
+        // bits) and the raw bits are or-ed: a select between two loads on a
+        // uniform condition is compiled into a branch around each load, and
+        // each branch then ends in a wait for every load issued before it.
+        const uint32_t rbytes = first ? 0u : 3u * (uint32_t)pp.rs_qk * (uint32_t)sizeof(E);
+        const size_t rrow = first ? 0 : (size_t)(t0 - 3) * pp.rs_qk;
+        const auto hq = raw_buffer(const_cast<E *>(qg) + rrow, rbytes);
+        const auto hkb = raw_buffer(const_cast<E *>(kg) + rrow, rbytes);
 #pragma unroll
         for (int j = 0; j < NHK; ++j) {
             const int idx = min(tid + 256 * j, 6 * DK - 1);
             const int m = idx / (2 * DK), c2 = idx % (2 * DK);
             const bool isk = c2 >= DK;
             const int c = isk ? c2 - DK : c2;
-            const float xr = to_f32((isk ? kg : qg)[(size_t)max(t0 - 3 + m, 0) * pp.rs_qk + (size_t)kh * DK + c]);
+            const uint32_t ro = (uint32_t)((size_t)m * pp.rs_qk + (size_t)kh * DK + c) * sizeof(E);
+            const uint32_t bq = buf_bits<E>(hq, isk ? kDropOffset : ro);
+            const uint32_t bk = buf_bits<E>(hkb, isk ? ro : kDropOffset);
             const size_t ch = (isk ? (size_t)pp.H_k * DK : 0) + (size_t)kh * DK + c;
-            const float xs = pp.conv_in[(size_t)cslot * pp.slot_stride + ch * 3 + m];
-            hk[j] = first ? (state_ok ? xs : 0.f) : xr;
+            const uint32_t bs = __builtin_amdgcn_raw_buffer_load_b32(hs, (uint32_t)(ch * 3 + m) * 4u, 0, 0);
+            hk[j] = __uint_as_float(bq | bk | bs);
         }
         const float4 *wkp = reinterpret_cast<const float4 *>(pp.conv_w + ((size_t)pp.H_k * DK + (size_t)kh * DK + kcv * VEC) * 4);
         const float4 *wqp = reinterpret_cast<const float4 *>(pp.conv_w + ((size_t)kh * DK + kcv * VEC) * 4);
