@@ -72,9 +72,9 @@ C = 64
 PREFILL_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
                for f in ("gdn_prefill.hip", "gdn_mfma.h", "gdn_device.h", "gdn_internal.h")]
 MEASURED_TRAFFIC = {
-    "source_sha256": "abcab3b5cbe8557a567a9eaa3e290476381c7f6b20062549762f57b3719acf76",
+    "source_sha256": "ea6400b37575d24bce700a21b25afeabb8ae279cee056994600deb9474914e1a",
     "scan": (83638.5 * 2.000 + 67584.0 * 1.000) * 1024,
-    "prepare": (42074.3 * 2.000 + 165270.9 * 1.000) * 1024,
+    "prepare": (42067.1 * 2.000 + 165239.0 * 1.000) * 1024,
 }
 
 
@@ -83,8 +83,8 @@ MEASURED_TRAFFIC = {
 DECODE_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
               for f in ("gdn_decode.hip", "gdn_device.h", "gdn_internal.h")]
 MEASURED_DECODE_TRAFFIC = {
-    "source_sha256": "29c6ff040a584a0d8d09fdabf2fdb6b34938c1ac6d4d4b50e39094345de49ac8",
-    "decode": (66151.2 * 2.000 + 132096.0 * 1.000) * 1024,
+    "source_sha256": "c77fdcc74375bfb641f27d6b943d0239cb6c84232cb452332bd1fa9f24af6b32",
+    "decode": (66154.5 * 2.000 + 132096.0 * 1.000) * 1024,
 }
 
 
