@@ -112,8 +112,8 @@ template <> __device__ __forceinline__ void buf_load4<float>(__amdgpu_buffer_rsr
     f[2] = __uint_as_float(u.z);
     f[3] = __uint_as_float(u.w);
 }
-__device__ __forceinline__ float4 buf_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+__device__ __forceinline__ float4 buf_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+    const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
     return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
 }
 __device__ __forceinline__ void buf_store_f4(float4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -226,7 +226,8 @@ __global__ __launch_bounds__(kDecodeThreads * GR, 4) void decode_kernel(RecParam
                                             : nullptr,
                                    sin >= 0 ? (uint32_t)(DK * DV * 4) : 0u);
 #pragma unroll
-        for (int r = 0; r < RPT; ++r) s[r] = buf_load_f4(sb, (uint32_t)(((rg + r * RG) * DV + col) * 4));
+        for (int r = 0; r < RPT; ++r)   // one lane offset, the row step as the scalar offset
+            s[r] = buf_load_f4(sb, (uint32_t)((rg * DV + col) * 4), (uint32_t)(r * RG * DV * 4));
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -373,7 +374,7 @@ __device__ __forceinline__ float rg_wave_sum(float x)
 }
 
 template <int DK, int DV, typename E, typename OT, bool FUSED, int GR>
-__global__ __launch_bounds__(kDecodeThreads * GR) void decode_multi_kernel(RecParams P)
+__global__ __launch_bounds__(kDecodeThreads * GR, 4) void decode_multi_kernel(RecParams P)
 {
     constexpr int CG = DV / 4;                  // float4 column groups
     constexpr int RG = kDecodeThreads / CG;     // row groups
@@ -402,6 +403,15 @@ __global__ __launch_bounds__(kDecodeThreads * GR) void decode_multi_kernel(RecPa
     // fused: v after the prologue and w * silu(z) of a token, per channel
     __shared__ __attribute__((aligned(16))) float sv_[FUSED ? GR : 1][2][FUSED ? DV : 1];
     __shared__ __attribute__((aligned(16))) float sz_[FUSED ? GR : 1][2][FUSED ? DV : 1];
+    // fused: the taps of this group's q / k channels and v channels, and the
+    // norm weight, read per token (registers are what limit this kernel)
+    // (one slot per thread: each thread reads back only what it wrote)
+    __shared__ __attribute__((aligned(16))) float4 stq_[FUSED ? GR : 1][FUSED ? kDecodeThreads : 1];
+    __shared__ __attribute__((aligned(16))) float4 stv_[FUSED ? GR : 1][FUSED ? kDecodeThreads : 1];
+    __shared__ float snw_[FUSED ? GR : 1][FUSED ? kDecodeThreads : 1];
+    // the convolution windows (the last three inputs of the q or k channel
+    // and of the v channel), one slot per thread
+    __shared__ float shw_[FUSED ? GR : 1][FUSED ? 6 : 1][FUSED ? kDecodeThreads : 1];
     float(&sk)[2][DK] = sk_[grp];
     float(&sq)[2][DK] = sq_[grp];
     float4(&red)[2][2][NW][CG] = red_[grp];
@@ -492,7 +502,8 @@ __global__ __launch_bounds__(kDecodeThreads * GR) void decode_multi_kernel(RecPa
                                             : nullptr,
                                    sin >= 0 ? (uint32_t)(DK * DV * 4) : 0u);
 #pragma unroll
-        for (int r = 0; r < RPT; ++r) s[r] = buf_load_f4(sb, (uint32_t)(((rg + r * RG) * DV + col) * 4));
+        for (int r = 0; r < RPT; ++r)   // one lane offset, the row step as the scalar offset
+            s[r] = buf_load_f4(sb, (uint32_t)((rg * DV + col) * 4), (uint32_t)(r * RG * DV * 4));
     } else if (sin >= 0) {
         const float *base = P.state_in + (int64_t)sin * P.slot_stride + (int64_t)h * DK * DV + col;
 #pragma unroll
@@ -504,9 +515,29 @@ __global__ __launch_bounds__(kDecodeThreads * GR) void decode_multi_kernel(RecPa
     }
     __builtin_amdgcn_sched_barrier(0);
 
+    if constexpr (FUSED) {
+        stq_[grp][tid] = wq;
+        stv_[grp][tid] = wv;
+        snw_[grp][tid] = nws;
+    }
     // convolution windows: the last three inputs of each channel
-    float hq[3] = {__uint_as_float(hq3.x), __uint_as_float(hq3.y), __uint_as_float(hq3.z)};
-    float hv[3] = {__uint_as_float(hv3.x), __uint_as_float(hv3.y), __uint_as_float(hv3.z)};
+    if constexpr (FUSED) {
+        shw_[grp][0][tid] = __uint_as_float(hq3.x);
+        shw_[grp][1][tid] = __uint_as_float(hq3.y);
+        shw_[grp][2][tid] = __uint_as_float(hq3.z);
+        shw_[grp][3][tid] = __uint_as_float(hv3.x);
+        shw_[grp][4][tid] = __uint_as_float(hv3.y);
+        shw_[grp][5][tid] = __uint_as_float(hv3.z);
+    }
+    // fused: the per-head gate parameters in scalar registers (their loads
+    // were issued before the state block's branch-free loads, so this waits
+    // for nothing later; after the plain kernel's branch it would wait for
+    // the whole block)
+    // (the builtin takes an int: the bits pass through it, not the value)
+    if constexpr (FUSED) {
+        rate = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(rate)));
+        bias = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bias)));
+    }
 
     for (int t = tb; t < te; ++t) {
         const int b = (t - tb) & 1;
@@ -514,19 +545,21 @@ __global__ __launch_bounds__(kDecodeThreads * GR) void decode_multi_kernel(RecPa
         const float bt = P.gates.raw ? gate_beta(cur.bt) : cur.bt;
         float kqv = cur.kq;
         if (conv) {
-            kqv = conv1(wq, hq[0], hq[1], hq[2], cur.kq);
-            hq[0] = hq[1]; hq[1] = hq[2]; hq[2] = cur.kq;
+            const float h0 = shw_[grp][0][tid], h1 = shw_[grp][1][tid], h2 = shw_[grp][2][tid];
+            kqv = conv1(stq_[grp][tid], h0, h1, h2, cur.kq);
+            shw_[grp][0][tid] = h1; shw_[grp][1][tid] = h2; shw_[grp][2][tid] = cur.kq;
         }
         if (tid < 2 * DK) (isk ? sk[b] : sq[b])[e] = kqv;
         if constexpr (FUSED) {
             float xv = cur.vv[0];
             if (conv) {
-                xv = conv1(wv, hv[0], hv[1], hv[2], cur.vv[0]);
-                hv[0] = hv[1]; hv[1] = hv[2]; hv[2] = cur.vv[0];
+                const float h0 = shw_[grp][3][tid], h1 = shw_[grp][4][tid], h2 = shw_[grp][5][tid];
+                xv = conv1(stv_[grp][tid], h0, h1, h2, cur.vv[0]);
+                shw_[grp][3][tid] = h1; shw_[grp][4][tid] = h2; shw_[grp][5][tid] = cur.vv[0];
             }
             if (tid < DV) {
                 sv_[grp][b][ev] = xv;
-                sz_[grp][b][ev] = norm ? nws * silu(cur.zs) : 0.f;
+                sz_[grp][b][ev] = norm ? snw_[grp][tid] * silu(cur.zs) : 0.f;
             }
         }
         const Tok nxt = fetch(min(t + 1, te - 1));
@@ -622,8 +655,11 @@ __global__ __launch_bounds__(kDecodeThreads * GR) void decode_multi_kernel(RecPa
             // before the barrier (the windows are formed from them); each
             // group's v channels and the key head's q and k channels are read
             // by no other workgroup.
+            float hq[3], hv[3];
 #pragma unroll
             for (int j = 0; j < 3; ++j) {
+                hq[j] = shw_[grp][j][tid];
+                hv[j] = shw_[grp][3 + j][tid];
                 loaded(hq[j]);
                 loaded(hv[j]);
             }
