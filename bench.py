@@ -34,6 +34,7 @@ Alongside (same JSON line):
   layer_prefill the fused layer path (convolution prologue, raw gates, gated
                 RMSNorm epilogue) on the T=4096 prefill, one call.
   layer_decode  the fused layer path on the decode workload, per step.
+  layer_multi   the fused layer path on the 64 x 4 multi-token workload.
   cpu_baseline  the fp64 oracle (test infrastructure, never tuned) on the
                 same prefill workload, on this host's cores.
 The gates follow the workloads' recipe: beta = sigmoid(b) and
@@ -83,7 +84,7 @@ MEASURED_TRAFFIC = {
 DECODE_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
               for f in ("gdn_decode.hip", "gdn_device.h", "gdn_internal.h")]
 MEASURED_DECODE_TRAFFIC = {
-    "source_sha256": "c77fdcc74375bfb641f27d6b943d0239cb6c84232cb452332bd1fa9f24af6b32",
+    "source_sha256": "9a228384eae16c2b72501c7158070a4e043497644f56631e0ba49b61809a3679",
     "decode": (66154.5 * 2.000 + 132096.0 * 1.000) * 1024,
 }
 
@@ -528,6 +529,46 @@ def bench_layer_decode(gdn, dev, reps=3):
                        "launch: one workgroup per (sequence, key head))"}
 
 
+def bench_layer_multi(gdn, dev, tokens=4, reps=200):
+    """The fused layer path on the multi-token decode workload: 64 sequences x
+    `tokens` tokens in one gdn_recurrent_multi call with the prologue (mixed
+    rows, convolution state in the slot rows), raw gates and the epilogue,
+    bf16 out, slot rows in place."""
+    case = gi.make_case(f"layer_spec64x{tokens}", [tokens] * 64, dtype="bf16", seed=40 + tokens,
+                        final_gates=workload_gates, **gi.QWEN3_NEXT_HEADS)
+    L = gi.make_layer_inputs(case.total_tokens, case.pool.shape[0], case.H_k, case.H_v, case.d_k,
+                             case.d_v, "bf16", 40 + tokens)
+    d = _layer_dev(case, L, dev)
+    out = torch.empty((case.total_tokens, case.H_v, case.d_v), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    cv = (d["conv_w"], case.H_k, case.d_k)
+    call = lambda: gdn.decode_multi(d["qkv"], None, None, d["a"], d["b"], d["rows"], d["rows"], out,
+                                    d["cu"], d["slot_in"], d["slot_out"], stream=stream,
+                                    gates=(d["ssm_a"], d["ssm_dt"]), conv=cv, z=d["z"],
+                                    norm_w=d["norm_w"])
+    settle(call)
+    t = Timer(stream, 2)
+    torch.cuda.synchronize()
+    t.mark(0)
+    for r in range(reps):
+        call()
+    t.mark(1)
+    torch.cuda.synchronize()
+    ms = t.ms(0, 1) / reps
+    assert torch.isfinite(out.float()).all()
+    N, H_k, H_v, dk, dv, T = 64, case.H_k, case.H_v, case.d_k, case.d_v, case.total_tokens
+    conv_dim = 2 * H_k * dk + H_v * dv
+    # state and convolution state read and written; per token the mixed rows,
+    # z, the bf16 output and the raw gate projections
+    by = N * (H_v * dk * dv * 4 + conv_dim * 3 * 4) * 2 + T * (conv_dim * 2 + H_v * dv * 2 * 2 + H_v * 8)
+    gbs = by / (ms * 1e-3) / 1e9
+    return {"workload": f"fused layer multi-token decode: 64 sequences x {tokens} tokens, mixed bf16 rows "
+                        "-> conv(4) + SiLU, raw gates, gated RMSNorm, bf16 out, state + conv state in "
+                        "slot rows",
+            "ms_per_call": ms, "tokens_s": T / (ms * 1e-3), "bytes_per_call": by, "achieved_gbs": gbs,
+            "frac": gbs / PEAK_HBM_GBS, "kernels": "decode_multi_kernel (one launch per call)"}
+
+
 def bench_varlen(gdn, dev, reps=20):
     """The varlen batch as one gdn_chunked_prefill call (it runs as chunk
     ranges of about 64 chunks), and as the two split-phase calls (one range
@@ -704,7 +745,10 @@ def main():
         lp = bench_layer_prefill(gdn, dev)
         log("fused layer decode 64x128 ...")
         ld = bench_layer_decode(gdn, dev)
-        log(f"  {lp['ms_per_call']*1e3:.1f} us/call, {ld['ms_per_step']*1e3:.1f} us/step")
+        log("fused layer multi-token decode 64x4 ...")
+        lm = bench_layer_multi(gdn, dev)
+        log(f"  {lp['ms_per_call']*1e3:.1f} us/call, {ld['ms_per_step']*1e3:.1f} us/step, "
+            f"{lm['ms_per_call']*1e3:.1f} us/multi call")
         return
     if args.copy_mib:
         n = args.copy_mib << 18
@@ -751,6 +795,9 @@ def main():
         log("fused layer decode 64x128 ...")
         extra["layer_decode"] = bench_layer_decode(gdn, dev)
         log(f"  {extra['layer_decode']['ms_per_step']*1e3:.1f} us/step")
+        log("fused layer multi-token decode 64x4 ...")
+        extra["layer_multi"] = bench_layer_multi(gdn, dev)
+        log(f"  {extra['layer_multi']['ms_per_call']*1e3:.1f} us/call")
         log("varlen ...")
         extra["varlen"] = bench_varlen(gdn, dev)
         log(f"  {extra['varlen']['ms_per_call']*1e3:.0f} us/call "
