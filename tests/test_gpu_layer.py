@@ -268,3 +268,42 @@ def test_norm_only_bf16_output_is_rounded_once():
     the norm, so the only rounding is the final one."""
     case = gi.config1(2048)
     _prefill(case, _layer(case, 90), conv=False, heads=[3, 17], out_dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("tokens", [1, 3])
+@pytest.mark.parametrize("no_pool", [False, True])
+def test_fused_decode_fresh_slots(tokens, no_pool):
+    """The fused recurrent kernels at Qwen3-Next heads (two value heads per
+    workgroup, convolution state replaced in place by the workgroup): one
+    token per sequence through gdn_recurrent_step, three through
+    gdn_recurrent_multi.  Sequences whose input slot is -1, and with no input
+    pool every sequence, start from zero recurrent and convolution states
+    (both read through empty ranges); outputs are written to other slots.
+    Against the oracle with the same starting states."""
+    import gated_deltanet_rule_amd as gdn
+    case = gi.make_case("layer_fresh", [tokens] * 8, dtype="bf16", seed=95, n_slots=16,
+                        scatter_slots=True, **gi.QWEN3_NEXT_HEADS)
+    slot_in = case.slot_in.copy()
+    if no_pool:
+        slot_in[:] = -1
+    else:
+        slot_in[1] = slot_in[5] = -1
+    case = dataclasses.replace(case, slot_in=slot_in)
+    L = _layer(case, 95)
+    say(f"fused decode fresh slots: tokens={tokens} no_pool={no_pool}")
+    d = dev_layer(case, L)
+    out = torch.empty((case.total_tokens, case.H_v, case.d_v), dtype=torch.float32, device="cuda")
+    pool_out = d["pool"].clone()
+    pool_in = None if no_pool else d["pool"]
+    si = torch.from_numpy(slot_in).cuda()
+    args = dict(gates=(d["ssm_a"], d["ssm_dt"]), conv=(d["conv_w"], case.H_k, case.d_k), z=d["z"],
+                norm_w=d["norm_w"])
+    if tokens == 1:
+        gdn.decode_step(d["qkv"], None, None, d["raw_a"], d["raw_b"], pool_in, pool_out, out, si,
+                        d["slot_out"], **args)
+    else:
+        gdn.decode_multi(d["qkv"], None, None, d["raw_a"], d["raw_b"], pool_in, pool_out, out, d["cu"],
+                         si, d["slot_out"], **args)
+    torch.cuda.synchronize()
+    heads = [0, 17, 31]
+    compare_layer(case, L, out, pool_out, oracle_layer(case, L, raw_gates=True, heads=heads), heads=heads)
