@@ -687,7 +687,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     u32x4 kx[KL], qx[KL], kxl[SI ? KL : 1], qxl[SI ? KL : 1];
     u32x4 kraw[CONV ? KR : 1], qraw[CONV ? KR : 1];
     float hk[NHK];
-    float4 wk[CONV ? VEC : 1], wq[CONV ? VEC : 1];
+    float4 wt = make_float4(0.f, 0.f, 0.f, 0.f);   // CONV: this thread's float4 of the key head's taps
     if constexpr (!CONV) {
 #pragma unroll
         for (int p = 0; p < KL; ++p) {
@@ -729,12 +729,14 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
             const uint32_t bs = __builtin_amdgcn_raw_buffer_load_b32(hs, (uint32_t)(ch * 3 + m) * 4u, 0, 0);
             hk[j] = __uint_as_float(bq | bk | bs);
         }
-        const float4 *wkp = reinterpret_cast<const float4 *>(pp.conv_w + ((size_t)pp.H_k * DK + (size_t)kh * DK + kcv * VEC) * 4);
-        const float4 *wqp = reinterpret_cast<const float4 *>(pp.conv_w + ((size_t)kh * DK + kcv * VEC) * 4);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            wk[e] = wkp[e];
-            wq[e] = wqp[e];
+        // the taps of the key head's q and k channels ([q | k] x 4, 4 KiB at
+        // DK = 128), one float4 per thread and staged through LDS: every row
+        // group needs all of them, and loaded per thread they would move 16
+        // times those bytes through the CU's load path
+        {
+            const int tt = min(tid, 2 * DK - 1);
+            const size_t ch = (tt < DK ? 0 : (size_t)pp.H_k * DK - DK) + (size_t)kh * DK + tt;
+            wt = *reinterpret_cast<const float4 *>(pp.conv_w + ch * 4);
         }
     }
     // the first value head's g, beta and V: issued after K and Q (the
@@ -748,9 +750,12 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
 #pragma unroll
         for (int j = 0; j < NHK; ++j)
             if (tid + 256 * j < 6 * DK) sA[tid + 256 * j] = hk[j];
+        // sA: the history [3][q | k], then the taps [q | k] (float4 each)
+        float4 *sW = reinterpret_cast<float4 *>(sA + 6 * DK);
+        if (tid < 2 * DK) sW[tid] = wt;
         lds_sync();
-        conv_rows<E, KL>(kraw, wk, krow0, len, sA, 2 * DK, DK + kcv * VEC, kx, SI ? kxl : nullptr);
-        conv_rows<E, KL>(qraw, wq, krow0, len, sA, 2 * DK, kcv * VEC, qx, SI ? qxl : nullptr);
+        conv_rows<E, KL>(kraw, sW + DK + kcv * VEC, krow0, len, sA, 2 * DK, DK + kcv * VEC, kx, SI ? kxl : nullptr);
+        conv_rows<E, KL>(qraw, sW + kcv * VEC, krow0, len, sA, 2 * DK, kcv * VEC, qx, SI ? qxl : nullptr);
     }
 #pragma unroll
     for (int p = 0; p < KL; ++p) {
