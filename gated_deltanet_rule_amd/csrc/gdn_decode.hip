@@ -116,10 +116,6 @@ __device__ __forceinline__ float4 buf_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t
     const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
     return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
 }
-__device__ __forceinline__ void buf_store_f4(float4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-    __builtin_amdgcn_raw_buffer_store_b128(
-        u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)}, r, off, 0, 0);
-}
 // The loads that produced v are complete at this point of the program (the
 // compiler's wait for them is placed here); no code is emitted.
 __device__ __forceinline__ void loaded(float v) { asm volatile("" ::"v"(v)); }
