@@ -504,8 +504,8 @@ __device__ __forceinline__ void conv_rows(const u32x4 *raw, const float4 *w, int
 // the convolution output becomes two-term bf16 operands (SI: hi + lo, about
 // 16 significant bits) in every product that reads q, k or v, and with fp32
 // rows the operands stay fp32.
-template <int DK, int DV, typename E, bool CONV>
-__global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_kernel(PrepParams pp)
+template <int DK, int DV, typename E, bool CONV, int NW>
+__global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW / 4) void prep_kernel(PrepParams pp)
 {
     constexpr bool SI = CONV && sizeof(E) == 2;
     using M = Mfma<E>;
@@ -520,6 +520,8 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     constexpr int NKD = G::NKD, NKC = G::NKC, NMT = DK / 16, NCT = DV / 16;
     constexpr int VPR = DK / VEC;         // 16-byte vectors per q/k row
     constexpr int VPRV = DV / VEC;        // 16-byte vectors per v row
+    constexpr int NT = 64 * NW;           // threads (NW = 4 or 8 waves)
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     E *sK = reinterpret_cast<E *>(smem + L::OFF_K);
@@ -562,12 +564,13 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     }
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = w % NH;                 // waves NH.. repeat the scalars of waves 0..NH-1
     const int n = lane & 15, qd = lane >> 4;
     const E *qg = static_cast<const E *>(pp.q);
     const E *kg = static_cast<const E *>(pp.k);
     const E *vg = static_cast<const E *>(pp.v);
 
-    // g and beta of up to NH value heads (wave w: head j0 + w, lane: row)
+    // g and beta of up to NH value heads (wave w: head j0 + w mod NH, lane: row)
     // Loads here are unconditional (clamped row / head, zero selected
     // afterwards): a load inside a branch leaves the compiler unable to count
     // outstanding memory operations, and the next wait for it then also waits
@@ -579,7 +582,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     float gq = 0.f, bq = 0.f, grate = 0.f, gbias = 0.f;
     const int lrow = min(lane, len - 1);
     auto load_gb = [&](int j0) {
-        const int hh = kh * ratio + min(j0 + w, ratio - 1);
+        const int hh = kh * ratio + min(j0 + wn, ratio - 1);
         gq = pp.g[(size_t)(t0 + lrow) * pp.H_v + hh];
         bq = pp.beta[(size_t)(t0 + lrow) * pp.H_v + hh];
         grate = pp.gates.rate[hh];
@@ -587,7 +590,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     };
     // cumulative log-decay (fp64) and the per-row scalars of those heads
     auto head_scalars = [&](int j0) {
-        const int jw = min(j0 + w, ratio - 1);
+        const int jw = min(j0 + wn, ratio - 1);
         const int hh = kh * ratio + jw, hs = jw % NH;
         float *scal = reinterpret_cast<float *>(pp.vblocks + ((size_t)slot * pp.H_v + hh) * ((size_t)G::VBLK * 1024) +
                                                 G::F_SCAL * 1024);
@@ -636,18 +639,18 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     // head's three history rows and of its taps, both staged through LDS;
     // the three rows before a thread's first are read back from LDS once
     // every row is there)
-    constexpr int VL = (C * VPRV + 255) / 256;
-    constexpr int NHV = CONV ? (3 * DV + 255) / 256 : 1;
-    constexpr int NWV = CONV ? (4 * DV + 255) / 256 : 1;
+    constexpr int VL = (C * VPRV + NT - 1) / NT;
+    constexpr int NHV = CONV ? (3 * DV + NT - 1) / NT : 1;
+    constexpr int NWV = CONV ? (4 * DV + NT - 1) / NT : 1;
     u32x4 vpre[VL];
     float vh[NHV], vw[NWV];
     const int vrow0 = (tid / VPRV) * VL, vcv = tid % VPRV;
-    static_assert(C * VPRV % 256 == 0 && C * VPR % 256 == 0, "whole vectors per thread");
+    static_assert(C * VPRV % NT == 0 && C * VPR % NT == 0, "whole vectors per thread");
     auto load_v = [&](int hh) {
         if constexpr (!CONV) {
 #pragma unroll
             for (int p = 0; p < VL; ++p) {
-                const int vi = tid + 256 * p;
+                const int vi = tid + NT * p;
                 const int r = vi / VPRV, cv = vi % VPRV;
                 const u32x4 x = load_once(vg + (size_t)(t0 + min(r, len - 1)) * pp.rs_v + (size_t)hh * DV + cv * VEC);
                 vpre[p] = r < len ? x : u32x4{0u, 0u, 0u, 0u};
@@ -664,7 +667,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
                                        first ? 0u : 3u * (uint32_t)pp.rs_v * (uint32_t)sizeof(E));
 #pragma unroll
             for (int j = 0; j < NHV; ++j) {
-                const int idx = min(tid + 256 * j, 3 * DV - 1);
+                const int idx = min(tid + NT * j, 3 * DV - 1);
                 const int m = idx / DV, c = idx % DV;
                 const uint32_t br = buf_bits<E>(hr, (uint32_t)((size_t)m * pp.rs_v + (size_t)hh * DV + c) * sizeof(E));
                 const uint32_t bs = __builtin_amdgcn_raw_buffer_load_b32(
@@ -673,16 +676,16 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
             }
 #pragma unroll
             for (int j = 0; j < NWV; ++j)
-                vw[j] = pp.conv_w[(vch0 + (size_t)hh * DV) * 4 + min(tid + 256 * j, 4 * DV - 1)];
+                vw[j] = pp.conv_w[(vch0 + (size_t)hh * DV) * 4 + min(tid + NT * j, 4 * DV - 1)];
         }
     };
 
 
     // 1. K and Q rows of the chunk (row-major, zero past the end) and their
     //    inverse norms; a row's VPR vectors sit in VPR adjacent lanes
-    constexpr int KL = C * VPR / 256;     // 16-byte vectors of K (and of Q) per thread
+    constexpr int KL = C * VPR / NT;      // 16-byte vectors of K (and of Q) per thread
     constexpr int KR = CONV ? KL + 3 : KL;
-    constexpr int NHK = CONV ? (6 * DK + 255) / 256 : 1;
+    constexpr int NHK = CONV ? (6 * DK + NT - 1) / NT : 1;
     const int krow0 = (tid / VPR) * KL, kcv = tid % VPR;
     u32x4 kx[KL], qx[KL], kxl[SI ? KL : 1], qxl[SI ? KL : 1];
     u32x4 kraw[CONV ? KR : 1], qraw[CONV ? KR : 1];
@@ -691,7 +694,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     if constexpr (!CONV) {
 #pragma unroll
         for (int p = 0; p < KL; ++p) {
-            const int vi = tid + 256 * p;
+            const int vi = tid + NT * p;
             const int r = vi / VPR, cv = vi % VPR;
             const size_t off = (size_t)(t0 + min(r, len - 1)) * pp.rs_qk + (size_t)kh * DK + (size_t)cv * VEC;
             kx[p] = load_once(kg + off);
@@ -718,7 +721,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
         const auto hkb = raw_buffer(const_cast<E *>(kg) + rrow, rbytes);
 #pragma unroll
         for (int j = 0; j < NHK; ++j) {
-            const int idx = min(tid + 256 * j, 6 * DK - 1);
+            const int idx = min(tid + NT * j, 6 * DK - 1);
             const int m = idx / (2 * DK), c2 = idx % (2 * DK);
             const bool isk = c2 >= DK;
             const int c = isk ? c2 - DK : c2;
@@ -749,7 +752,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     if constexpr (CONV) {
 #pragma unroll
         for (int j = 0; j < NHK; ++j)
-            if (tid + 256 * j < 6 * DK) sA[tid + 256 * j] = hk[j];
+            if (tid + NT * j < 6 * DK) sA[tid + NT * j] = hk[j];
         // sA: the history [3][q | k], then the taps [q | k] (float4 each)
         float4 *sW = reinterpret_cast<float4 *>(sA + 6 * DK);
         if (tid < 2 * DK) sW[tid] = wt;
@@ -759,7 +762,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     }
 #pragma unroll
     for (int p = 0; p < KL; ++p) {
-        const int r = CONV ? krow0 + p : (tid + 256 * p) / VPR;
+        const int r = CONV ? krow0 + p : (tid + NT * p) / VPR;
         const int cv = kcv;
         const u32x4 kv = r < len ? kx[p] : u32x4{0u, 0u, 0u, 0u};
         const u32x4 qv = r < len ? qx[p] : u32x4{0u, 0u, 0u, 0u};
@@ -802,17 +805,18 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     // 2. raw q and k^T of this key head as operand fragments for the scan
     {
         char *kb_blk = pp.kblocks + ((size_t)slot * pp.H_k + kh) * ((size_t)G::KBLK * 1024);
+        static_assert(G::NQF % NW == 0 && G::NKF % NW == 0, "fragments per wave");
 #pragma unroll
-        for (int ff = 0; ff < G::NQF / 4; ++ff) {
-            const int f = w + 4 * ff;
+        for (int ff = 0; ff < G::NQF / NW; ++ff) {
+            const int f = w + NW * ff;
             const int rt = f / NKD, kb = f % NKD;
             store_frag<E>(kb_blk + G::F_Q * 1024, f, lane, M::load_rm(sX + (16 * rt + n) * LDX, kb * KB, qd));
             if constexpr (SI)
                 store_frag<E>(kb_blk + G::F_QL * 1024, f, lane, M::load_rm(sXL + (16 * rt + n) * LDX, kb * KB, qd));
         }
 #pragma unroll
-        for (int ff = 0; ff < G::NKF / 4; ++ff) {
-            const int f = w + 4 * ff;
+        for (int ff = 0; ff < G::NKF / NW; ++ff) {
+            const int f = w + NW * ff;
             const int mt = f / NKC, kc = f % NKC;
             store_frag<E>(kb_blk + G::F_KT * 1024, f, lane, TR::frag(sK, LDK, kc * KB, 16 * mt, lane));
             if constexpr (SI)
@@ -821,12 +825,15 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     }
 
     // 3. raw K K^T (lower tiles) and K Q^T (tiles (ct, rt), ct <= rt): 20
-    //    tile products, 5 per wave; kept in registers for all value heads.
-    floatx4 acc[5];
+    //    tile products, tile it = w + NW s in wave w (5 per wave, or 3 and 2
+    //    with eight waves); kept in registers for all value heads.
+    constexpr int NPW = (20 + NW - 1) / NW;
+    floatx4 acc[NPW];
 #pragma unroll
-    for (int s = 0; s < 5; ++s) {
+    for (int s = 0; s < NPW; ++s) {
         acc[s] = floatx4{0.f, 0.f, 0.f, 0.f};
-        const int it = w + 4 * s;
+        const int it = w + NW * s;
+        if (it >= 20) continue;     // wave-uniform; LDS reads and matrix-core ops only
         const int pr = it < 10 ? it : it - 10;
         const int rt = low_r(pr), ct = low_c(pr);
         const int ka = (16 * (it < 10 ? rt : ct) + n) * LDK;
@@ -847,6 +854,14 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
     lds_sync();   // Q is dead: sX holds V from here on
 
     for (int jv = jbeg; jv < jend; ++jv) {
+        // With eight waves the lane index is made opaque once per head, so
+        // that the per-lane LDS offsets and store addresses of the head's
+        // phases are formed inside the loop: hoisted out of it, they held
+        // about 60 registers across all heads, more than four waves per SIMD
+        // leave.
+        int tid_o = threadIdx.x;
+        if constexpr (NW == 8) asm volatile("" : "+v"(tid_o));
+        const int tid = tid_o, lane = tid & 63, n = lane & 15, qd = lane >> 4;
         const int h = kh * ratio + jv;
         char *blk = pp.vblocks + ((size_t)slot * pp.H_v + h) * ((size_t)G::VBLK * 1024);
         char *Wf = blk + G::F_W * 1024;
@@ -862,7 +877,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
         if constexpr (!CONV) {
 #pragma unroll
             for (int p = 0; p < VL; ++p) {
-                const int vi = tid + 256 * p;
+                const int vi = tid + NT * p;
                 if (vi < C * VPRV)
                     *reinterpret_cast<u32x4 *>(sX + (vi / VPRV) * LDX + (vi % VPRV) * VEC) = vpre[p];
             }
@@ -879,10 +894,10 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
             }
 #pragma unroll
             for (int j = 0; j < NHV; ++j)
-                if (tid + 256 * j < 3 * DV) sA[tid + 256 * j] = vh[j];
+                if (tid + NT * j < 3 * DV) sA[tid + NT * j] = vh[j];
 #pragma unroll
             for (int j = 0; j < NWV; ++j)
-                if (tid + 256 * j < 4 * DV) sA[3 * DV + tid + 256 * j] = vw[j];
+                if (tid + NT * j < 4 * DV) sA[3 * DV + tid + NT * j] = vw[j];
             lds_sync();
 #pragma unroll
             for (int u = 0; u < 3; ++u)
@@ -908,7 +923,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
         //     exp is always taken of G_r - G_c <= 0 (fp64 difference).
         auto a_tile = [&](int s) {
                 // lane: column c, rows r0 + j
-                const int it = w + 4 * s;
+                const int it = w + NW * s;
                 const int rt = low_r(it), ct = low_c(it);
                 const int c = 16 * ct + n, r0 = 16 * rt + 4 * qd;
                 const double gc = sG[c];
@@ -925,7 +940,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
         };
         auto p_tile = [&](int s) {
                 // lane: row r, columns c0 + j
-                const int pr = w + 4 * s - 10;
+                const int pr = w + NW * s - 10;
                 const int rt = low_r(pr), ct = low_c(pr);
                 const int r = 16 * rt + n, c0 = 16 * ct + 4 * qd;
                 const double gr = sG[r];
@@ -942,14 +957,23 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
                 }
                 store_quarter2<E>(Pf, Plf, rt * NKC + ct / TPB, lane, ct % TPB, pv);
         };
-        // tiles w and w + 4 are A tiles for every wave, w + 12 and w + 16 P
-        // tiles, w + 8 is an A tile for waves 0, 1 and a P tile for 2, 3
-        a_tile(0);
-        a_tile(1);
-        p_tile(3);
-        p_tile(4);
-        if (w < 2) a_tile(2); else p_tile(2);
-        for (int z = w; z < 6; z += 4) {
+        // tiles 0..9 are A tiles, 10..19 P tiles.  Four waves: w and w + 4
+        // are A tiles for every wave, w + 12 and w + 16 P tiles, w + 8 an A
+        // tile for waves 0, 1 and a P tile for 2, 3.  Eight waves: w is an A
+        // tile, w + 8 an A tile for waves 0, 1 and a P tile for 2..7, w + 16
+        // a P tile for waves 0..3.
+        if constexpr (NW == 4) {
+            a_tile(0);
+            a_tile(1);
+            p_tile(3);
+            p_tile(4);
+            if (w < 2) a_tile(2); else p_tile(2);
+        } else {
+            a_tile(0);
+            if (w < 2) a_tile(1); else p_tile(1);
+            if (w < 4) p_tile(2);
+        }
+        for (int z = w; z < 6; z += NW) {
             const int rt = up_r(z), ct = up_c(z);
             store_quarter2<E>(Pf, Plf, rt * NKC + ct / TPB, lane, ct % TPB, floatx4{0.f, 0.f, 0.f, 0.f});
             // the products with T read whole K blocks: its upper blocks are zero
@@ -1011,18 +1035,24 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
         }
 
         // 4d. W^T = K^T T''^T, T'' = T diag(beta e^G / |k|): wave w takes token
-        //     tile tt = w (B operand loaded once, all dk tiles).
-        //     U0 = T diag(beta) V: wave w takes token tile 3 - w, so every
-        //     wave runs the same number of products.
+        //     tile tt = w mod 4 (B operand loaded once) and its share of the
+        //     dk tiles (all of them with four waves, half with eight).
+        //     U0 = T diag(beta) V: wave w takes token tile 3 - w mod 4 and its
+        //     share of the column tiles, so every wave runs the same number of
+        //     products.
+        constexpr int NSH = NW / 4;
+        const int sh = w / 4;
+        static_assert(NMT % NSH == 0 && NCT % NSH == 0, "tiles per share");
         {
-            const int tt = w;
+            const int tt = w % 4;
             const int nkb = (16 * tt + 15) / KB + 1;    // K blocks reaching the diagonal
             Frag bh[NKC], bl[NKC];
 #pragma unroll
             for (int kb = 0; kb < NKC; ++kb)
                 if (kb < nkb) SP::rm_f32(sT + (16 * tt + n) * LDA, kb * KB, qd, sCol, bh[kb], bl[kb]);
 #pragma unroll
-            for (int dt = 0; dt < NMT; ++dt) {
+            for (int dd = 0; dd < NMT / NSH; ++dd) {
+                const int dt = sh * (NMT / NSH) + dd;
                 floatx4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < NKC; ++kb) {
@@ -1040,14 +1070,15 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
             }
         }
         {
-            const int rt = 3 - w;
+            const int rt = 3 - w % 4;
             const int nkb = (16 * rt + 15) / KB + 1;
             Frag ah[NKC], al[NKC];
 #pragma unroll
             for (int kb = 0; kb < NKC; ++kb)
                 if (kb < nkb) SP::rm_f32(sT + (16 * rt + n) * LDA, kb * KB, qd, sBeta, ah[kb], al[kb]);
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
+            for (int cc = 0; cc < NCT / NSH; ++cc) {
+                const int ct = sh * (NCT / NSH) + cc;
                 floatx4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < NKC; ++kb) {
@@ -1070,7 +1101,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
         const int hs = jbeg % NH;
         const double *sG = sGh + hs * C;
         const float *sCol = sColh + hs * C;
-        for (int x = tid; x < C * C; x += 256) pp.dbg->T[x / C][x % C] = sT[(x / C) * LDA + x % C];
+        for (int x = tid; x < C * C; x += NT) pp.dbg->T[x / C][x % C] = sT[(x / C) * LDA + x % C];
         if (tid < C) pp.dbg->G[tid] = sG[tid];
         if (tid == 0) {
             pp.dbg->chunk = chunk;
@@ -1081,7 +1112,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && !CONV) ? 2 : 1) void prep_k
         const int tt = w;
         const int nkb = (16 * tt + 15) / KB + 1;
 #pragma unroll 1
-        for (int dt = 0; dt < NMT; ++dt) {
+        for (int dt = 0; dt < (tt < 4 ? NMT : 0); ++dt) {     // token tiles 0..3: waves 0..3
             floatx4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
             for (int kb = 0; kb < nkb; ++kb) {
@@ -1582,6 +1613,13 @@ WsPtrs ws_ptrs(const Problem &p, const PrefillArgs &a)
     return w;
 }
 
+// Waves per preparation workgroup.  At d_k = d_v = 128 eight: the per-thread
+// row vectors and product tiles halve, so two workgroups of eight waves fit a
+// CU (128 registers, LDS unchanged) where two of four did, and every phase
+// but the triangular solve splits over twice the waves.  Smaller heads keep
+// four (their fragment counts do not split eight ways).
+template <int DK, int DV> constexpr int kPrepWaves = DK == 128 && DV == 128 ? 8 : 4;
+
 template <int DK, int DV, typename E>
 hipError_t prepare_t(const Problem &p, const PrefillArgs &a, const Segment &sg, hipStream_t st)
 {
@@ -1620,15 +1658,17 @@ hipError_t prepare_t(const Problem &p, const PrefillArgs &a, const Segment &sg, 
     if (p.conv_w) {
         // bf16 rows: two-term bf16 operands (SI); fp32 rows: fp32 operands
         constexpr size_t lds = PrepLds<DK, DV, E, sizeof(E) == 2>::BYTES;
-        e = set_lds(prep_kernel<DK, DV, E, true>, lds);
+        e = set_lds(prep_kernel<DK, DV, E, true, kPrepWaves<DK, DV>>, lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((prep_kernel<DK, DV, E, true>), grid, dim3(256), lds, st, pp);
+        hipLaunchKernelGGL((prep_kernel<DK, DV, E, true, kPrepWaves<DK, DV>>), grid, dim3(64 * kPrepWaves<DK, DV>), lds,
+                           st, pp);
         return hipGetLastError();
     }
     constexpr size_t lds = PrepLds<DK, DV, E>::BYTES;
-    e = set_lds(prep_kernel<DK, DV, E, false>, lds);
+    e = set_lds(prep_kernel<DK, DV, E, false, kPrepWaves<DK, DV>>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prep_kernel<DK, DV, E, false>), grid, dim3(256), lds, st, pp);
+    hipLaunchKernelGGL((prep_kernel<DK, DV, E, false, kPrepWaves<DK, DV>>), grid, dim3(64 * kPrepWaves<DK, DV>), lds, st,
+                       pp);
     return hipGetLastError();
 }
 
