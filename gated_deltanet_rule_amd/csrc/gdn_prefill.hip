@@ -290,6 +290,12 @@ __device__ __forceinline__ u32x4 load_once(const bf16_t *p) {
 __device__ __forceinline__ u32x4 load_once(const float *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
+// The same through a buffer resource (bit 1 of the cache-policy operand is
+// the non-temporal bit): zero past the range's end, and no memory access at
+// all when the range is empty.
+__device__ __forceinline__ u32x4 load_once(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
 
 // Squared norm of the 16 bytes a lane loaded from a q / k row.
 template <typename E> __device__ __forceinline__ float sumsq16(u32x4 u);
@@ -646,20 +652,26 @@ __global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW /
     float vh[NHV], vw[NWV];
     const int vrow0 = (tid / VPRV) * VL, vcv = tid % VPRV;
     static_assert(C * VPRV % NT == 0 && C * VPR % NT == 0, "whole vectors per thread");
-    auto load_v = [&](int hh) {
+    // The rows are read through a buffer range that is empty when they are
+    // not needed (the prefetch after the last head): the loads still issue,
+    // so every wait counts exactly, but they read no memory (a reload of the
+    // last head's rows added 16 MiB of reads to a 4096-token call).
+    auto load_v = [&](int hh, bool live) {
+        const auto vr = raw_buffer(const_cast<E *>(vg) + (size_t)t0 * pp.rs_v + (size_t)hh * DV,
+                                   live ? (uint32_t)(((size_t)(len - 1) * pp.rs_v + DV) * sizeof(E)) : 0u);
         if constexpr (!CONV) {
 #pragma unroll
             for (int p = 0; p < VL; ++p) {
                 const int vi = tid + NT * p;
                 const int r = vi / VPRV, cv = vi % VPRV;
-                const u32x4 x = load_once(vg + (size_t)(t0 + min(r, len - 1)) * pp.rs_v + (size_t)hh * DV + cv * VEC);
+                const u32x4 x = load_once(vr, (uint32_t)(((size_t)min(r, len - 1) * pp.rs_v + cv * VEC) * sizeof(E)));
                 vpre[p] = r < len ? x : u32x4{0u, 0u, 0u, 0u};
             }
         } else {
 #pragma unroll
             for (int p = 0; p < VL; ++p) {
                 const int rr = min(vrow0 + p, len - 1);
-                vpre[p] = load_once(vg + (size_t)(t0 + rr) * pp.rs_v + (size_t)hh * DV + vcv * VEC);
+                vpre[p] = load_once(vr, (uint32_t)(((size_t)rr * pp.rs_v + vcv * VEC) * sizeof(E)));
             }
             // history: the three rows before the chunk, or for a sequence's
             // first chunk the slot's stored inputs (see the K and Q history)
@@ -748,7 +760,7 @@ __global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW /
     __builtin_amdgcn_sched_barrier(0);
     const int jbase = jbeg - jbeg % NH;
     load_gb(jbase);
-    load_v(kh * ratio + jbeg);
+    load_v(kh * ratio + jbeg, true);
     if constexpr (CONV) {
 #pragma unroll
         for (int j = 0; j < NHK; ++j)
@@ -912,7 +924,7 @@ __global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW /
                 if constexpr (SI) *reinterpret_cast<u32x4 *>(sXL + (vrow0 + p) * LDX + vcv * VEC) = resl[p];
             }
         }
-        load_v(kh * ratio + min(jv + 1, jend - 1));    // next head (the last reloads itself)
+        load_v(kh * ratio + min(jv + 1, jend - 1), jv + 1 < jend);    // next head (none after the last)
         if (jv > jbase && hs == 0) {
             load_gb(jv);
             head_scalars(jv);
@@ -975,7 +987,9 @@ __global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW /
         }
         for (int z = w; z < 6; z += NW) {
             const int rt = up_r(z), ct = up_c(z);
-            store_quarter2<E>(Pf, Plf, rt * NKC + ct / TPB, lane, ct % TPB, floatx4{0.f, 0.f, 0.f, 0.f});
+            // a fragment wholly above the diagonal is never read by the scan
+            if ((ct / TPB) * KB <= 16 * rt + 15)
+                store_quarter2<E>(Pf, Plf, rt * NKC + ct / TPB, lane, ct % TPB, floatx4{0.f, 0.f, 0.f, 0.f});
             // the products with T read whole K blocks: its upper blocks are zero
             *reinterpret_cast<floatx4 *>(sT + (16 * rt + (lane >> 2)) * LDA + 16 * ct + 4 * (lane & 3)) =
                 floatx4{0.f, 0.f, 0.f, 0.f};
@@ -1454,6 +1468,14 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
     } else {
         OT *og = static_cast<OT *>(sp.out);
         Frag Qf[NKD], Qlf[SI ? NKD : 1], Ph[NKC], Pl[NKC];
+        // P row tile rt is zero past column 16 rt + 15, so its K blocks from
+        // npl on are zero and the preparation does not write them: they are
+        // read through a range that ends before them (zero, no memory access)
+        const int npl = (16 * rt + 15) / KB + 1;
+        auto pfrag = [&](int c, int base, int kc) -> Frag {
+            const auto r = raw_buffer(const_cast<u32x4 *>(vblk(c)) + (size_t)(base + rt * NKC) * 64, (uint32_t)npl * 1024u);
+            return __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(kc * 64 + lane) * 16u, 0, 0));
+        };
 #pragma unroll
         for (int kb = 0; kb < NKD; ++kb) {
             Qf[kb] = kfrag(c0, G::F_Q + rt * NKD + kb);
@@ -1461,8 +1483,8 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
         }
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
-            Ph[kc] = vfrag(c0, G::F_PH + rt * NKC + kc);
-            if constexpr (NS == 2) Pl[kc] = vfrag(c0, G::F_PL + rt * NKC + kc);
+            Ph[kc] = pfrag(c0, G::F_PH, kc);
+            if constexpr (NS == 2) Pl[kc] = pfrag(c0, G::F_PL, kc);
         }
         floatx4 qs4 = scal4(c0, ro);
         // the sequence's token range; its chunks are consecutive 64-token pieces
@@ -1525,8 +1547,8 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
             }
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
-                Ph[kc] = vfrag(cn, G::F_PH + rt * NKC + kc);
-                if constexpr (NS == 2) Pl[kc] = vfrag(cn, G::F_PL + rt * NKC + kc);
+                Ph[kc] = pfrag(cn, G::F_PH, kc);
+                if constexpr (NS == 2) Pl[kc] = pfrag(cn, G::F_PL, kc);
             }
             lds_sync();
         }

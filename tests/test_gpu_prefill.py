@@ -201,6 +201,38 @@ def test_long_prefill_f32_runs_in_ranges():
     compare_prefill(case, out, pool, ref_o, ref_s, heads=heads)
 
 
+@pytest.mark.parametrize("dtype,dk,dv,lens", [("bf16", 128, 128, [700, 129]), ("f32", 64, 64, [200, 1])])
+def test_prefill_reads_no_workspace_byte_before_writing_it(dtype, dk, dv, lens):
+    """The same call with a workspace filled with 0xff bytes (NaN as fp32
+    and bf16) and with a zeroed one gives bitwise equal results: every byte
+    the scan reads was written by the preparation of the same call.  The
+    preparation leaves out the P fragments that lie wholly above the
+    diagonal, which the scan reads through a range that ends before them."""
+    import gated_deltanet_rule_amd as gdn
+    case = gi.make_case(f"ws_dirty_{dtype}_{dk}", lens, 2, 4, dk, dv, dtype, seed=71, decay="weak",
+                        n_slots=4, scatter_slots=True)
+    d = dev_case(case)
+    T = case.total_tokens
+    dims = gdn._dims_from(d["q"], d["v"], torch.empty(d["v"].shape, device="meta"), 0.0, 1e-6,
+                          d["pool"])
+    need = gdn.chunked_workspace_size(dims, case.n_seqs, T)
+    say(f"prefill {case.name}: lengths {lens}, workspace {need} bytes")
+
+    def run(fill):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
+        out = torch.empty(d["v"].shape, dtype=torch.float32, device="cuda")
+        pool = d["pool"].clone()
+        gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], pool, out, d["cu"],
+                    d["slot_in"], d["slot_out"], ws)
+        torch.cuda.synchronize()
+        return out, pool
+
+    o1, p1 = run(0)
+    o2, p2 = run(255)
+    assert torch.isfinite(o1).all() and torch.isfinite(p1).all()
+    assert torch.equal(o1, o2) and torch.equal(p1, p2)
+
+
 def test_one_range_workspace():
     """gdn_chunked_prefill with exactly gdn_chunked_prefill_workspace_size
     bytes (the factor slots of one 64-chunk range for 130 chunks) gives the
