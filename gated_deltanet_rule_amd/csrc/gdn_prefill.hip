@@ -277,6 +277,28 @@ template <> __device__ __forceinline__ void store_quarter2<float>(void *hi_base,
     store_quarter<float>(hi_base, f, lane, half, v);
 }
 
+// Both halves of fragment f at once (bf16 operands: two 16-column tiles of
+// a 32-deep K block, v0 the first), one 16-byte store per lane: written half
+// by half, each store instruction would fill only half of the lines it
+// touches.  Single-term, and two-term into hi_base / lo_base.
+__device__ __forceinline__ void store_pair(void *base, int f, int lane, floatx4 v0, floatx4 v1) {
+    const uint4 u = make_uint4(pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v1[0], v1[1]),
+                               pack_bf16x2(v1[2], v1[3]));
+    *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(base) + ((size_t)f * 64 + lane) * 16) = u;
+}
+__device__ __forceinline__ void store_pair2(void *hi_base, void *lo_base, int f, int lane, floatx4 v0, floatx4 v1) {
+    floatx4 h0, h1, l0, l1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        h0[j] = (float)(__bf16)v0[j];
+        h1[j] = (float)(__bf16)v1[j];
+        l0[j] = v0[j] - h0[j];
+        l1[j] = v1[j] - h1[j];
+    }
+    store_pair(hi_base, f, lane, h0, h1);
+    store_pair(lo_base, f, lane, l0, l1);
+}
+
 // 16 bytes of an input row (q, k, v or the mixed rows), which the preparation
 // reads once.  The load is non-temporal, so a miss does not allocate the line
 // in the MALL (the memory-side last-level cache): that cache then holds the
@@ -354,6 +376,36 @@ __device__ __forceinline__ float exp_neg(double d) {
     return __builtin_amdgcn_exp2f((float)(d * 1.4426950408889634));
 }
 
+// A DPP move of an fp64 value (both halves; lanes without a source, and
+// rows outside RM, read zero).  CTRL 0x111..0x118: row_shr 1..8 (within rows
+// of 16 lanes); 0x142: row_bcast 15 (lane 15 of each row to the next row);
+// 0x143: row_bcast 31 (lane 31 to rows 2 and 3).
+template <int CTRL, int RM> __device__ __forceinline__ double dpp_f64(double x) {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, RM, 0xf, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, RM, 0xf, true);
+    return __builtin_bit_cast(double, ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+// Inclusive prefix sum of an fp64 value over the 64 lanes of a wave: within
+// each row of 16 lanes by row shifts, then across rows by the broadcasts of
+// lanes 15 and 31.  The moves run in the vector ALU, without the LDS round
+// trip of a shuffle.
+__device__ __forceinline__ double wave_inclusive_sum(double x) {
+    x += dpp_f64<0x111, 0xf>(x);
+    x += dpp_f64<0x112, 0xf>(x);
+    x += dpp_f64<0x114, 0xf>(x);
+    x += dpp_f64<0x118, 0xf>(x);
+    x += dpp_f64<0x142, 0xa>(x);
+    x += dpp_f64<0x143, 0xc>(x);
+    return x;
+}
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
 // The 10 lower 16x16 tile pairs (rt, ct), ct <= rt, of a 64x64 matrix in
 // row order, and the 6 strictly upper ones.  Computed, not tabulated: a table
 // indexed per wave becomes a vector memory load, and on gfx9 waiting for it
@@ -362,6 +414,25 @@ __device__ __forceinline__ int low_r(int it) { return it >= 6 ? 3 : it >= 3 ? 2 
 __device__ __forceinline__ int low_c(int it) { const int r = low_r(it); return it - r * (r + 1) / 2; }
 __device__ __forceinline__ int up_r(int z) { return z >= 5 ? 2 : z >= 3 ? 1 : 0; }
 __device__ __forceinline__ int up_c(int z) { const int r = up_r(z); return r == 0 ? z + 1 : r == 1 ? z - 1 : 3; }
+
+// Product tile of slot s in wave w of the preparation (0..9: the lower
+// tiles of K K^T, 10..19: the tiles of K Q^T; -1: none).  Four waves: w + 4 s.
+// Eight waves: the A tiles w and, in waves 0 and 1, 8 + w; the P tiles in the
+// pairs that fill one bf16 operand fragment (the two 16-column halves of a
+// 32-deep K block): waves 2..5 the tiles 1+2, 3+4, 6+7 and 8+9, waves 0 and
+// 1 the tiles 0 and 5 ((0,0) and (2,2)), whose partners lie above the
+// diagonal and are zero.
+template <int NW> __device__ __forceinline__ int prod_it(int w, int s)
+{
+    if constexpr (NW == 4) {
+        return w + 4 * s;
+    } else {
+        if (s == 0) return w;
+        if (w < 2) return s == 1 ? 8 + w : (w == 0 ? 10 : 15);
+        if (w < 6) return 10 + (w == 2 ? 1 : w == 3 ? 3 : w == 4 ? 6 : 8) + (s - 1);
+        return -1;
+    }
+}
 
 struct PrepParams {
     const void *q, *k, *v;
@@ -605,13 +676,8 @@ __global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW /
         const float bl = pp.gates.raw ? gate_beta(bq) : bq;
         const float gv = lane < len ? gl : 0.f;
         const float bv = lane < len ? bl : 0.f;
-        double Gc = gv;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const double y = __shfl_up(Gc, off, 64);
-            if (lane >= off) Gc += y;
-        }
-        const double Gn = __shfl(Gc, 63, 64);
+        const double Gc = wave_inclusive_sum((double)gv);
+        const double Gn = readlane_f64(Gc, 63);
         const float rk = sRK[r];
         const float eG = expf((float)Gc);
         sGh[hs * C + r] = Gc;
@@ -844,8 +910,8 @@ __global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW /
 #pragma unroll
     for (int s = 0; s < NPW; ++s) {
         acc[s] = floatx4{0.f, 0.f, 0.f, 0.f};
-        const int it = w + NW * s;
-        if (it >= 20) continue;     // wave-uniform; LDS reads and matrix-core ops only
+        const int it = prod_it<NW>(w, s);
+        if (it < 0 || it >= 20) continue;     // wave-uniform; LDS reads and matrix-core ops only
         const int pr = it < 10 ? it : it - 10;
         const int rt = low_r(pr), ct = low_c(pr);
         const int ka = (16 * (it < 10 ? rt : ct) + n) * LDK;
@@ -935,7 +1001,7 @@ __global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW /
         //     exp is always taken of G_r - G_c <= 0 (fp64 difference).
         auto a_tile = [&](int s) {
                 // lane: column c, rows r0 + j
-                const int it = w + NW * s;
+                const int it = prod_it<NW>(w, s);
                 const int rt = low_r(it), ct = low_c(it);
                 const int c = 16 * ct + n, r0 = 16 * rt + 4 * qd;
                 const double gc = sG[c];
@@ -950,9 +1016,9 @@ __global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW /
                     sA[(r0 + j) * LDA + c] = (c < r0 + j) ? fr[j] * fc * acc[s][j] * e : 0.f;
                 }
         };
-        auto p_tile = [&](int s) {
+        auto p_val = [&](int s) -> floatx4 {
                 // lane: row r, columns c0 + j
-                const int pr = w + NW * s - 10;
+                const int pr = prod_it<NW>(w, s) - 10;
                 const int rt = low_r(pr), ct = low_c(pr);
                 const int r = 16 * rt + n, c0 = 16 * ct + 4 * qd;
                 const double gr = sG[r];
@@ -967,13 +1033,17 @@ __global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW /
                     const float e = exp_neg(gr - gc[j]);
                     pv[j] = (c0 + j <= r) ? fr * fc[j] * acc[s][j] * e : 0.f;
                 }
-                store_quarter2<E>(Pf, Plf, rt * NKC + ct / TPB, lane, ct % TPB, pv);
+                return pv;
         };
-        // tiles 0..9 are A tiles, 10..19 P tiles.  Four waves: w and w + 4
-        // are A tiles for every wave, w + 12 and w + 16 P tiles, w + 8 an A
-        // tile for waves 0, 1 and a P tile for 2, 3.  Eight waves: w is an A
-        // tile, w + 8 an A tile for waves 0, 1 and a P tile for 2..7, w + 16
-        // a P tile for waves 0..3.
+        auto p_tile = [&](int s) {
+                const int pr = prod_it<NW>(w, s) - 10;
+                const int rt = low_r(pr), ct = low_c(pr);
+                store_quarter2<E>(Pf, Plf, rt * NKC + ct / TPB, lane, ct % TPB, p_val(s));
+        };
+        // tiles 0..9 are A tiles, 10..19 P tiles (see prod_it).  Four waves:
+        // w and w + 4 are A tiles for every wave, w + 12 and w + 16 P tiles,
+        // w + 8 an A tile for waves 0, 1 and a P tile for 2, 3.  Eight waves:
+        // each wave's P tiles fill whole fragments, written at once.
         if constexpr (NW == 4) {
             a_tile(0);
             a_tile(1);
@@ -982,13 +1052,29 @@ __global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW /
             if (w < 2) a_tile(2); else p_tile(2);
         } else {
             a_tile(0);
-            if (w < 2) a_tile(1); else p_tile(1);
-            if (w < 4) p_tile(2);
+            if (w < 2) {
+                a_tile(1);
+                if constexpr (TPB == 2) {
+                    const int pr = prod_it<NW>(w, 2) - 10;
+                    store_pair2(Pf, Plf, low_r(pr) * NKC + low_c(pr) / TPB, lane, p_val(2), floatx4{0.f, 0.f, 0.f, 0.f});
+                } else {
+                    p_tile(2);
+                }
+            } else if (w < 6) {
+                if constexpr (TPB == 2) {
+                    const int pr = prod_it<NW>(w, 1) - 10;
+                    store_pair2(Pf, Plf, low_r(pr) * NKC + low_c(pr) / TPB, lane, p_val(1), p_val(2));
+                } else {
+                    p_tile(1);
+                    p_tile(2);
+                }
+            }
         }
         for (int z = w; z < 6; z += NW) {
             const int rt = up_r(z), ct = up_c(z);
-            // a fragment wholly above the diagonal is never read by the scan
-            if ((ct / TPB) * KB <= 16 * rt + 15)
+            // a fragment wholly above the diagonal is never read by the scan;
+            // with eight waves the partly zero ones are written whole above
+            if (NW == 4 && (ct / TPB) * KB <= 16 * rt + 15)
                 store_quarter2<E>(Pf, Plf, rt * NKC + ct / TPB, lane, ct % TPB, floatx4{0.f, 0.f, 0.f, 0.f});
             // the products with T read whole K blocks: its upper blocks are zero
             *reinterpret_cast<floatx4 *>(sT + (16 * rt + (lane >> 2)) * LDA + 16 * ct + 4 * (lane & 3)) =
@@ -1064,6 +1150,7 @@ __global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW /
 #pragma unroll
             for (int kb = 0; kb < NKC; ++kb)
                 if (kb < nkb) SP::rm_f32(sT + (16 * tt + n) * LDA, kb * KB, qd, sCol, bh[kb], bl[kb]);
+            floatx4 wprev = {0.f, 0.f, 0.f, 0.f};   // bf16: the first half of a fragment
 #pragma unroll
             for (int dd = 0; dd < NMT / NSH; ++dd) {
                 const int dt = sh * (NMT / NSH) + dd;
@@ -1076,10 +1163,18 @@ __global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW /
                     if constexpr (NS == 2) M::mma(a4, a, bl[kb]);
                     if constexpr (SI) M::mma(a4, TR::frag(sKL, LDK, kb * KB, 16 * dt, lane), bh[kb]);
                 }
-                if constexpr (SI)
-                    store_quarter2<E>(Wf, Wlf, tt * NKD + dt / TPB, lane, dt % TPB, a4);
-                else
-                    store_quarter<E>(Wf, tt * NKD + dt / TPB, lane, dt % TPB, a4);
+                if constexpr (TPB == 2) {
+                    // both halves of the fragment in one store
+                    if (dd % 2 == 0) {
+                        wprev = a4;
+                    } else {
+                        if constexpr (SI) store_pair2(Wf, Wlf, tt * NKD + dt / TPB, lane, wprev, a4);
+                        else store_pair(Wf, tt * NKD + dt / TPB, lane, wprev, a4);
+                    }
+                } else {
+                    if constexpr (SI) store_quarter2<E>(Wf, Wlf, tt * NKD + dt / TPB, lane, dt % TPB, a4);
+                    else store_quarter<E>(Wf, tt * NKD + dt / TPB, lane, dt % TPB, a4);
+                }
 
             }
         }
