@@ -820,13 +820,12 @@ __global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW /
             wt = *reinterpret_cast<const float4 *>(pp.conv_w + ch * 4);
         }
     }
-    // the first value head's g, beta and V: issued after K and Q (the
+    // the first value heads' g and beta: issued after K and Q (the
     // scheduling barrier keeps that order), so that waiting for K and Q does
     // not wait for these too
     __builtin_amdgcn_sched_barrier(0);
     const int jbase = jbeg - jbeg % NH;
     load_gb(jbase);
-    load_v(kh * ratio + jbeg, true);
     if constexpr (CONV) {
 #pragma unroll
         for (int j = 0; j < NHK; ++j)
@@ -879,6 +878,11 @@ __global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW /
     }
     lds_sync();
     head_scalars(jbase);
+    // The first value head's V rows, issued only now: every workgroup of a
+    // round starts by loading its rows at once, and K and Q (which the norms
+    // wait for) arrive sooner without V competing for the same bandwidth; V
+    // is first used after the fragment stores and the K K^T products.
+    load_v(kh * ratio + jbeg, true);
 
     // 2. raw q and k^T of this key head as operand fragments for the scan
     {
