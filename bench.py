@@ -73,9 +73,9 @@ C = 64
 PREFILL_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
                for f in ("gdn_prefill.hip", "gdn_mfma.h", "gdn_device.h", "gdn_internal.h")]
 MEASURED_TRAFFIC = {
-    "source_sha256": "5ff54ae4c347151aa16cdb0b5d34c37f99e5936ea686bdb1fb9f763a46aba718",
-    "scan": (83638.6 * 2.000 + 67584.0 * 1.000) * 1024,
-    "prepare": (42078.8 * 2.000 + 165239.4 * 1.000) * 1024,
+    "source_sha256": "e5ae882e17c64a7e28ce48e2e3fd6ee9df0f5d850858fdb93a682aeef700ef0c",
+    "scan": (79541.5 * 2.000 + 67584.0 * 1.000) * 1024,
+    "prepare": (33939.2 * 2.000 + 156743.0 * 1.000) * 1024,
 }
 
 
