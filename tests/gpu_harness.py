@@ -5,8 +5,8 @@ oracle under the tolerance the operator is held to:
     max |gpu - oracle| <= tol * rms(oracle)   for outputs and final states,
     tol = 1e-4 (fp32 q/k/v) or 2e-2 (bf16 q/k/v).
 
-With a bf16 output the result is additionally rounded once to bf16 (relative
-error <= 2^-9), so each output element is held to
+With a bf16 output the result is additionally rounded once to bf16 (round to
+nearest even: relative error <= 2^-8), so each output element is held to
     |gpu - oracle| <= tol * rms(oracle) + 2^-8 * |oracle|.
 """
 from __future__ import annotations
