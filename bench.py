@@ -73,9 +73,9 @@ C = 64
 PREFILL_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
                for f in ("gdn_prefill.hip", "gdn_mfma.h", "gdn_device.h", "gdn_internal.h")]
 MEASURED_TRAFFIC = {
-    "source_sha256": "e5ae882e17c64a7e28ce48e2e3fd6ee9df0f5d850858fdb93a682aeef700ef0c",
-    "scan": (79541.5 * 2.000 + 67584.0 * 1.000) * 1024,
-    "prepare": (33939.2 * 2.000 + 156743.0 * 1.000) * 1024,
+    "source_sha256": "a8a58f5f88f89545905f933412b2e5fec26eda731d7ee0c1b5cfca125a056564",
+    "scan": (79543.0 * 2.000 + 67584.0 * 1.000) * 1024,
+    "prepare": (34003.2 * 2.000 + 156743.0 * 1.000) * 1024,
 }
 
 

@@ -312,12 +312,6 @@ __device__ __forceinline__ u32x4 load_once(const bf16_t *p) {
 __device__ __forceinline__ u32x4 load_once(const float *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
-// The same through a buffer resource (bit 1 of the cache-policy operand is
-// the non-temporal bit): zero past the range's end, and no memory access at
-// all when the range is empty.
-__device__ __forceinline__ u32x4 load_once(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
-}
 
 // Squared norm of the 16 bytes a lane loaded from a q / k row.
 template <typename E> __device__ __forceinline__ float sumsq16(u32x4 u);
@@ -718,26 +712,25 @@ __global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW /
     float vh[NHV], vw[NWV];
     const int vrow0 = (tid / VPRV) * VL, vcv = tid % VPRV;
     static_assert(C * VPRV % NT == 0 && C * VPR % NT == 0, "whole vectors per thread");
-    // The rows are read through a buffer range that is empty when they are
-    // not needed (the prefetch after the last head): the loads still issue,
-    // so every wait counts exactly, but they read no memory (a reload of the
-    // last head's rows added 16 MiB of reads to a 4096-token call).
+    // When the rows are not needed (the prefetch after the last head) every
+    // lane reads the head's first 16 bytes instead: the loads still issue, so
+    // every wait counts exactly, but together they read one line (a reload of
+    // the last head's rows added 16 MiB of reads to a 4096-token call).
     auto load_v = [&](int hh, bool live) {
-        const auto vr = raw_buffer(const_cast<E *>(vg) + (size_t)t0 * pp.rs_v + (size_t)hh * DV,
-                                   live ? (uint32_t)(((size_t)(len - 1) * pp.rs_v + DV) * sizeof(E)) : 0u);
+        const E *v0 = vg + (size_t)t0 * pp.rs_v + (size_t)hh * DV;
         if constexpr (!CONV) {
 #pragma unroll
             for (int p = 0; p < VL; ++p) {
                 const int vi = tid + NT * p;
                 const int r = vi / VPRV, cv = vi % VPRV;
-                const u32x4 x = load_once(vr, (uint32_t)(((size_t)min(r, len - 1) * pp.rs_v + cv * VEC) * sizeof(E)));
+                const u32x4 x = load_once(live ? v0 + (size_t)min(r, len - 1) * pp.rs_v + cv * VEC : v0);
                 vpre[p] = r < len ? x : u32x4{0u, 0u, 0u, 0u};
             }
         } else {
 #pragma unroll
             for (int p = 0; p < VL; ++p) {
                 const int rr = min(vrow0 + p, len - 1);
-                vpre[p] = load_once(vr, (uint32_t)(((size_t)rr * pp.rs_v + vcv * VEC) * sizeof(E)));
+                vpre[p] = load_once(live ? v0 + (size_t)rr * pp.rs_v + vcv * VEC : v0);
             }
             // history: the three rows before the chunk, or for a sequence's
             // first chunk the slot's stored inputs (see the K and Q history)
