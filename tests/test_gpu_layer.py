@@ -53,6 +53,15 @@ def test_prefill_layer_varlen_in_ranges_bf16():
     _prefill(case, _layer(case, 89), raw_gates=True, heads=[0, 17, 31])
 
 
+@pytest.mark.parametrize("H_k,H_v,dtype", [(2, 2, "bf16"), (1, 4, "bf16"), (1, 8, "f32")])
+def test_prefill_layer_head_ratios_d128(H_k, H_v, dtype):
+    """The fused prefill at d_k = d_v = 128 (the eight-wave two-term or fp32
+    preparation) at head ratios other than 2, ragged lengths, raw gates."""
+    case = gi.make_case(f"layer_ratio_{H_k}_{H_v}_{dtype}", [1, 63, 64, 65, 200], H_k, H_v, 128,
+                        128, dtype, seed=97 + H_v, decay="weak", n_slots=8, scatter_slots=True)
+    _prefill(case, _layer(case, 97 + H_v), raw_gates=True)
+
+
 def test_prefill_conv_ragged_short_sequences_f32():
     case = gi.make_case("layer_ragged", [1, 2, 3, 63, 64, 65, 130], 2, 4, 64, 32, "f32", seed=81,
                         decay="weak", n_slots=12, scatter_slots=True)

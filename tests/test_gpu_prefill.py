@@ -84,6 +84,10 @@ LENGTHS = [1, 2, 63, 64, 65, 127, 128, 129, 0, 200]
     (2, 2, 32, 32, "f32"), (1, 4, 64, 32, "f32"), (2, 4, 32, 128, "bf16"),
     (4, 4, 128, 64, "bf16"), (1, 2, 128, 128, "f32"), (2, 4, 128, 128, "bf16"),
     (1, 1, 64, 64, "bf16"), (2, 8, 64, 128, "bf16"),
+    # d_k = d_v = 128 runs the eight-wave preparation, whose waves 4..7 repeat
+    # the row scalars of waves 0..3: head ratios 1, 4 and 8 there
+    (2, 2, 128, 128, "bf16"), (1, 4, 128, 128, "bf16"), (1, 8, 128, 128, "bf16"),
+    (1, 8, 128, 128, "f32"),
 ])
 def test_ragged_lengths_dims_and_ratios(H_k, H_v, d_k, d_v, dtype):
     case = gi.make_case(f"ragged_{H_k}_{H_v}_{d_k}_{d_v}_{dtype}", LENGTHS, H_k, H_v, d_k, d_v,
