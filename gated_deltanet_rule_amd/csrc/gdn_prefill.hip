@@ -1283,6 +1283,19 @@ template <int DK, int DV, int CT, typename E> struct ScanLds {
     static constexpr size_t BYTES = SF + 2 * UF;
 };
 
+// The four row scalars of a lane's accumulator rows (4 qd + j, j = 0..3)
+// from one value per lane (lane 4 m + j of each quad holds row j's): DPP
+// quad broadcasts, so a wave's load returns 4 instead of 16 bytes per lane
+// through the CU's data-return path, which the scan keeps busy.
+__device__ __forceinline__ floatx4 quad_rows(float x)
+{
+    const int b = __float_as_int(x);
+    return floatx4{__int_as_float(__builtin_amdgcn_mov_dpp(b, 0x00, 0xf, 0xf, true)),
+                   __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x55, 0xf, 0xf, true)),
+                   __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xAA, 0xf, 0xf, true)),
+                   __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xFF, 0xf, 0xf, true))};
+}
+
 // Two-term conversion of one accumulator tile (4 values per lane).  For bf16
 // operands it fills `part` (0 or 1) of a K block's 16-byte lane slot: 8 bytes
 // of hi and 8 bytes of lo bf16; fp32 operands have a single term filling the
@@ -1386,9 +1399,6 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
     auto kblk = [&](int c) { return reinterpret_cast<const u32x4 *>(kbase + (size_t)(c - sp.seg_lo) * kstep); };
     auto vfrag = [&](int c, int f) -> Frag { return __builtin_bit_cast(Frag, vblk(c)[f * 64 + lane]); };
     auto kfrag = [&](int c, int f) -> Frag { return __builtin_bit_cast(Frag, kblk(c)[f * 64 + lane]); };
-    auto scal4 = [&](int c, int off) -> floatx4 {
-        return *reinterpret_cast<const floatx4 *>(reinterpret_cast<const float *>(vblk(c) + G::F_SCAL * 64) + off);
-    };
     auto scal1 = [&](int c, int off) -> float {
         return reinterpret_cast<const float *>(vblk(c) + G::F_SCAL * 64)[off];
     };
@@ -1439,7 +1449,7 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
                 }
             }
         floatx4 u0 = __builtin_bit_cast(floatx4, vblk(c0)[u0f * 64 + lane]);
-        floatx4 ks4 = scal4(c0, 64 + ro);
+        float ks1 = scal1(c0, 64 + ro + (n & 3));
         float gn = scal1(c0, 128);
         // debug record: the chunk whose U is recorded (-1: none here)
         int dbg_c = -1;
@@ -1466,7 +1476,7 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
                 }
             }
             const floatx4 U = u0 - (WSh + WSl);
-            const floatx4 Uk = U * ks4;
+            const floatx4 Uk = U * quad_rows(ks1);
             if (c == dbg_c) {
                 const __amdgpu_buffer_rsrc_t dbg_u = raw_buffer(&sp.dbg->U[0][0], (uint32_t)sizeof(sp.dbg->U));
 #pragma unroll
@@ -1474,7 +1484,7 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
                 if (ct == 0 && rt == 0 && lane == 0) sp.dbg->scanned = 1;
             }
             u0 = __builtin_bit_cast(floatx4, vblk(cn)[u0f * 64 + lane]);
-            ks4 = scal4(cn, 64 + ro);
+            ks1 = scal1(cn, 64 + ro + (n & 3));
             {
                 const int kc = rt / TPB, part = rt % TPB;
                 TileOut<E>::put(myUf + (kc * NS) * 64, myUf + (kc * NS + NS - 1) * 64, lane, part, U);
@@ -1578,7 +1588,7 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
             Ph[kc] = pfrag(c0, G::F_PH, kc);
             if constexpr (NS == 2) Pl[kc] = pfrag(c0, G::F_PL, kc);
         }
-        floatx4 qs4 = scal4(c0, ro);
+        float qs1 = scal1(c0, ro + (n & 3));
         // the sequence's token range; its chunks are consecutive 64-token pieces
         const int tbeg = single ? C * cs : cs >= ce ? 0 : sp.ent[cs].t0;
         const int tend = single ? sp.single_T : cs < ce ? sp.ent[ce - 1].t0 + sp.ent[ce - 1].len : 0;
@@ -1602,8 +1612,8 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
                     Qlf[kb] = kfrag(cn, G::F_QL + rt * NKD + kb);
                 }
             }
-            const floatx4 Oi = (OQh + OQl) * qs4;
-            qs4 = scal4(cn, ro);
+            const floatx4 Oi = (OQh + OQl) * quad_rows(qs1);
+            qs1 = scal1(cn, ro + (n & 3));
 #pragma unroll
             for (int q = 0; q < NKD; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
