@@ -1409,6 +1409,8 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
 
     if (role == 0) {
         // state: registers of the owning wave, published as two-term B fragments
+        // (loaded first, published once the first chunk's operands are in
+        // flight too, so that the two latencies overlap)
         floatx4 Sreg[NOWN][TPB];
         {
             const int sin = sp.state_in ? sp.slot_in[i] : -1;
@@ -1426,7 +1428,6 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
                         for (int j = 0; j < 4; ++j) v[j] = base[(int64_t)(16 * (kb * TPB + t) + 4 * qd + j) * DV];
                     }
                     Sreg[o][t] = v;
-                    if (kb < NKD) TileOut<E>::put(mySf + (kb * NS) * 64, mySf + (kb * NS + NS - 1) * 64, lane, t, v);
                 }
             }
         }
@@ -1454,9 +1455,17 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
         // debug record: the chunk whose U is recorded (-1: none here)
         int dbg_c = -1;
         if (sp.dbg && h == sp.dbg_h) dbg_c = __builtin_amdgcn_readfirstlane(sp.dbg->chunk);
-        // Let the first chunk's operands land before the loop: the loop's
-        // waits then only have to account for the loads issued inside it.
+        // Let the state and the first chunk's operands land before the loop:
+        // the loop's waits then only have to account for the loads issued
+        // inside it.
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+#pragma unroll
+        for (int o = 0; o < NOWN; ++o) {
+            const int kb = rt + 4 * o;
+#pragma unroll
+            for (int t = 0; t < TPB; ++t)
+                if (kb < NKD) TileOut<E>::put(mySf + (kb * NS) * 64, mySf + (kb * NS + NS - 1) * 64, lane, t, Sreg[o][t]);
+        }
         lds_sync();
 
         for (int c = cs; c < ce; ++c) {
