@@ -18,7 +18,8 @@
 // MI355X mapping (three launches):
 //   1. chunk_table_kernel: cu_seqlens -> one descriptor per 64-token chunk
 //      (sequence, first token, length) and each sequence's chunk range.
-//   2. prep_kernel, one workgroup per (chunk, key head), fully parallel:
+//   2. prep_kernel, one workgroup per (chunk, key head) (eight waves at
+//      d_k = d_v = 128), fully parallel:
 //      everything that does not depend on the carried state, for all value
 //      heads sharing the key head.  K K^T and K Q^T once (bf16 MFMA, fp32
 //      accumulate); the decay masks from an fp64 cumulative sum (so
@@ -30,11 +31,13 @@
 //      and accumulator tiles (U0).
 //   3. scan_kernel, one workgroup per (sequence, value head, 16 state
 //      columns): walks the sequence's chunks in order with the state in
-//      registers for the whole sequence.  Each of the four waves takes 16
-//      token rows of a chunk and owns 32 rows of the state:
-//        phase A (token rows):  U = U0 - W S,  Q S
-//        phase B (token rows):  O = qs * (Q S) + P U
-//                (state rows):  S = gn * S + K^T (ks * U)
+//      registers for the whole sequence.  Four state waves each take 16
+//      token rows of a chunk and own 32 rows of the state; four output
+//      waves each take 16 token rows of the output:
+//        phase A  state waves:  U = U0 - W S           (token rows)
+//                 output waves: Q S                    (token rows)
+//        phase B  state waves:  S = gn * S + K^T (ks * U)   (state rows)
+//                 output waves: O = qs * (Q S) + P U   (token rows)
 //      U and S are exchanged through LDS as ready-made operand fragments;
 //      each wave loads its own operands from the workspace straight into
 //      registers, one chunk ahead.  With the layer prologue the launch that
