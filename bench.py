@@ -73,9 +73,9 @@ C = 64
 PREFILL_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
                for f in ("gdn_prefill.hip", "gdn_mfma.h", "gdn_device.h", "gdn_internal.h")]
 MEASURED_TRAFFIC = {
-    "source_sha256": "cac91a4fcc579698be8326c9deca3a6a9d949db16166a05c3897aaca04ff496c",
-    "scan": (79539.6 * 2.000 + 67584.0 * 1.000) * 1024,
-    "prepare": (34003.5 * 2.000 + 156742.0 * 1.000) * 1024,
+    "source_sha256": "e343370db74045dc2137963ee370abbbd05febcbc9d8a335362b507ed286e892",
+    "scan": (79543.0 * 2.000 + 67584.0 * 1.000) * 1024,
+    "prepare": (34001.9 * 2.000 + 156741.0 * 1.000) * 1024,
 }
 
 
@@ -84,8 +84,8 @@ MEASURED_TRAFFIC = {
 DECODE_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
               for f in ("gdn_decode.hip", "gdn_device.h", "gdn_internal.h")]
 MEASURED_DECODE_TRAFFIC = {
-    "source_sha256": "1d1c105f06855498ba67589b48002f1eacbf6d15ed20d159941803373d54b041",
-    "decode": (66153.0 * 2.000 + 132096.0 * 1.000) * 1024,
+    "source_sha256": "e60a8893cca8bf1c09073edbd6646c910951f15edede56c86cc30cae4e2be296",
+    "decode": (66153.4 * 2.000 + 132096.0 * 1.000) * 1024,
 }
 
 

@@ -87,9 +87,7 @@ __device__ __forceinline__ float conv1(float4 w, float h0, float h1, float h2, f
 template <int CG, int DV>
 __device__ __forceinline__ void gated_norm_row(float o[4], const float zg[4], float eps)
 {
-    float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
-#pragma unroll
-    for (int off = CG / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    const float ss = group_sum<CG>(o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3]);
     const float rn = rsqrtf(ss / DV + eps);
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = o[j] * rn * zg[j];
@@ -277,9 +275,9 @@ __global__ __launch_bounds__(kDecodeThreads * GR, 4) void decode_kernel(RecParam
         qq += b * b;
         kq += a * b;
     }
-    kk = wave_sum(kk);
-    qq = wave_sum(qq);
-    kq = wave_sum(kq);
+    kk = group_sum<64>(kk);
+    qq = group_sum<64>(qq);
+    kq = group_sum<64>(kq);
     const float rk = rsqrtf(kk + P.eps);
     const float rq = rsqrtf(qq + P.eps) * P.scale;
 
@@ -340,6 +338,17 @@ __global__ __launch_bounds__(kDecodeThreads * GR, 4) void decode_kernel(RecParam
     }
 }
 
+// Sum over the row groups of one wave: lanes that hold the same column group
+// (lane mod CG) and different row groups, i.e. lanes l ^ 8 (CG = 8: a rotation
+// by 8 within the row), l ^ 16 and l ^ 32 (the row swaps).
+template <int CG>
+__device__ __forceinline__ float rg_wave_sum(float x)
+{
+    if constexpr (CG <= 8) x = dpp_add<0x128>(x);      // row_ror:8
+    if constexpr (CG <= 16) x = row_swap_add<1>(x);
+    return row_swap_add<2>(x);
+}
+
 // Several tokens per sequence (speculative-decoding verification, short
 // prompts): the same step, token after token, with the state block held in
 // registers, so it is read from and written to HBM once per call instead of
@@ -347,28 +356,10 @@ __global__ __launch_bounds__(kDecodeThreads * GR, 4) void decode_kernel(RecParam
 // while the current one is processed; k, q and the reduction partials
 // alternate between two LDS buffers, so a token needs two barriers.  With the
 // prologue, each thread keeps the convolution window of its q or k channel
-// and of its v channel in registers from token to token.  FUSED (here and in decode_kernel):
+// and of its v channel from token to token (in LDS slots of its own: registers
+// are what limit this kernel).  FUSED (here and in decode_kernel):
 // prologue and/or epilogue present; the plain instantiation carries none of
 // their code or registers.
-// Sum over the row groups of one wave: lanes that hold the same column group
-// (lane mod CG) and different row groups.
-template <int CG>
-__device__ __forceinline__ float rg_wave_sum(float x)
-{
-    if constexpr (CG <= 8) x += __shfl_xor(x, 8, 64);
-    if constexpr (CG <= 16) x += __shfl_xor(x, 16, 64);
-    // lanes l and l ^ 32 (v_permlane32_swap with both operands x: the low
-    // half of the first result and the high half of the second hold x, the
-    // other halves x of the partner lane).  The results pass through an
-    // empty asm: with identical operands the compiler otherwise takes the
-    // two results for one and adds the first to itself.
-    const unsigned a = __builtin_bit_cast(unsigned, x);
-    const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
-    unsigned lo = r[0], hi = r[1];
-    asm volatile("" : "+v"(lo), "+v"(hi));
-    return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
-}
-
 template <int DK, int DV, typename E, typename OT, bool FUSED, int GR>
 __global__ __launch_bounds__(kDecodeThreads * GR, 4) void decode_multi_kernel(RecParams P)
 {
@@ -574,9 +565,9 @@ __global__ __launch_bounds__(kDecodeThreads * GR, 4) void decode_multi_kernel(Re
             qq += c * c;
             kq += a * c;
         }
-        kk = wave_sum(kk);
-        qq = wave_sum(qq);
-        kq = wave_sum(kq);
+        kk = group_sum<64>(kk);
+        qq = group_sum<64>(qq);
+        kq = group_sum<64>(kq);
         const float rk = rsqrtf(kk + P.eps);
         const float rq = rsqrtf(qq + P.eps) * P.scale;
 

@@ -92,10 +92,48 @@ __device__ __forceinline__ float silu(float x) {
     return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
 }
 
-// Wave-wide (64 lanes) sum.
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+// x plus the x of the lane that the DPP control CTRL selects (every lane of
+// the wave active and every source lane inside the wave).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+// x plus the x of the lane ROWS x 16 lanes away (ROWS 1 or 2), by the gfx950
+// row swaps: with both operands x, the two results hold x and the partner
+// rows' x in complementary rows, so their sum is the pair's sum in the same
+// order on both sides.  The results pass through an empty asm: with
+// identical operands the compiler otherwise takes the two results for one.
+template <int ROWS>
+__device__ __forceinline__ float row_swap_add(float x) {
+    const unsigned a = __float_as_uint(x);
+    unsigned lo, hi;
+    if constexpr (ROWS == 1) {
+        const auto r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+        lo = r[0]; hi = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+        lo = r[0]; hi = r[1];
+    }
+    asm volatile("" : "+v"(lo), "+v"(hi));
+    return __uint_as_float(lo) + __uint_as_float(hi);
+}
+
+// Sum over aligned groups of N consecutive lanes (N a power of two, 2 to 64);
+// every lane of a group receives the group's total, bitwise the same on each.
+// Each step pairs a lane with one whose partial it does not hold yet: lane ^ 1
+// and lane ^ 2 (quad permutations), lane 7 - i and 15 - i within a row (the
+// half-row and row mirrors), then the row swaps.  All of it is VALU work: no
+// LDS round trip per step, as a shuffle through ds_bpermute would take.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N >= 2 && N <= 64 && (N & (N - 1)) == 0, "group of 2 to 64 lanes");
+    x = dpp_add<0xB1>(x);                               // quad_perm [1,0,3,2]
+    if constexpr (N >= 4) x = dpp_add<0x4E>(x);         // quad_perm [2,3,0,1]
+    if constexpr (N >= 8) x = dpp_add<0x141>(x);        // row_half_mirror
+    if constexpr (N >= 16) x = dpp_add<0x140>(x);       // row_mirror
+    if constexpr (N >= 32) x = row_swap_add<1>(x);
+    if constexpr (N >= 64) x = row_swap_add<2>(x);
     return x;
 }
 

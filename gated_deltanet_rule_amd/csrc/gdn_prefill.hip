@@ -862,11 +862,9 @@ __global__ __launch_bounds__(64 * NW, ((sizeof(E) == 2 && !CONV) ? 2 : 1) * NW /
             k2 = sumsq16<E>(kv);
             q2 = sumsq16<E>(qv);
         }
-#pragma unroll
-        for (int off = VPR / 2; off >= 1; off >>= 1) {
-            k2 += __shfl_xor(k2, off, 64);
-            q2 += __shfl_xor(q2, off, 64);
-        }
+        // a row's VPR vectors sit in VPR consecutive lanes
+        k2 = group_sum<VPR>(k2);
+        q2 = group_sum<VPR>(q2);
         if (cv == 0) {
             sRK[r] = r < len ? rsqrtf(k2 + pp.eps) : 0.f;
             sRQ[r] = r < len ? rsqrtf(q2 + pp.eps) * pp.scale : 0.f;
