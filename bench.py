@@ -73,8 +73,8 @@ C = 64
 PREFILL_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
                for f in ("gdn_prefill.hip", "gdn_mfma.h", "gdn_device.h", "gdn_internal.h")]
 MEASURED_TRAFFIC = {
-    "source_sha256": "e343370db74045dc2137963ee370abbbd05febcbc9d8a335362b507ed286e892",
-    "scan": (79543.0 * 2.000 + 67584.0 * 1.000) * 1024,
+    "source_sha256": "ace15307f041711fe6d158b857305fad90c9139d6587a2901b9bea434f2d9615",
+    "scan": (79541.0 * 2.000 + 67584.0 * 1.000) * 1024,
     "prepare": (34001.9 * 2.000 + 156741.0 * 1.000) * 1024,
 }
 

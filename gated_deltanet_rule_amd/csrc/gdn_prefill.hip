@@ -1581,8 +1581,12 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
         OT *og = static_cast<OT *>(sp.out);
         Frag Qf[NKD], Qlf[SI ? NKD : 1], Ph[NKC], Pl[NKC];
         // P row tile rt is zero past column 16 rt + 15, so its K blocks from
-        // npl on are zero and the preparation does not write them: they are
-        // read through a range that ends before them (zero, no memory access)
+        // npl on are zero and the preparation does not write them, and phase
+        // B skips them.  The one-term kernel reads them through a range that
+        // ends before them (zero, no memory access): skipping those loads on
+        // the wave-uniform branch makes the waits after it more conservative,
+        // which costs that kernel more than the loads.  The two-term kernel,
+        // with twice the fragments per block, skips them.
         const int npl = (16 * rt + 15) / KB + 1;
         auto pfrag = [&](int c, int base, int kc) -> Frag {
             const auto r = raw_buffer(const_cast<u32x4 *>(vblk(c)) + (size_t)(base + rt * NKC) * 64, (uint32_t)npl * 1024u);
@@ -1595,6 +1599,7 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
         }
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
+            if (SI && kc >= npl) continue;
             Ph[kc] = pfrag(c0, G::F_PH, kc);
             if constexpr (NS == 2) Pl[kc] = pfrag(c0, G::F_PL, kc);
         }
@@ -1659,6 +1664,7 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
             }
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
+                if (SI && kc >= npl) continue;
                 Ph[kc] = pfrag(cn, G::F_PH, kc);
                 if constexpr (NS == 2) Pl[kc] = pfrag(cn, G::F_PL, kc);
             }
