@@ -1584,9 +1584,9 @@ __global__ __launch_bounds__(CT * 512) void scan_kernel(ScanParams sp)
         // npl on are zero and the preparation does not write them, and phase
         // B skips them.  The one-term kernel reads them through a range that
         // ends before them (zero, no memory access): skipping those loads on
-        // the wave-uniform branch makes the waits after it more conservative,
-        // which costs that kernel more than the loads.  The two-term kernel,
-        // with twice the fragments per block, skips them.
+        // the wave-uniform branch made that kernel slower (by about 7%, also
+        // with the skipped loads issued first).  The two-term kernel, with
+        // twice the fragments per block, skips them.
         const int npl = (16 * rt + 15) / KB + 1;
         auto pfrag = [&](int c, int base, int kc) -> Frag {
             const auto r = raw_buffer(const_cast<u32x4 *>(vblk(c)) + (size_t)(base + rt * NKC) * 64, (uint32_t)npl * 1024u);
