@@ -422,8 +422,7 @@ __global__ __launch_bounds__(kDecodeThreads * GR, 4) void decode_multi_kernel(Re
 
     // Order of memory operations as in decode_kernel: the prologue's taps and
     // stored inputs, the norm weight and the first token are loaded before
-    // the state block, and a token's inputs are only fetched (the gate
-    // activations are applied when the token is processed), so the next
+    // the state block, and a token's inputs are only fetched, so the next
     // token's loads stay in flight while the current one is processed.
     u32x3 hq3 = {0u, 0u, 0u}, hv3 = {0u, 0u, 0u};
     float4 wq = make_float4(0.f, 0.f, 0.f, 0.f), wv = wq;
@@ -441,18 +440,16 @@ __global__ __launch_bounds__(kDecodeThreads * GR, 4) void decode_multi_kernel(Re
             raw_buffer(const_cast<float *>(P.norm_w), norm ? DV * 4u : 0u), ev * 4u, 0, 0));
     }
 
-    // a token's inputs for this thread: its q or k value, v (fused: its
-    // channel and z; plain: four columns), and the raw g and beta
+    // a token's inputs for this thread: its q or k value and v (fused: its
+    // channel and z; plain: four columns)
     struct Tok {
-        float kq, gt, bt;
+        float kq;
         float vv[4];
         float zs;
     };
     auto fetch = [&](int t) {
         Tok r;
         r.kq = to_f32((isk ? k : q)[(int64_t)t * P.rs_qk + (int64_t)kh * DK + e]);
-        r.gt = P.g[(int64_t)t * P.H_v + h];
-        r.bt = P.beta[(int64_t)t * P.H_v + h];
         const E *vrow = v + (int64_t)t * P.rs_v + (int64_t)h * DV;
         if constexpr (FUSED) {
             r.vv[0] = to_f32(vrow[ev]);
@@ -469,10 +466,23 @@ __global__ __launch_bounds__(kDecodeThreads * GR, 4) void decode_multi_kernel(Re
         }
         return r;
     };
+    // g and beta of up to 64 tokens per wave: lane l holds those of token
+    // tb + base + l (the last token's past the end).  A batch is activated
+    // once, all its tokens at once, and each token takes its pair with a
+    // lane read: activated per token in every thread, the raw gates (two
+    // exponentials, a logarithm and a division) cost more vector-ALU time
+    // than the token's state arithmetic leaves free.
+    float gl = 0.f, bl = 0.f;
+    auto gate_load = [&](int base) {
+        const int64_t t = min(tb + base + lane, te - 1);
+        gl = P.g[t * P.H_v + h];
+        bl = P.beta[t * P.H_v + h];
+    };
     Tok cur{};
     float rate = 0.f, bias = 0.f;
     if (tb < te) {                              // an empty sequence reads no token
         cur = fetch(tb);
+        gate_load(0);
         rate = P.gates.rate[h];
         bias = P.gates.bias[h];
     }
@@ -528,8 +538,16 @@ __global__ __launch_bounds__(kDecodeThreads * GR, 4) void decode_multi_kernel(Re
 
     for (int t = tb; t < te; ++t) {
         const int b = (t - tb) & 1;
-        const float gt = P.gates.raw ? gate_g(cur.gt, bias, rate) : cur.gt;
-        const float bt = P.gates.raw ? gate_beta(cur.bt) : cur.bt;
+        const int j = (t - tb) & 63;
+        if (j == 0) {
+            if (t != tb) gate_load(t - tb);
+            if (P.gates.raw) {
+                gl = gate_g(gl, bias, rate);
+                bl = gate_beta(bl);
+            }
+        }
+        const float gt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), j));
+        const float bt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bl), j));
         float kqv = cur.kq;
         if (conv) {
             const float h0 = shw_[grp][0][tid], h1 = shw_[grp][1][tid], h2 = shw_[grp][2][tid];

@@ -99,6 +99,14 @@ def test_multi_weak_decay_ragged_tails():
     _multi(_scaled(case, 20.0, 20.0))
 
 
+def test_multi_raw_gates_past_64_tokens():
+    """The multi-token kernel activates the raw gates of 64 tokens at a time
+    per wave: sequences that cross one and two such batches."""
+    case = gi.make_case("gates_multi_long", [65, 0, 130, 2, 64], 1, 2, 128, 64, "bf16", seed=77,
+                        decay="weak", gate_bias=True)
+    _multi(case)
+
+
 def test_raw_gates_match_precomputed_gates():
     """The raw path and the final-gate path on the same tokens agree: the
     kernels' fp32 activations differ from torch's fp32 ones only by rounding."""
