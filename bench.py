@@ -84,8 +84,8 @@ MEASURED_TRAFFIC = {
 DECODE_SRC = [os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", f)
               for f in ("gdn_decode.hip", "gdn_device.h", "gdn_internal.h")]
 MEASURED_DECODE_TRAFFIC = {
-    "source_sha256": "e60a8893cca8bf1c09073edbd6646c910951f15edede56c86cc30cae4e2be296",
-    "decode": (66153.4 * 2.000 + 132096.0 * 1.000) * 1024,
+    "source_sha256": "63b31562283da88aa828759356d09f680d1bf501fc60011d736b3e4025747225",
+    "decode": (66152.4 * 2.000 + 132096.0 * 1.000) * 1024,
 }
 
 
